@@ -1,0 +1,273 @@
+"""Seeded synthetic workloads for the LatentIndex decode indexer.
+
+This module only draws random inputs and arranges them into shapes: it holds
+none of the method's arithmetic (no absorption, scoring, selection or
+quantisation).  Both the CPU oracle (through the tests and the bench's CPU leg)
+and the HIP path consume exactly the arrays produced here.
+
+Shapes follow the LatentIndex paper summary (picx.dev, "Methodology"): one
+shared latent c_t of width d_C (= r here) per token per layer group, per-layer
+decoders D^(l) that map it to d_I-wide indexer keys (eq. 3), per-head queries
+q_{s,h} of width d_I and head weights w_{s,h} (eq. 8), groups of four layers
+(explainer page, storage paragraph), k = 2048 and a candidate budget B = 8192
+(Table 4 caption text).
+
+Every array comes from its own counter-seeded NumPy PCG64 stream,
+``default_rng([seed, cfg_id, stream])``, so any part (one sequence's latent,
+one layer's queries) can be regenerated alone, identically on every machine.
+
+Stream ids:
+  1            context lengths (ragged configurations)
+  1000 + s     latent rows of sequence s, then its planted-token choice
+  2000         decoders: the shared matrix G0, then one noise matrix per layer
+  3000 + l     queries, then head weights, of layer l
+  4000         physical block permutation (block table)
+  5000 + l     prefill absorbed queries and head weights of layer l
+
+Readings taken where the configuration text is terse:
+  * D_l = (G0 + 0.3 * G_l) / sqrt(r), G0 and G_l i.i.d. N(0, 1), stored
+    transposed as Dt_l of shape [r, d_I] and shared by all heads of the layer.
+  * Planted tokens are drawn uniformly without replacement; their latent rows
+    are multiplied by the planting factor before any quantisation.
+  * Ragged lengths are round(exp(U[ln 8192, ln 131072])).
+  * The prefill chunk's absorbed queries are drawn directly on the bf16 grid
+    (an N(0, d_I*(1+0.3^2)/r) draw with the low 16 bits of the fp32 pattern
+    cleared), which matches the variance of Dt_l @ q without this module
+    doing the absorption itself.
+  * The decode step appends the last token of each sequence: the cache holds
+    positions 0..L-2 before the step and 0..L-1 after it; layer queries score
+    all L positions (causal set inclusive of the current token).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+BLOCK = 64  # tokens per paged latent block
+
+
+@dataclasses.dataclass
+class Workload:
+    """One synthetic configuration.  All arrays are host NumPy arrays."""
+
+    name: str
+    cfg_id: int
+    seed: int
+    G: int                       # layers per group (layer 0 is the anchor)
+    H: int                       # indexer heads
+    r: int                       # latent width d_C
+    d_I: int                     # indexer key width
+    k: int                       # per-layer top-k
+    B: Optional[int]             # HS candidate budget (None: full scan only)
+    cache_dtype: str             # "fp32" | "bf16" | "fp8"
+    lens: np.ndarray             # int64 [n_seq] context lengths L_s
+    block_table: np.ndarray      # int32 [n_seq, max_blocks], -1 = unused
+    n_phys_blocks: int
+    nope_off: int                # key coordinates [nope_off, d_I) carry the bias b
+    Dt: np.ndarray               # fp32 [G, r, d_I]  (D_l transposed)
+    b: np.ndarray                # fp32 [G, d_I - nope_off]
+    q: Optional[np.ndarray]      # fp32 [G, n_q, H, d_I]   (decode)
+    w: np.ndarray                # fp32 [G, n_q, H]
+    q_seq: np.ndarray            # int32 [n_q] sequence of each query
+    q_len: np.ndarray            # int32 [n_q] causal prefix length of each query
+    planted: list                # per sequence: int64 array of planted token ids
+    plant_factor: float
+    _latent: Optional[list] = None   # per-sequence fp32 [L_s, r], drawn lazily
+    prefill_positions: Optional[np.ndarray] = None  # int64 [n_q] (prefill only)
+
+    @property
+    def n_seq(self) -> int:
+        return int(self.lens.shape[0])
+
+    @property
+    def n_q(self) -> int:
+        return int(self.q_seq.shape[0])
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def max_len(self) -> int:
+        return int(self.lens.max())
+
+    def latent(self, s: int) -> np.ndarray:
+        """fp32 [L_s, r] latent rows of sequence s (planted rows scaled)."""
+        if self._latent is None:
+            self._latent = [None] * self.n_seq
+        if self._latent[s] is None:
+            self._latent[s] = _draw_latent(self, s)[0]
+        return self._latent[s]
+
+    def drop_latents(self) -> None:
+        self._latent = None
+
+    def prefill_queries(self, layer: int) -> tuple[np.ndarray, np.ndarray]:
+        """(q_tilde bf16 bit patterns uint16 [n_q, H, r], w fp32 [n_q, H])."""
+        assert self.prefill_positions is not None
+        rng = _rng(self.seed, self.cfg_id, 5000 + layer)
+        std = math.sqrt(self.d_I * (1.0 + 0.3 ** 2) / self.r)
+        qt = rng.standard_normal((self.n_q, self.H, self.r), dtype=np.float32)
+        qt *= np.float32(std)
+        bits = (qt.view(np.uint32) >> 16).astype(np.uint16)
+        w = rng.standard_normal((self.n_q, self.H), dtype=np.float32)
+        w *= np.float32(1.0 / math.sqrt(self.H))
+        return bits, w
+
+
+def _rng(seed: int, cfg_id: int, stream: int) -> np.random.Generator:
+    return np.random.default_rng([int(seed), int(cfg_id), int(stream)])
+
+
+def _draw_latent(wl: Workload, s: int):
+    rng = _rng(wl.seed, wl.cfg_id, 1000 + s)
+    L = int(wl.lens[s])
+    lat = rng.standard_normal((L, wl.r), dtype=np.float32)
+    n_plant = len(wl.planted[s])
+    idx = rng.choice(L, size=n_plant, replace=False) if n_plant else np.zeros(0, np.int64)
+    idx = np.sort(idx.astype(np.int64))
+    lat[idx] *= np.float32(wl.plant_factor)
+    return lat, idx
+
+
+def _planted_ids(seed, cfg_id, s, L, n_plant, r):
+    # The planted choice is drawn from the latent stream after the latent rows.
+    rng = _rng(seed, cfg_id, 1000 + s)
+    rng.standard_normal((L, r), dtype=np.float32)
+    idx = rng.choice(L, size=n_plant, replace=False) if n_plant else np.zeros(0, np.int64)
+    return np.sort(idx.astype(np.int64))
+
+
+def _block_table(seed, cfg_id, lens, permute):
+    nblk = [(int(L) + BLOCK - 1) // BLOCK for L in lens]
+    total = sum(nblk)
+    max_blocks = max(nblk)
+    if permute:
+        perm = _rng(seed, cfg_id, 4000).permutation(total).astype(np.int32)
+    else:
+        perm = np.arange(total, dtype=np.int32)
+    bt = np.full((len(lens), max_blocks), -1, dtype=np.int32)
+    off = 0
+    for s, n in enumerate(nblk):
+        bt[s, :n] = perm[off:off + n]
+        off += n
+    return bt, total
+
+
+def _decoders(seed, cfg_id, G, r, d_I):
+    rng = _rng(seed, cfg_id, 2000)
+    g0 = rng.standard_normal((r, d_I), dtype=np.float32)
+    Dt = np.empty((G, r, d_I), dtype=np.float32)
+    inv = np.float32(1.0 / math.sqrt(r))
+    for l in range(G):
+        gl = rng.standard_normal((r, d_I), dtype=np.float32)
+        Dt[l] = (g0 + np.float32(0.3) * gl) * inv
+    return Dt
+
+
+def _queries(seed, cfg_id, G, n_q, H, d_I):
+    q = np.empty((G, n_q, H, d_I), dtype=np.float32)
+    w = np.empty((G, n_q, H), dtype=np.float32)
+    for l in range(G):
+        rng = _rng(seed, cfg_id, 3000 + l)
+        q[l] = rng.standard_normal((n_q, H, d_I), dtype=np.float32)
+        w[l] = rng.standard_normal((n_q, H), dtype=np.float32) * np.float32(1.0 / math.sqrt(H))
+    return q, w
+
+
+def make_decode(name, cfg_id, seed, *, G, H, r, d_I, k, B, cache_dtype, lens,
+                plant_frac=None, n_plant=None, plant_factor, permute_blocks,
+                nope_off=None, bias=False) -> Workload:
+    lens = np.asarray(lens, dtype=np.int64)
+    n_seq = len(lens)
+    planted = []
+    for s in range(n_seq):
+        L = int(lens[s])
+        n = n_plant if n_plant is not None else int(round(plant_frac * L))
+        planted.append(_planted_ids(seed, cfg_id, s, L, n, r))
+    bt, nphys = _block_table(seed, cfg_id, lens, permute_blocks)
+    Dt = _decoders(seed, cfg_id, G, r, d_I)
+    q, w = _queries(seed, cfg_id, G, n_seq, H, d_I)
+    no = d_I if nope_off is None else nope_off
+    b = np.zeros((G, d_I - no), dtype=np.float32)
+    if bias and d_I - no > 0:
+        b = _rng(seed, cfg_id, 2001).standard_normal((G, d_I - no), dtype=np.float32)
+    return Workload(
+        name=name, cfg_id=cfg_id, seed=seed, G=G, H=H, r=r, d_I=d_I, k=k, B=B,
+        cache_dtype=cache_dtype, lens=lens, block_table=bt, n_phys_blocks=nphys,
+        nope_off=no, Dt=Dt, b=b, q=q, w=w,
+        q_seq=np.arange(n_seq, dtype=np.int32), q_len=lens.astype(np.int32),
+        planted=planted, plant_factor=plant_factor)
+
+
+def ragged_lens(seed, cfg_id, n, lo=8192, hi=131072):
+    u = _rng(seed, cfg_id, 1).uniform(math.log(lo), math.log(hi), size=n)
+    return np.rint(np.exp(u)).astype(np.int64)
+
+
+def config(i: int, seed: int = 0) -> Workload:
+    """The five synthetic configurations, by index.
+
+    0  tiny: 1 sequence, L=4096, H=8, r=32, d_I=64, fp32 cache, k=256,
+       16 planted tokens x4 (CPU-seconds parity case).
+    1  DeepSeek-V3.2-shaped decode at 32K: H=64, r=256, d_I=128, bf16 cache,
+       batch 1, k=2048, 1% planted x3.
+    2  batched long decode: 16 sequences, ragged log-uniform 8K-128K,
+       fp8 e4m3 cache with per-token fp32 scale, 64-token pages behind a
+       random block table, k=2048.
+    3  HS at 128K: batch 4, L=131072 each, bf16, paged as 2, B=8192, k=2048.
+    4  prefill chunk: 2048 queries at positions 63488..65535 against a
+       65536-token bf16 latent, H=64, r=256, causal, k=2048.
+    """
+    if i == 0:
+        return make_decode("tiny-4k", 0, seed, G=4, H=8, r=32, d_I=64, k=256, B=None,
+                           cache_dtype="fp32", lens=[4096], n_plant=16, plant_factor=4.0,
+                           permute_blocks=False)
+    if i == 1:
+        return make_decode("dsv32-decode-32k", 1, seed, G=4, H=64, r=256, d_I=128, k=2048,
+                           B=None, cache_dtype="bf16", lens=[32768], plant_frac=0.01,
+                           plant_factor=3.0, permute_blocks=False)
+    if i == 2:
+        return make_decode("ragged-16x8k-128k-fp8", 2, seed, G=4, H=64, r=256, d_I=128,
+                           k=2048, B=None, cache_dtype="fp8", lens=ragged_lens(seed, 2, 16),
+                           plant_frac=0.01, plant_factor=3.0, permute_blocks=True)
+    if i == 3:
+        return make_decode("hs-128k-b4", 3, seed, G=4, H=64, r=256, d_I=128, k=2048, B=8192,
+                           cache_dtype="bf16", lens=[131072] * 4, plant_frac=0.01,
+                           plant_factor=3.0, permute_blocks=True)
+    if i == 4:
+        return make_prefill(seed)
+    raise ValueError(f"no configuration {i}")
+
+
+def make_prefill(seed: int = 0, n_q: int = 2048, L: int = 65536, H: int = 64, r: int = 256,
+                 d_I: int = 128, k: int = 2048, G: int = 4, cfg_id: int = 4) -> Workload:
+    lens = np.array([L], dtype=np.int64)
+    planted = [_planted_ids(seed, cfg_id, 0, L, int(round(0.01 * L)), r)]
+    bt, nphys = _block_table(seed, cfg_id, lens, False)
+    pos = np.arange(L - n_q, L, dtype=np.int64)
+    w = np.empty((G, n_q, H), dtype=np.float32)
+    wl = Workload(
+        name=f"prefill-{n_q}x{L // 1024}k", cfg_id=cfg_id, seed=seed, G=G, H=H, r=r, d_I=d_I,
+        k=k, B=None, cache_dtype="bf16", lens=lens, block_table=bt, n_phys_blocks=nphys,
+        nope_off=d_I, Dt=np.zeros((G, r, d_I), np.float32), b=np.zeros((G, 0), np.float32),
+        q=None, w=w, q_seq=np.zeros(n_q, dtype=np.int32), q_len=(pos + 1).astype(np.int32),
+        planted=planted, plant_factor=3.0, prefill_positions=pos)
+    for l in range(G):
+        w[l] = wl.prefill_queries(l)[1]
+    return wl
+
+
+def small_decode(seed: int, *, n_seq=2, lens=None, H=8, r=32, d_I=16, G=2, k=16, B=None,
+                 cache_dtype="fp32", nope_off=None, bias=False, plant=0, factor=4.0,
+                 permute=True, cfg_id=90) -> Workload:
+    """A tiny decode workload for fast tests (ragged lengths allowed)."""
+    if lens is None:
+        lens = [100 + 37 * s for s in range(n_seq)]
+    return make_decode(f"small-{cfg_id}", cfg_id, seed, G=G, H=H, r=r, d_I=d_I, k=k, B=B,
+                       cache_dtype=cache_dtype, lens=lens, n_plant=plant, plant_factor=factor,
+                       permute_blocks=permute, nope_off=nope_off, bias=bias)
