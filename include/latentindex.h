@@ -1,0 +1,204 @@
+/*
+ * latentindex.h -- C ABI of the LatentIndex decode indexer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (LatentIndex paper summary on picx.dev, "Methodology"): a group
+ * of consecutive layers shares one latent cache c_t built from the anchor
+ * layer's hidden state (eqs. 1-2); each layer l owns a decoder D^(l) that
+ * defines its indexer keys k_t = D^(l) c_t (+ b^(l) on the NoPE part, eq. 3);
+ * decoders are absorbed into the queries, q~ = D^T q and beta = q^N . b
+ * (eq. 6), so that q . k_t = q~ . c_t + beta (eq. 7); every layer scores the
+ * shared cache with u_t = sum_h w_h ReLU(q~_h . c_t + beta_h) (eq. 8) and
+ * keeps its own top-k (the TopK definition after eq. 8).  Hierarchical
+ * selection ("Hierarchical Selection" paragraph): the anchor's top-B
+ * positions form a candidate set that each follower rescores and refines.
+ *
+ * Conventions shared by every call:
+ *  - Ownership: the caller allocates every buffer (inputs, outputs and the
+ *    workspace); the library never allocates, frees or synchronises.
+ *  - Pointers named "device" must be device memory of the current HIP device;
+ *    all other arguments are host values.  Arrays are dense row-major.
+ *  - Execution: each call only enqueues kernels on `stream` (a hipStream_t;
+ *    NULL = the null stream) and returns.  Results are ready when the stream
+ *    reaches that point.
+ *  - Errors: every shape/dtype/pointer check runs on the host before any
+ *    launch; a non-OK status means nothing was enqueued (LI_ERR_HIP: a launch
+ *    failed).  li_last_error() returns a thread-local message.  Device data
+ *    is trusted: out-of-range block-table entries, token ids or lengths are
+ *    undefined behaviour.
+ *  - Only gfx950 devices are supported (LI_ERR_UNSUPPORTED otherwise).
+ *  - Calls are reentrant; the library holds no state besides the
+ *    thread-local error string and a per-device architecture check.
+ *  - Scores are never NaN for finite inputs.  Ordering of scores treats
+ *    -0.0 and +0.0 as equal.  "Top-k" always means: the first min(k, n)
+ *    positions under (score descending, token id ascending), returned as
+ *    ascending token ids and padded with -1.
+ */
+#ifndef LATENTINDEX_H
+#define LATENTINDEX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum li_status {
+  LI_OK = 0,
+  LI_ERR_INVALID = 1,      /* bad pointer, size or combination of arguments */
+  LI_ERR_UNSUPPORTED = 2,  /* valid request outside what this build handles */
+  LI_ERR_HIP = 3           /* a HIP runtime call or kernel launch failed */
+} li_status;
+
+typedef enum li_dtype {
+  LI_FP32 = 0,
+  LI_BF16 = 1,
+  LI_FP8_E4M3 = 2          /* OCP E4M3FN: bias 7, no inf, max 448 */
+} li_dtype;
+
+/*
+ * One layer group's paged latent cache (the shared cache of "Methodology",
+ * eq. 2).  Token t of sequence s lives in physical block
+ * block_table[s * max_blocks + t / block_size], row t % block_size.
+ *   data        device [n_blocks, block_size, r] of `dtype` (FP32, BF16 or
+ *               FP8_E4M3).  Row-major: one token's r values are contiguous.
+ *   scale       device fp32 [n_blocks, block_size]: per-token dequantisation
+ *               scale, FP8 only (NULL otherwise).  Value = code * scale.
+ *   block_table device int32 [n_seq, max_blocks] physical block ids.
+ *   block_size  must be 64.
+ *   r           latent width d_C; a multiple of 16, at most 1024.
+ */
+typedef struct li_cache {
+  void *data;
+  float *scale;
+  const int32_t *block_table;
+  int32_t n_seq;
+  int32_t max_blocks;
+  int32_t n_blocks;
+  int32_t block_size;
+  int32_t r;
+  li_dtype dtype;
+} li_cache;
+
+/* Thread-local message describing the last non-OK status of this thread. */
+const char *li_last_error(void);
+
+/* LI_OK if the current HIP device is a gfx950, LI_ERR_UNSUPPORTED if not. */
+li_status li_check_device(void);
+
+/*
+ * li_append_latent -- write new tokens' shared latents into the cache
+ * ("Methodology", eqs. 1-2: c_t = [Q_t P_R^T x_t ; P_N^T x_t], built once per
+ * token from the anchor layer's hidden state x_t).
+ *   x          device [n_tok, d_model] of x_dt (FP32 or BF16).
+ *   P          device [d_model, r] of x_dt; columns 0..r_R-1 are P_R, the
+ *              rest P_N.  NULL: x already is the latent (d_model must be r).
+ *   rope_theta device fp32 [r_R / 2] rotary frequencies, or NULL when
+ *              r_R == 0.  Pair (2j, 2j+1) of the R branch is rotated by the
+ *              angle pos * theta_j (as the complex number z_2j + i z_2j+1
+ *              times exp(i * angle)); the angle is formed in double.
+ *   seq_idx, pos device int32 [n_tok]: destination sequence and position.
+ *   cache      destination; BF16: round to nearest even; FP8: per token
+ *              amax = max|c|, scale = amax / 448, codes = RNE(c * (448 /
+ *              amax)) saturated to +-448 (amax == 0: scale 1, codes 0);
+ *              FP32: stored as is.  The projection accumulates in fp32.
+ *   ws         device workspace of li_append_workspace_bytes() bytes
+ *              (may be NULL when that is 0, i.e. when P is NULL).
+ * Tokens with equal (seq_idx, pos) race.  n_tok == 0 is a no-op.
+ */
+size_t li_append_workspace_bytes(int32_t n_tok, int32_t d_model, int32_t r, int32_t has_P);
+li_status li_append_latent(const void *x, li_dtype x_dt, int32_t n_tok, int32_t d_model,
+                           const void *P, const float *rope_theta, int32_t r_R,
+                           const int32_t *seq_idx, const int32_t *pos, const li_cache *cache,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * li_absorb_queries -- query-side decoder absorption ("Methodology", eq. 6):
+ * q~_{s,h} = D^T q_{s,h} and beta_{s,h} = q_{s,h}[nope_off:] . b.
+ *   q        device [n_q, H, d_I] of q_dt (FP32 or BF16).
+ *   Dt       device fp32 D transposed, [r, d_I] row-major; head h uses
+ *            Dt + h * Dt_head_stride (elements; 0 = one decoder for all
+ *            heads, the per-layer decoder of eq. 3).
+ *   b        device fp32 [d_I - nope_off] key bias on the NoPE coordinates,
+ *            or NULL for b = 0.  0 <= nope_off <= d_I.
+ *   q_tilde  device fp32 [n_q, H, r] (out).
+ *   beta     device fp32 [n_q, H] (out); may be NULL.
+ * Accumulates in fp32.  H <= 1024, d_I <= 1024, r <= 1024.
+ */
+li_status li_absorb_queries(const void *q, li_dtype q_dt, int32_t n_q, int32_t H, int32_t d_I,
+                            const float *Dt, int64_t Dt_head_stride, const float *b,
+                            int32_t nope_off, int32_t r, float *q_tilde, float *beta,
+                            void *stream);
+
+/*
+ * li_score -- score the shared cache for n_q queries ("Methodology", eq. 8):
+ * scores[i * ld + t] = sum_h w[i,h] ReLU(q~[i,h,:] . c_t + beta[i,h]) for
+ * 0 <= t < q_len[i], c_t read from sequence q_seq[i].  Entries at
+ * t >= q_len[i] are left untouched.
+ *   q_tilde  device [n_q, H, r] of qt_dt: FP32 (decode; absorbed queries as
+ *            li_absorb_queries returns them) or BF16 (stored absorbed queries).
+ *   w        device fp32 [n_q, H] head weights.
+ *   beta     device fp32 [n_q, H] or NULL (= 0).
+ *   q_seq    device int32 [n_q] sequence of each query.
+ *   q_len    device int32 [n_q] causal prefix length (1 <= q_len[i], and
+ *            q_len[i] <= max_len, and the sequence holds that many tokens).
+ *   max_len  host bound on every q_len (used to size the launch), <= ld.
+ *   scores   device fp32 [n_q, ld] (out).
+ * Arithmetic: products and sums in fp32 from exact operands.  An FP32 q~
+ * against a BF16 cache is carried as a pair of bf16 values (hi + lo), whose
+ * sum is within 2^-16 relative of q~; against an FP8 cache q~ is rounded to
+ * a single bf16.  The FP8 per-token scale multiplies the dot product before
+ * beta and ReLU.
+ */
+li_status li_score(const void *q_tilde, li_dtype qt_dt, const float *w, const float *beta,
+                   int32_t n_q, int32_t H, const int32_t *q_seq, const int32_t *q_len,
+                   int32_t max_len, const li_cache *cache, float *scores, int64_t ld,
+                   void *stream);
+
+/*
+ * li_topk -- each layer's own selection (the TopK definition after eq. 8:
+ * S = TopK_{t in V}(u_t, min(k, |V|))), per row of a score matrix.
+ *   scores    device fp32 [n_rows, ld]; row i is valid on [0, valid_len[i]).
+ *   valid_len device int32 [n_rows], each in [0, max_len].
+ *   max_len   host bound on valid_len, <= ld.
+ *   k         1 <= k <= 65536.
+ *   out_idx   device int32 [n_rows, k] (out): ascending token ids of the
+ *             first min(k, valid_len) positions by (score desc, id asc),
+ *             then -1.
+ *   out_val   device fp32 [n_rows, k] (out, may be NULL): the score of each
+ *             selected id; -inf in padding slots.
+ *   ws        device workspace of li_topk_workspace_bytes() bytes.
+ * Integer decisions are made on the fp32 bit patterns (no rounding).
+ */
+size_t li_topk_workspace_bytes(int32_t n_rows, int32_t max_len, int32_t k);
+li_status li_topk(const float *scores, int64_t ld, int32_t n_rows, const int32_t *valid_len,
+                  int32_t max_len, int32_t k, int32_t *out_idx, float *out_val, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/*
+ * li_hs_select -- a follower layer's hierarchical selection ("Hierarchical
+ * Selection" paragraph): rescore only the anchor's candidate set with the
+ * follower's own absorbed queries, then keep its top-k within the set.
+ *   cand        device int32 [n_q, B]: ascending token ids of query i's
+ *               candidates (e.g. li_topk with k = B on the anchor's scores),
+ *               padded at the end with -1.
+ *   q_tilde, qt_dt, w, beta, q_seq, H, cache: as for li_score.
+ *   k           1 <= k <= B.
+ *   out_idx     device int32 [n_q, k] (out): ascending token ids, -1 padded.
+ *   cand_scores device fp32 [n_q, B] (out, may be NULL): the follower's score
+ *               of each candidate slot; -inf in padding slots.
+ *   ws          device workspace of li_hs_workspace_bytes() bytes.
+ * Ties are broken by token id (equivalently by candidate slot).
+ */
+size_t li_hs_workspace_bytes(int32_t n_q, int32_t B, int32_t k);
+li_status li_hs_select(const int32_t *cand, int32_t B, const void *q_tilde, li_dtype qt_dt,
+                       const float *w, const float *beta, int32_t n_q, int32_t H,
+                       const int32_t *q_seq, const li_cache *cache, int32_t k, int32_t *out_idx,
+                       float *cand_scores, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LATENTINDEX_H */

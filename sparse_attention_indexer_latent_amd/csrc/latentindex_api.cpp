@@ -1,0 +1,226 @@
+// C ABI of the LatentIndex indexer: argument validation on the host, device
+// architecture check, and dispatch to the kernel launchers.  Nothing here
+// allocates, frees or synchronises device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/latentindex.h"
+#include "li_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+li_status fail(li_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+li_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return LI_OK;
+  return fail(LI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxDev = 64;
+std::mutex g_dev_mu;
+int g_dev_state[kMaxDev];  // 0 unknown, 1 gfx950, 2 other
+
+li_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDev) return fail(LI_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDeviceProperties");
+    g_dev_state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+  }
+  if (g_dev_state[dev] != 1) return fail(LI_ERR_UNSUPPORTED, "device %d is not a gfx950", dev);
+  return LI_OK;
+}
+
+bool dtype_ok(int d) { return d == LI_FP32 || d == LI_BF16 || d == LI_FP8_E4M3; }
+
+li_status check_cache(const li_cache *c, bool writable) {
+  if (!c) return fail(LI_ERR_INVALID, "cache is NULL");
+  if (!c->data || !c->block_table) return fail(LI_ERR_INVALID, "cache data/block_table is NULL");
+  if (!dtype_ok(c->dtype)) return fail(LI_ERR_INVALID, "cache dtype %d unknown", (int)c->dtype);
+  if (c->block_size != 64) return fail(LI_ERR_UNSUPPORTED, "block_size %d (only 64)", c->block_size);
+  if (c->r <= 0 || c->r > 1024) return fail(LI_ERR_INVALID, "r = %d out of range", c->r);
+  if (c->r % 16) return fail(LI_ERR_UNSUPPORTED, "r = %d not a multiple of 16", c->r);
+  if (c->n_seq <= 0 || c->max_blocks <= 0 || c->n_blocks <= 0)
+    return fail(LI_ERR_INVALID, "cache n_seq/max_blocks/n_blocks must be positive");
+  if ((c->dtype == LI_FP8_E4M3) != (c->scale != nullptr))
+    return fail(LI_ERR_INVALID, "scale must be given exactly for an FP8 cache");
+  (void)writable;
+  return LI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *li_last_error(void) { return g_err.c_str(); }
+
+li_status li_check_device(void) { return check_device(); }
+
+size_t li_append_workspace_bytes(int32_t n_tok, int32_t d_model, int32_t r, int32_t has_P) {
+  if (n_tok <= 0 || d_model <= 0 || r <= 0) return 0;
+  return li::append_ws_bytes(n_tok, d_model, r, has_P != 0);
+}
+
+li_status li_append_latent(const void *x, li_dtype x_dt, int32_t n_tok, int32_t d_model,
+                           const void *P, const float *rope_theta, int32_t r_R,
+                           const int32_t *seq_idx, const int32_t *pos, const li_cache *cache,
+                           void *ws, size_t ws_bytes, void *stream) {
+  li_status s = check_cache(cache, true);
+  if (s != LI_OK) return s;
+  if (n_tok < 0) return fail(LI_ERR_INVALID, "n_tok < 0");
+  if (x_dt != LI_FP32 && x_dt != LI_BF16) return fail(LI_ERR_INVALID, "x dtype must be FP32 or BF16");
+  if (d_model <= 0 || d_model > (1 << 20)) return fail(LI_ERR_INVALID, "d_model = %d out of range", d_model);
+  if (!P && d_model != cache->r) return fail(LI_ERR_INVALID, "P is NULL but d_model (%d) != r (%d)", d_model, cache->r);
+  if (r_R < 0 || r_R > cache->r || (r_R & 1)) return fail(LI_ERR_INVALID, "r_R = %d must be even and in [0, r]", r_R);
+  if ((r_R > 0) != (rope_theta != nullptr)) return fail(LI_ERR_INVALID, "rope_theta must be given exactly when r_R > 0");
+  if (n_tok == 0) return LI_OK;
+  if (!x || !seq_idx || !pos) return fail(LI_ERR_INVALID, "x/seq_idx/pos is NULL");
+  size_t need = li::append_ws_bytes(n_tok, d_model, cache->r, P != nullptr);
+  if (need && (!ws || ws_bytes < need)) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
+  if ((s = check_device()) != LI_OK) return s;
+  return hip_status(li::launch_append(x, x_dt, n_tok, d_model, P, rope_theta, r_R, seq_idx, pos,
+                                      *cache, ws, (hipStream_t)stream),
+                    "li_append_latent launch");
+}
+
+li_status li_absorb_queries(const void *q, li_dtype q_dt, int32_t n_q, int32_t H, int32_t d_I,
+                            const float *Dt, int64_t Dt_head_stride, const float *b,
+                            int32_t nope_off, int32_t r, float *q_tilde, float *beta,
+                            void *stream) {
+  if (q_dt != LI_FP32 && q_dt != LI_BF16) return fail(LI_ERR_INVALID, "q dtype must be FP32 or BF16");
+  if (n_q < 0) return fail(LI_ERR_INVALID, "n_q < 0");
+  if (H <= 0 || H > 1024 || d_I <= 0 || d_I > 1024 || r <= 0 || r > 1024)
+    return fail(LI_ERR_INVALID, "H/d_I/r out of range (1..1024)");
+  if (nope_off < 0 || nope_off > d_I) return fail(LI_ERR_INVALID, "nope_off out of [0, d_I]");
+  if (Dt_head_stride < 0) return fail(LI_ERR_INVALID, "Dt_head_stride < 0");
+  if (n_q == 0) return LI_OK;
+  if (!q || !Dt || !q_tilde) return fail(LI_ERR_INVALID, "q/Dt/q_tilde is NULL");
+  li_status s = check_device();
+  if (s != LI_OK) return s;
+  return hip_status(li::launch_absorb(q, q_dt, n_q, H, d_I, Dt, Dt_head_stride, b, nope_off, r,
+                                      q_tilde, beta, (hipStream_t)stream),
+                    "li_absorb_queries launch");
+}
+
+static li_status check_score_args(const void *q_tilde, li_dtype qt_dt, const float *w, int32_t n_q,
+                                  int32_t H, const int32_t *q_seq, const li_cache *cache) {
+  li_status s = check_cache(cache, false);
+  if (s != LI_OK) return s;
+  if (qt_dt != LI_FP32 && qt_dt != LI_BF16) return fail(LI_ERR_INVALID, "q_tilde dtype must be FP32 or BF16");
+  if (n_q < 0) return fail(LI_ERR_INVALID, "n_q < 0");
+  if (H <= 0 || H > 1024) return fail(LI_ERR_INVALID, "H = %d out of range", H);
+  if ((int64_t)H * cache->r > 16384) return fail(LI_ERR_UNSUPPORTED, "H * r = %d exceeds 16384", H * cache->r);
+  if (n_q > 0 && (!q_tilde || !w || !q_seq)) return fail(LI_ERR_INVALID, "q_tilde/w/q_seq is NULL");
+  return LI_OK;
+}
+
+li_status li_score(const void *q_tilde, li_dtype qt_dt, const float *w, const float *beta,
+                   int32_t n_q, int32_t H, const int32_t *q_seq, const int32_t *q_len,
+                   int32_t max_len, const li_cache *cache, float *scores, int64_t ld,
+                   void *stream) {
+  li_status s = check_score_args(q_tilde, qt_dt, w, n_q, H, q_seq, cache);
+  if (s != LI_OK) return s;
+  if (max_len < 0 || (int64_t)max_len > ld) return fail(LI_ERR_INVALID, "need 0 <= max_len <= ld");
+  if ((int64_t)max_len > (int64_t)cache->max_blocks * 64)
+    return fail(LI_ERR_INVALID, "max_len %d exceeds the block table (%d blocks)", max_len, cache->max_blocks);
+  if (n_q == 0 || max_len == 0) return LI_OK;
+  if (!q_len || !scores) return fail(LI_ERR_INVALID, "q_len/scores is NULL");
+  if ((s = check_device()) != LI_OK) return s;
+  li::CacheView cv = li::view_of(*cache);
+  hipError_t e;
+  if (li::score_mfma_supported(qt_dt, H, cv))
+    e = li::launch_score_mfma(q_tilde, qt_dt, w, beta, n_q, H, q_seq, q_len, max_len, cv, nullptr,
+                              0, scores, ld, (hipStream_t)stream);
+  else
+    e = li::launch_score_valu(q_tilde, qt_dt, w, beta, n_q, H, q_seq, q_len, max_len, cv, nullptr,
+                              0, scores, ld, (hipStream_t)stream);
+  return hip_status(e, "li_score launch");
+}
+
+size_t li_topk_workspace_bytes(int32_t n_rows, int32_t max_len, int32_t k) {
+  if (n_rows <= 0 || max_len <= 0 || k <= 0) return 0;
+  return li::topk_ws_bytes(n_rows, max_len, k);
+}
+
+li_status li_topk(const float *scores, int64_t ld, int32_t n_rows, const int32_t *valid_len,
+                  int32_t max_len, int32_t k, int32_t *out_idx, float *out_val, void *ws,
+                  size_t ws_bytes, void *stream) {
+  if (n_rows < 0) return fail(LI_ERR_INVALID, "n_rows < 0");
+  if (k <= 0 || k > 65536) return fail(LI_ERR_INVALID, "k = %d out of [1, 65536]", k);
+  if (max_len < 0 || (int64_t)max_len > ld) return fail(LI_ERR_INVALID, "need 0 <= max_len <= ld");
+  if (n_rows == 0) return LI_OK;
+  if (!scores || !valid_len || !out_idx) return fail(LI_ERR_INVALID, "scores/valid_len/out_idx is NULL");
+  size_t need = li::topk_ws_bytes(n_rows, max_len, k);
+  if (need && (!ws || ws_bytes < need)) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
+  li_status s = check_device();
+  if (s != LI_OK) return s;
+  return hip_status(li::launch_topk(scores, ld, n_rows, valid_len, nullptr, 0, max_len, k, out_idx,
+                                    out_val, ws, (hipStream_t)stream),
+                    "li_topk launch");
+}
+
+size_t li_hs_workspace_bytes(int32_t n_q, int32_t B, int32_t k) {
+  if (n_q <= 0 || B <= 0 || k <= 0) return 0;
+  size_t scores = (size_t)n_q * B * sizeof(float);
+  size_t counts = ((size_t)n_q * sizeof(int32_t) + 255) & ~(size_t)255;
+  return ((scores + 255) & ~(size_t)255) + counts + li::topk_ws_bytes(n_q, B, k);
+}
+
+li_status li_hs_select(const int32_t *cand, int32_t B, const void *q_tilde, li_dtype qt_dt,
+                       const float *w, const float *beta, int32_t n_q, int32_t H,
+                       const int32_t *q_seq, const li_cache *cache, int32_t k, int32_t *out_idx,
+                       float *cand_scores, void *ws, size_t ws_bytes, void *stream) {
+  li_status s = check_score_args(q_tilde, qt_dt, w, n_q, H, q_seq, cache);
+  if (s != LI_OK) return s;
+  if (B <= 0 || B > 65536) return fail(LI_ERR_INVALID, "B = %d out of [1, 65536]", B);
+  if (k <= 0) return fail(LI_ERR_INVALID, "k = %d must be positive", k);
+  if (B < k) return fail(LI_ERR_INVALID, "B (%d) < k (%d): the candidate set must hold k", B, k);
+  if (n_q == 0) return LI_OK;
+  if (!cand || !out_idx) return fail(LI_ERR_INVALID, "cand/out_idx is NULL");
+  size_t need = li_hs_workspace_bytes(n_q, B, k);
+  if (!ws || ws_bytes < need) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
+  if ((s = check_device()) != LI_OK) return s;
+  char *p = (char *)ws;
+  float *sc = (float *)p;
+  p += ((size_t)n_q * B * sizeof(float) + 255) & ~(size_t)255;
+  int32_t *counts = (int32_t *)p;
+  p += ((size_t)n_q * sizeof(int32_t) + 255) & ~(size_t)255;
+  void *tws = p;
+  float *dst = cand_scores ? cand_scores : sc;
+  hipStream_t st = (hipStream_t)stream;
+  li::CacheView cv = li::view_of(*cache);
+  hipError_t e = li::launch_count_valid(cand, n_q, B, counts, dst, st);
+  if (e == hipSuccess) {
+    if (li::score_mfma_supported(qt_dt, H, cv))
+      e = li::launch_score_mfma(q_tilde, qt_dt, w, beta, n_q, H, q_seq, counts, B, cv, cand, B, dst,
+                                B, st);
+    else
+      e = li::launch_score_valu(q_tilde, qt_dt, w, beta, n_q, H, q_seq, counts, B, cv, cand, B, dst,
+                                B, st);
+  }
+  if (e == hipSuccess)
+    e = li::launch_topk(dst, B, n_q, counts, cand, B, B, k, out_idx, nullptr, tws, st);
+  return hip_status(e, "li_hs_select launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Device-side helpers shared by the LatentIndex kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace li {
+
+constexpr int kWave = 64;
+constexpr int kPage = 64;  // tokens per cache block
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round a finite fp32 to bf16, nearest, ties to even.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// OCP E4M3FN code -> fp32 (exact).  0x7F/0xFF (NaN) never occur in a cache
+// written by the quantiser.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -v : v;
+}
+
+// fp32 -> OCP E4M3FN, round to nearest even, saturating at +-448.  The sign
+// bit follows the input (so -0.0 and tiny negatives give 0x80).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __uint_as_float(u & 0x7FFFFFFFu);
+  if (!(a < 448.0f)) return sign | 0x7Eu;
+  if (a < 0.015625f) {  // below 2^-6: subnormal codes m * 2^-9, m = 0..8 (8 = 2^-6)
+    return sign | (uint32_t)rintf(a * 512.0f);
+  }
+  const uint32_t ua = __float_as_uint(a);
+  uint32_t e = (ua >> 23) - 120u;  // biased e4m3 exponent, 1..15
+  uint32_t keep = (ua >> 20) & 7u;
+  const uint32_t rest = ua & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
+  if (keep == 8u) { keep = 0; ++e; }
+  return sign | (e << 3) | keep;
+}
+
+// Order-preserving map fp32 -> uint32 (larger float => larger key); -0.0 is
+// mapped like +0.0 so the two tie.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Load a latent row element range as fp32 (generic paths).
+__device__ __forceinline__ float load_latent(const void *data, int dtype, int64_t off) {
+  if (dtype == 0) return ((const float *)data)[off];
+  if (dtype == 1) return bf16_bits_to_f32(((const uint16_t *)data)[off]);
+  return e4m3_to_f32(((const uint8_t *)data)[off]);
+}
+
+}  // namespace li

@@ -1,0 +1,68 @@
+// Host-side launcher interface between the C ABI layer (latentindex_api.cpp)
+// and the kernel translation units.  Every launcher enqueues on `st`, assumes
+// its arguments were validated by the ABI layer, and returns the status of
+// the launch (hipGetLastError after enqueue).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/latentindex.h"
+
+namespace li {
+
+// Plain-value view of a validated li_cache, passed to kernels by value.
+struct CacheView {
+  const void *data;
+  const float *scale;
+  const int32_t *block_table;
+  int32_t max_blocks;
+  int32_t r;
+  int32_t dtype;  // li_dtype
+};
+
+inline CacheView view_of(const li_cache &c) {
+  return CacheView{c.data, c.scale, c.block_table, c.max_blocks, c.r, (int32_t)c.dtype};
+}
+
+// append.hip
+size_t append_ws_bytes(int n_tok, int d_model, int r, bool has_P);
+hipError_t launch_append(const void *x, int x_dt, int n_tok, int d_model, const void *P,
+                         const float *theta, int r_R, const int32_t *seq_idx,
+                         const int32_t *pos, const li_cache &cache, void *ws, hipStream_t st);
+
+// absorb.hip
+hipError_t launch_absorb(const void *q, int q_dt, int n_q, int H, int d_I, const float *Dt,
+                         int64_t Dt_head_stride, const float *b, int nope_off, int r,
+                         float *q_tilde, float *beta, hipStream_t st);
+
+// score_valu.hip: generic vector-ALU scorer, any supported dtype.
+// When `cand` is non-null the tokens of query i are cand[i*B + j] (j < B,
+// stopping at the first -1) and results go to out[i*ld + j]; otherwise
+// token t < q_len[i] goes to out[i*ld + t].
+hipError_t launch_score_valu(const void *q_tilde, int qt_dt, const float *w, const float *beta,
+                             int n_q, int H, const int32_t *q_seq, const int32_t *q_len,
+                             int max_len, const CacheView &cv, const int32_t *cand, int B,
+                             float *out, int64_t ld, hipStream_t st);
+
+// score_mfma.hip: matrix-core scorer for H == 64 and bf16/fp8 caches.
+bool score_mfma_supported(int qt_dt, int H, const CacheView &cv);
+hipError_t launch_score_mfma(const void *q_tilde, int qt_dt, const float *w, const float *beta,
+                             int n_q, int H, const int32_t *q_seq, const int32_t *q_len,
+                             int max_len, const CacheView &cv, const int32_t *cand, int B,
+                             float *out, int64_t ld, hipStream_t st);
+
+// topk.hip.  `ids` (may be null) maps a row position j to the id reported
+// for it (row i uses ids + i*ids_ld); positions are ordered by id exactly as
+// by j (ids ascending), so ties break by position.
+size_t topk_ws_bytes(int n_rows, int max_len, int k);
+hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
+                       const int32_t *ids, int64_t ids_ld, int max_len, int k, int32_t *out_idx,
+                       float *out_val, void *ws, hipStream_t st);
+
+// hs.hip: count valid candidates per row (entries before the first -1).
+hipError_t launch_count_valid(const int32_t *cand, int n_q, int B, int32_t *counts,
+                              float *cand_scores, hipStream_t st);
+
+}  // namespace li

@@ -1,0 +1,113 @@
+// Vector-ALU scorer for eq. (8) of the LatentIndex summary ("Methodology"):
+// u_t = sum_h w_h ReLU(q~_h . c_t + beta_h).
+//
+// This path serves shapes where the head x latent product is small (H * r of a
+// few hundred: about 4 flop per cached byte, far below the fp32 VALU ridge),
+// any cache dtype, and shapes the matrix-core scorer does not take.  Each
+// workgroup takes a tile of TT tokens of one query: the query's absorbed
+// vectors and the tile (dequantised to fp32, row stride r+1 so that lanes
+// reading different tokens hit different banks) are staged in LDS; thread
+// (token, head group) accumulates its heads, and the head groups are summed
+// in a fixed order.
+#include "li_device.h"
+#include "li_internal.h"
+
+namespace li {
+namespace {
+
+__global__ void __launch_bounds__(256)
+score_valu_kernel(const void *__restrict__ q_tilde, int qt_dt, const float *__restrict__ w,
+                  const float *__restrict__ beta, int H, const int32_t *__restrict__ q_seq,
+                  const int32_t *__restrict__ q_len, CacheView cv, const int32_t *__restrict__ cand,
+                  int B, float *__restrict__ out, int64_t ld, int TT) {
+  extern __shared__ float lds[];
+  const int r = cv.r;
+  const int i = blockIdx.y;
+  const int t0 = blockIdx.x * TT;
+  const int n = q_len[i];
+  if (t0 >= n) return;  // uniform across the workgroup, before any barrier
+  const int nt = min(TT, n - t0);
+  float *qs = lds;                      // [H][r]
+  float *wsm = qs + H * r;              // [H]
+  float *bsm = wsm + H;                 // [H]
+  float *ssm = bsm + H;                 // [TT] per-token scale
+  float *cs = ssm + TT;                 // [TT][r + 1]
+  float *red = cs + TT * (r + 1);       // [256 / TT][TT]
+  const int tid = threadIdx.x;
+  const int64_t qoff = (int64_t)i * H * r;
+  for (int e = tid; e < H * r; e += 256)
+    qs[e] = qt_dt == LI_FP32 ? ((const float *)q_tilde)[qoff + e]
+                             : bf16_bits_to_f32(((const uint16_t *)q_tilde)[qoff + e]);
+  for (int h = tid; h < H; h += 256) {
+    wsm[h] = w[(int64_t)i * H + h];
+    bsm[h] = beta ? beta[(int64_t)i * H + h] : 0.f;
+  }
+  const int seq = q_seq[i];
+  const int32_t *bt = cv.block_table + (int64_t)seq * cv.max_blocks;
+  for (int tok = tid; tok < TT; tok += 256) {
+    float sc = 1.f;
+    if (tok < nt && cv.dtype == LI_FP8_E4M3) {
+      const int t = cand ? cand[(int64_t)i * B + t0 + tok] : t0 + tok;
+      sc = cv.scale[(int64_t)bt[t / kPage] * kPage + t % kPage];
+    }
+    ssm[tok] = sc;
+  }
+  for (int e = tid; e < TT * r; e += 256) {
+    const int tok = e / r, j = e % r;
+    float v = 0.f;
+    if (tok < nt) {
+      const int t = cand ? cand[(int64_t)i * B + t0 + tok] : t0 + tok;
+      const int64_t row = (int64_t)bt[t / kPage] * kPage + t % kPage;
+      v = load_latent(cv.data, cv.dtype, row * r + j);
+    }
+    cs[tok * (r + 1) + j] = v;
+  }
+  __syncthreads();
+  const int n_groups = 256 / TT;
+  const int tok = tid % TT, hg = tid / TT;
+  const float *c = cs + tok * (r + 1);
+  const float sc = ssm[tok];
+  float acc = 0.f;
+  for (int h = hg; h < H; h += n_groups) {
+    const float *qh = qs + h * r;
+    float dot = 0.f;
+    for (int j = 0; j < r; ++j) dot = fmaf(qh[j], c[j], dot);
+    const float x = fmaf(dot, sc, bsm[h]);
+    acc = fmaf(wsm[h], fmaxf(x, 0.f), acc);
+  }
+  red[hg * TT + tok] = acc;
+  __syncthreads();
+  if (tid < nt) {
+    float s = 0.f;
+    for (int g = 0; g < n_groups; ++g) s += red[g * TT + tid];
+    out[(int64_t)i * ld + t0 + tid] = s;
+  }
+}
+
+size_t valu_lds_bytes(int H, int r, int TT) {
+  return sizeof(float) * ((size_t)H * r + 2 * H + TT + (size_t)TT * (r + 1) + 256);
+}
+
+}  // namespace
+
+hipError_t launch_score_valu(const void *q_tilde, int qt_dt, const float *w, const float *beta,
+                             int n_q, int H, const int32_t *q_seq, const int32_t *q_len,
+                             int max_len, const CacheView &cv, const int32_t *cand, int B,
+                             float *out, int64_t ld, hipStream_t st) {
+  int TT = 64;
+  while (TT > 4 && valu_lds_bytes(H, cv.r, TT) > 160 * 1024) TT >>= 1;
+  const size_t lds = valu_lds_bytes(H, cv.r, TT);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void *)score_valu_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr_set = true;
+  }
+  dim3 grid((max_len + TT - 1) / TT, n_q);
+  score_valu_kernel<<<grid, 256, lds, st>>>(q_tilde, qt_dt, w, beta, H, q_seq, q_len, cv, cand, B,
+                                            out, ld, TT);
+  return hipGetLastError();
+}
+
+}  // namespace li

@@ -1,0 +1,263 @@
+"""Thin Python binding of liblatentindex.so (include/latentindex.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+Tensors must be contiguous device tensors of the current CUDA (HIP) device;
+work is enqueued on torch's current stream.  Outputs that are not passed in
+are allocated with torch.  A missing library raises immediately: there is no
+fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblatentindex.so")
+HEADER = os.path.join(HERE, "..", "include", "latentindex.h")
+
+LI_OK, LI_ERR_INVALID, LI_ERR_UNSUPPORTED, LI_ERR_HIP = 0, 1, 2, 3
+LI_FP32, LI_BF16, LI_FP8_E4M3 = 0, 1, 2
+BLOCK = 64
+
+
+class LiError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+class LiCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("n_seq", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+        ("n_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("r", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "li_last_error": (ctypes.c_char_p, []),
+    "li_check_device": (_I32, []),
+    "li_append_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "li_append_latent": (_I32, [_P, _I32, _I32, _I32, _P, _P, _I32, _P, _P,
+                                ctypes.POINTER(LiCacheStruct), _P, _SZ, _P]),
+    "li_absorb_queries": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _I64, _P, _I32, _I32, _P, _P, _P]),
+    "li_score": (_I32, [_P, _I32, _P, _P, _I32, _I32, _P, _P, _I32,
+                        ctypes.POINTER(LiCacheStruct), _P, _I64, _P]),
+    "li_topk_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "li_topk": (_I32, [_P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "li_hs_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "li_hs_select": (_I32, [_P, _I32, _P, _I32, _P, _P, _I32, _I32, _P,
+                            ctypes.POINTER(LiCacheStruct), _I32, _P, _P, _P, _SZ, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_attention_indexer_latent_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Function names declared in include/latentindex.h."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(li_[a-z_0-9]+)\s*\(", txt)))
+
+
+def _check(status: int) -> None:
+    if status != LI_OK:
+        raise LiError(status, lib().li_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LI_FP32
+    if t.dtype == torch.bfloat16:
+        return LI_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return LI_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+class Cache:
+    """A paged shared latent cache of one layer group (device tensors).
+
+    data: [n_blocks, 64, r] float32 | bfloat16 | uint8 (E4M3FN codes)
+    scale: [n_blocks, 64] float32 for fp8, else None
+    block_table: int32 [n_seq, max_blocks]
+    """
+
+    def __init__(self, data: torch.Tensor, block_table: torch.Tensor,
+                 scale: Optional[torch.Tensor] = None):
+        _need(data, "cache data")
+        _need(block_table, "block_table", torch.int32)
+        if scale is not None:
+            _need(scale, "scale", torch.float32)
+        self.data, self.block_table, self.scale = data, block_table, scale
+        self.dtype = _dtype_code(data)
+        self._s = LiCacheStruct(
+            data=data.data_ptr(), scale=_ptr(scale), block_table=block_table.data_ptr(),
+            n_seq=block_table.shape[0], max_blocks=block_table.shape[1],
+            n_blocks=data.shape[0], block_size=data.shape[1], r=data.shape[2], dtype=self.dtype)
+
+    @classmethod
+    def empty(cls, n_blocks: int, r: int, dtype: str, block_table: torch.Tensor, device="cuda"):
+        tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[dtype]
+        data = torch.empty((n_blocks, BLOCK, r), dtype=tdt, device=device)
+        scale = torch.empty((n_blocks, BLOCK), dtype=torch.float32, device=device) \
+            if dtype == "fp8" else None
+        return cls(data, block_table, scale)
+
+    @property
+    def r(self) -> int:
+        return self.data.shape[2]
+
+    def struct(self):
+        return ctypes.byref(self._s)
+
+
+def append_latent(x: torch.Tensor, cache: Cache, seq_idx: torch.Tensor, pos: torch.Tensor,
+                  P: Optional[torch.Tensor] = None, rope_theta: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None) -> None:
+    _need(x, "x", (torch.float32, torch.bfloat16))
+    _need(seq_idx, "seq_idx", torch.int32)
+    _need(pos, "pos", torch.int32)
+    n_tok, d_model = x.shape
+    if P is not None:
+        _need(P, "P", x.dtype)
+    r_R = 0
+    if rope_theta is not None:
+        _need(rope_theta, "rope_theta", torch.float32)
+        r_R = 2 * rope_theta.numel()
+    need = lib().li_append_workspace_bytes(n_tok, d_model, cache.r, int(P is not None))
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib().li_append_latent(x.data_ptr(), _dtype_code(x), n_tok, d_model, _ptr(P),
+                                  _ptr(rope_theta), r_R, seq_idx.data_ptr(), pos.data_ptr(),
+                                  cache.struct(), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream()))
+
+
+def absorb_queries(q: torch.Tensor, Dt: torch.Tensor, b: Optional[torch.Tensor] = None,
+                   nope_off: Optional[int] = None, q_tilde: Optional[torch.Tensor] = None,
+                   beta: Optional[torch.Tensor] = None, per_head: bool = False):
+    """q [n_q, H, d_I]; Dt [r, d_I] (or [H, r, d_I] with per_head) -> (q~ [n_q,H,r], beta [n_q,H])."""
+    _need(q, "q", (torch.float32, torch.bfloat16))
+    _need(Dt, "Dt", torch.float32)
+    n_q, H, d_I = q.shape
+    r = Dt.shape[-2]
+    stride = r * d_I if per_head else 0
+    no = d_I if nope_off is None else nope_off
+    if b is not None:
+        _need(b, "b", torch.float32)
+    if q_tilde is None:
+        q_tilde = torch.empty((n_q, H, r), dtype=torch.float32, device=q.device)
+    if beta is None:
+        beta = torch.empty((n_q, H), dtype=torch.float32, device=q.device)
+    _check(lib().li_absorb_queries(q.data_ptr(), _dtype_code(q), n_q, H, d_I, Dt.data_ptr(),
+                                   stride, _ptr(b), no, r, q_tilde.data_ptr(), _ptr(beta),
+                                   _stream()))
+    return q_tilde, beta
+
+
+def score(q_tilde: torch.Tensor, w: torch.Tensor, beta: Optional[torch.Tensor],
+          q_seq: torch.Tensor, q_len: torch.Tensor, max_len: int, cache: Cache,
+          scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(q_tilde, "q_tilde", (torch.float32, torch.bfloat16))
+    _need(w, "w", torch.float32)
+    _need(q_seq, "q_seq", torch.int32)
+    _need(q_len, "q_len", torch.int32)
+    if beta is not None:
+        _need(beta, "beta", torch.float32)
+    n_q, H, _ = q_tilde.shape
+    if scores is None:
+        scores = torch.empty((n_q, max(1, max_len)), dtype=torch.float32, device=q_tilde.device)
+    _need(scores, "scores", torch.float32)
+    _check(lib().li_score(q_tilde.data_ptr(), _dtype_code(q_tilde), w.data_ptr(), _ptr(beta), n_q,
+                          H, q_seq.data_ptr(), q_len.data_ptr(), max_len, cache.struct(),
+                          scores.data_ptr(), scores.shape[1], _stream()))
+    return scores
+
+
+def topk(scores: torch.Tensor, valid_len: torch.Tensor, max_len: int, k: int,
+         out_idx: Optional[torch.Tensor] = None, out_val: Optional[torch.Tensor] = None,
+         ws: Optional[torch.Tensor] = None, want_val: bool = False):
+    _need(scores, "scores", torch.float32)
+    _need(valid_len, "valid_len", torch.int32)
+    n_rows = scores.shape[0]
+    if out_idx is None:
+        out_idx = torch.empty((n_rows, k), dtype=torch.int32, device=scores.device)
+    if out_val is None and want_val:
+        out_val = torch.empty((n_rows, k), dtype=torch.float32, device=scores.device)
+    need = lib().li_topk_workspace_bytes(n_rows, max_len, k)
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    _check(lib().li_topk(scores.data_ptr(), scores.shape[1], n_rows, valid_len.data_ptr(), max_len,
+                         k, out_idx.data_ptr(), _ptr(out_val), _ptr(ws),
+                         0 if ws is None else ws.numel(), _stream()))
+    return (out_idx, out_val) if want_val else out_idx
+
+
+def hs_workspace(n_q: int, B: int, k: int, device="cuda") -> torch.Tensor:
+    return torch.empty(lib().li_hs_workspace_bytes(n_q, B, k), dtype=torch.uint8, device=device)
+
+
+def hs_select(cand: torch.Tensor, q_tilde: torch.Tensor, w: torch.Tensor,
+              beta: Optional[torch.Tensor], q_seq: torch.Tensor, cache: Cache, k: int,
+              out_idx: Optional[torch.Tensor] = None, cand_scores: Optional[torch.Tensor] = None,
+              ws: Optional[torch.Tensor] = None, want_scores: bool = False):
+    _need(cand, "cand", torch.int32)
+    _need(q_tilde, "q_tilde", (torch.float32, torch.bfloat16))
+    n_q, B = cand.shape
+    H = q_tilde.shape[1]
+    if out_idx is None:
+        out_idx = torch.empty((n_q, k), dtype=torch.int32, device=cand.device)
+    if cand_scores is None and want_scores:
+        cand_scores = torch.empty((n_q, B), dtype=torch.float32, device=cand.device)
+    if ws is None:
+        ws = hs_workspace(n_q, B, k, cand.device)
+    _check(lib().li_hs_select(cand.data_ptr(), B, q_tilde.data_ptr(), _dtype_code(q_tilde),
+                              w.data_ptr(), _ptr(beta), n_q, H, q_seq.data_ptr(), cache.struct(),
+                              k, out_idx.data_ptr(), _ptr(cand_scores), ws.data_ptr(), ws.numel(),
+                              _stream()))
+    return (out_idx, cand_scores) if want_scores else out_idx

@@ -1,0 +1,136 @@
+"""Device-side driver of one layer group's decode step.
+
+Uploads a synthetic workload, fills its paged latent cache through
+li_append_latent, and runs the two decode variants of the LatentIndex
+summary ("Methodology"):
+
+* full scan: every layer absorbs its queries (eq. 6), scores the whole shared
+  cache (eq. 8) and keeps its own top-k;
+* hierarchical selection: the anchor scores everything and proposes its
+  top-B candidates; each follower rescores and refines only those.
+
+Every buffer a step touches is allocated up front, so a step allocates
+nothing (and can be captured in a HIP graph).  All arithmetic runs in the
+library's kernels; torch only owns memory and the stream.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import ops
+from .workloads import BLOCK, Workload
+
+
+def _t(a, dtype=None, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dtype)
+
+
+class DeviceWorkload:
+    def __init__(self, wl: Workload, device="cuda", hold_last: bool = True):
+        """Upload wl.  With hold_last the cache receives positions 0..L-2 of
+        each sequence; the decode step appends position L-1 (then scores L)."""
+        self.wl = wl
+        self.device = device
+        bt = _t(wl.block_table, torch.int32, device)
+        self.cache = ops.Cache.empty(wl.n_phys_blocks, wl.r, wl.cache_dtype, bt, device)
+        self.q_seq = _t(wl.q_seq, torch.int32, device)
+        self.q_len = _t(wl.q_len, torch.int32, device)
+        self.max_len = int(wl.q_len.max())
+        G, H = wl.G, wl.H
+        self.Dt = [_t(wl.Dt[l], torch.float32, device) for l in range(G)]
+        self.b = [_t(wl.b[l], torch.float32, device) if wl.b.shape[1] else None for l in range(G)]
+        self.w = [_t(wl.w[l], torch.float32, device) for l in range(G)]
+        self.q = [_t(wl.q[l], torch.float32, device) for l in range(G)] if wl.q is not None else None
+        self.fill_cache(hold_last)
+        n_q = wl.n_q
+        # last token of every sequence: appended by each decode step
+        last = np.stack([wl.latent(s)[int(wl.lens[s]) - 1] for s in range(wl.n_seq)])
+        self.x_new = _t(last, torch.float32, device)
+        self.new_seq = torch.arange(wl.n_seq, dtype=torch.int32, device=device)
+        self.new_pos = _t((wl.lens - 1).astype(np.int32), torch.int32, device)
+        # per-step buffers
+        r = wl.r
+        self.q_tilde = torch.empty((n_q, H, r), dtype=torch.float32, device=device)
+        self.beta = torch.empty((n_q, H), dtype=torch.float32, device=device)
+        self.scores = torch.empty((n_q, self.max_len), dtype=torch.float32, device=device)
+        self.sel = torch.empty((G, n_q, wl.k), dtype=torch.int32, device=device)
+        self.topk_ws = self._ws(ops.lib().li_topk_workspace_bytes(n_q, self.max_len, max(wl.k, wl.B or 0)))
+        if wl.B:
+            self.cand = torch.empty((n_q, wl.B), dtype=torch.int32, device=device)
+            self.hs_sel = torch.empty((G, n_q, wl.k), dtype=torch.int32, device=device)
+            self.cand_scores = torch.empty((G, n_q, wl.B), dtype=torch.float32, device=device)
+            self.hs_ws = ops.hs_workspace(n_q, wl.B, wl.k, device)
+
+    def _ws(self, n):
+        return torch.empty(n, dtype=torch.uint8, device=self.device) if n else None
+
+    def fill_cache(self, hold_last: bool = True, chunk: int = 1 << 16) -> None:
+        wl = self.wl
+        for s in range(wl.n_seq):
+            lat = wl.latent(s)
+            L = int(wl.lens[s]) - (1 if hold_last else 0)
+            for a in range(0, L, chunk):
+                b = min(L, a + chunk)
+                x = _t(lat[a:b], torch.float32, self.device)
+                seq = torch.full((b - a,), s, dtype=torch.int32, device=self.device)
+                pos = torch.arange(a, b, dtype=torch.int32, device=self.device)
+                ops.append_latent(x, self.cache, seq, pos)
+        torch.cuda.synchronize()
+
+    # ---- steps -------------------------------------------------------------
+    def append(self) -> None:
+        ops.append_latent(self.x_new, self.cache, self.new_seq, self.new_pos)
+
+    def absorb(self, layer: int) -> None:
+        ops.absorb_queries(self.q[layer], self.Dt[layer], self.b[layer], self.wl.nope_off,
+                           q_tilde=self.q_tilde, beta=self.beta)
+
+    def score(self, layer: int, scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+        return ops.score(self.q_tilde, self.w[layer], self.beta, self.q_seq, self.q_len,
+                         self.max_len, self.cache, scores=self.scores if scores is None else scores)
+
+    def full_step(self, append: bool = True) -> None:
+        """Full-scan decode step of the group: per layer absorb, score, top-k."""
+        if append:
+            self.append()
+        for l in range(self.wl.G):
+            self.absorb(l)
+            self.score(l)
+            ops.topk(self.scores, self.q_len, self.max_len, self.wl.k, out_idx=self.sel[l],
+                     ws=self.topk_ws)
+
+    def hs_step(self, append: bool = True, keep_scores: bool = False) -> None:
+        """Hierarchical-selection decode step: the anchor scans and proposes
+        its top-B, followers rescore and refine within the candidates."""
+        wl = self.wl
+        if append:
+            self.append()
+        self.absorb(0)
+        self.score(0)
+        ops.topk(self.scores, self.q_len, self.max_len, wl.B, out_idx=self.cand, ws=self.topk_ws)
+        ops.topk(self.scores, self.q_len, self.max_len, wl.k, out_idx=self.hs_sel[0],
+                 ws=self.topk_ws)
+        for l in range(1, wl.G):
+            self.absorb(l)
+            ops.hs_select(self.cand, self.q_tilde, self.w[l], self.beta, self.q_seq, self.cache,
+                          wl.k, out_idx=self.hs_sel[l],
+                          cand_scores=self.cand_scores[l] if keep_scores else None,
+                          ws=self.hs_ws)
+
+
+def read_cache_rows(cache: ops.Cache, block_table: np.ndarray, s: int, L: int):
+    """Host copy of sequence s's first L stored rows (and scales) in token order."""
+    nblk = (L + BLOCK - 1) // BLOCK
+    blocks = torch.as_tensor(block_table[s, :nblk].astype(np.int64), device=cache.data.device)
+    src = cache.data.view(torch.int16) if cache.data.dtype == torch.bfloat16 else cache.data
+    data = src.index_select(0, blocks).reshape(nblk * BLOCK, -1)[:L].cpu().numpy()
+    if cache.data.dtype == torch.bfloat16:
+        data = data.view(np.uint16)
+    scale = None
+    if cache.scale is not None:
+        scale = cache.scale.index_select(0, blocks).reshape(-1)[:L].cpu().numpy()
+    return data, scale

@@ -11,3 +11,18 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: large CPU-side oracle work")
+
+
+def pytest_collection_modifyitems(config, items):
+    """Build the library if nothing is built; skip GPU tests without a GPU."""
+    import torch
+
+    lib = os.path.join(ROOT, "sparse_attention_indexer_latent_amd", "liblatentindex.so")
+    if not os.path.exists(lib):
+        from sparse_attention_indexer_latent_amd import build
+        build.build()
+    if not torch.cuda.is_available():
+        skip = pytest.mark.skip(reason="no GPU in this environment")
+        for it in items:
+            if "gpu" in it.keywords:
+                it.add_marker(skip)

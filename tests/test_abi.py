@@ -1,0 +1,70 @@
+"""C-ABI library: it loads, exports every declared symbol, and rejects bad
+arguments on the host before touching any device (CPU only)."""
+
+import ctypes
+
+import pytest
+
+from sparse_attention_indexer_latent_amd import ops
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ops.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = ops.header_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    for core in ["li_append_latent", "li_absorb_queries", "li_score", "li_topk", "li_hs_select"]:
+        assert core in names
+
+
+def _cache(**kw):
+    c = dict(data=1, scale=None, block_table=2, n_seq=1, max_blocks=4, n_blocks=4, block_size=64,
+             r=256, dtype=ops.LI_BF16)
+    c.update(kw)
+    return ops.LiCacheStruct(**c)
+
+
+def test_validation_errors_are_host_side(L):
+    FAKE = 0x1000  # never dereferenced: every case fails validation first
+    assert L.li_topk(FAKE, 100, 1, FAKE, 100, 0, FAKE, None, None, 0, None) == ops.LI_ERR_INVALID
+    assert b"k = 0" in L.li_last_error()
+    assert L.li_topk(FAKE, 10, 1, FAKE, 100, 5, FAKE, None, None, 0, None) == ops.LI_ERR_INVALID
+    assert L.li_topk(None, 10, 1, FAKE, 10, 5, FAKE, None, None, 0, None) == ops.LI_ERR_INVALID
+    # no rows: a no-op that succeeds without a device
+    assert L.li_topk(None, 10, 0, None, 10, 5, None, None, None, 0, None) == ops.LI_OK
+    c = _cache(block_size=32)
+    assert L.li_score(FAKE, ops.LI_FP32, FAKE, None, 1, 64, FAKE, FAKE, 64, ctypes.byref(c), FAKE,
+                      64, None) == ops.LI_ERR_UNSUPPORTED
+    c = _cache(r=250)
+    assert L.li_score(FAKE, ops.LI_FP32, FAKE, None, 1, 64, FAKE, FAKE, 64, ctypes.byref(c), FAKE,
+                      64, None) == ops.LI_ERR_UNSUPPORTED
+    c = _cache(dtype=ops.LI_FP8_E4M3)  # fp8 without a scale array
+    assert L.li_score(FAKE, ops.LI_FP32, FAKE, None, 1, 64, FAKE, FAKE, 64, ctypes.byref(c), FAKE,
+                      64, None) == ops.LI_ERR_INVALID
+    c = _cache()
+    assert L.li_score(FAKE, ops.LI_FP32, FAKE, None, 1, 64, FAKE, FAKE, 300, ctypes.byref(c), FAKE,
+                      300, None) == ops.LI_ERR_INVALID          # max_len beyond the block table
+    assert L.li_score(FAKE, ops.LI_FP8_E4M3, FAKE, None, 1, 64, FAKE, FAKE, 64, ctypes.byref(c),
+                      FAKE, 64, None) == ops.LI_ERR_INVALID     # q~ cannot be fp8
+    # HS: B < k is invalid (the candidate set must hold k)
+    assert L.li_hs_select(FAKE, 100, FAKE, ops.LI_FP32, FAKE, None, 1, 64, FAKE, ctypes.byref(c),
+                          200, FAKE, None, FAKE, 1 << 30, None) == ops.LI_ERR_INVALID
+    assert b"B (100) < k (200)" in L.li_last_error()
+    # append: P NULL requires d_model == r; odd r_R
+    assert L.li_append_latent(FAKE, ops.LI_FP32, 4, 100, None, None, 0, FAKE, FAKE,
+                              ctypes.byref(c), None, 0, None) == ops.LI_ERR_INVALID
+    assert L.li_append_latent(FAKE, ops.LI_FP32, 4, 256, None, FAKE, 3, FAKE, FAKE,
+                              ctypes.byref(c), None, 0, None) == ops.LI_ERR_INVALID
+    assert L.li_absorb_queries(FAKE, ops.LI_FP32, 1, 64, 128, FAKE, 0, None, 129, 256, FAKE, None,
+                               None) == ops.LI_ERR_INVALID
+
+
+def test_workspace_sizes(L):
+    assert L.li_append_workspace_bytes(4, 7168, 256, 0) == 0
+    assert L.li_append_workspace_bytes(4, 7168, 256, 1) > 0
+    assert L.li_hs_workspace_bytes(4, 8192, 2048) >= 4 * 8192 * 4

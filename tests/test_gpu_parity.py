@@ -1,0 +1,292 @@
+"""GPU parity of every C-ABI call against the CPU oracle (MI355X only)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from sparse_attention_indexer_latent_amd import ops
+from sparse_attention_indexer_latent_amd import workloads as W
+from sparse_attention_indexer_latent_amd.runtime import DeviceWorkload, read_cache_rows
+
+from parity_util import (RTOL_BF16, RTOL_FP8, RTOL_FP32, assert_scores_close,
+                         assert_selection_band, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_device_is_gfx950():
+    assert ops.lib().li_check_device() == ops.LI_OK
+
+
+# ------------------------------------------------------------------ append ---
+
+@pytest.mark.parametrize("dtype,r", [("fp32", 32), ("bf16", 256), ("fp8", 256), ("fp8", 64)])
+def test_append_matches_oracle_quantiser_bit_exact(dtype, r):
+    say(f"append exact dtype={dtype} r={r}")
+    wl = W.small_decode(1, n_seq=3, lens=[1, 130, 777], r=r, H=8, d_I=16, cache_dtype=dtype,
+                        plant=4, factor=4.0)
+    dw = DeviceWorkload(wl, hold_last=False)
+    for s in range(wl.n_seq):
+        L = int(wl.lens[s])
+        data, scale = read_cache_rows(dw.cache, wl.block_table, s, L)
+        stored, oscale, _ = O.store_latent(wl.latent(s), dtype)
+        assert np.array_equal(np.asarray(data).view(stored.dtype).reshape(stored.shape), stored), s
+        if dtype == "fp8":
+            assert np.array_equal(scale.view(np.uint32), oscale.view(np.uint32)), s
+
+
+def test_append_zero_row_and_extremes_fp8():
+    say("append fp8 zero row and extremes")
+    r = 64
+    rows = np.zeros((5, r), np.float32)
+    rows[1, 3] = 1e-30
+    rows[2] = np.linspace(-1000, 1000, r, dtype=np.float32)
+    rows[3, :] = -2.5
+    rows[4] = np.random.default_rng(0).standard_normal(r).astype(np.float32) * 1e-5
+    bt = torch.arange(1, dtype=torch.int32, device="cuda").reshape(1, 1)
+    cache = ops.Cache.empty(1, r, "fp8", bt)
+    ops.append_latent(torch.from_numpy(rows).cuda(), cache, torch.zeros(5, dtype=torch.int32, device="cuda"),
+                      torch.arange(5, dtype=torch.int32, device="cuda"))
+    codes, oscale = O.quantize_fp8(rows)
+    got = cache.data[0, :5].cpu().numpy()
+    assert np.array_equal(got, codes)
+    assert np.array_equal(cache.scale[0, :5].cpu().numpy().view(np.uint32), oscale.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp8"])
+@pytest.mark.parametrize("xdt", [torch.float32, torch.bfloat16])
+def test_append_projection_and_rope(dtype, xdt):
+    say(f"append with P and rope dtype={dtype} x={xdt}")
+    rng = np.random.default_rng(5)
+    n_tok, d_model, r, r_R = 37, 300, 64, 16
+    x = rng.standard_normal((n_tok, d_model)).astype(np.float32)
+    P = (rng.standard_normal((d_model, r)) / np.sqrt(d_model)).astype(np.float32)
+    theta = (10000.0 ** (-np.arange(r_R // 2) * 2.0 / r_R)).astype(np.float32)
+    pos = rng.permutation(200)[:n_tok].astype(np.int32)
+    xt = torch.from_numpy(x).cuda().to(xdt)
+    Pt = torch.from_numpy(P).cuda().to(xdt)
+    xe = xt.float().cpu().numpy()
+    Pe = Pt.float().cpu().numpy()
+    bt = torch.arange(4, dtype=torch.int32, device="cuda").reshape(1, 4)
+    cache = ops.Cache.empty(4, r, dtype, bt)
+    ops.append_latent(xt, cache, torch.zeros(n_tok, dtype=torch.int32, device="cuda"),
+                      torch.from_numpy(pos).cuda(), P=Pt, rope_theta=torch.from_numpy(theta).cuda())
+    ref = O.project_latent(xe, Pe, theta, pos)              # float64, eqs. 1-2
+    data = cache.data.reshape(256, r)[pos.astype(np.int64)].cpu()
+    if dtype == "fp32":
+        got = data.numpy().astype(np.float64)
+        tol = 1e-5 * np.abs(ref).max()
+    elif dtype == "bf16":
+        got = data.float().numpy().astype(np.float64)
+        tol = np.abs(ref) * 2.0 ** -7 + 1e-6               # one bf16 rounding
+    else:
+        sc = cache.scale.reshape(256)[pos.astype(np.int64)].cpu().numpy()
+        got = O.dequantize_fp8(data.numpy(), sc)
+        tol = np.abs(ref) * 2.0 ** -3 + sc[:, None] * 2.0 ** -9 * 1.01
+    assert np.all(np.abs(got - ref) <= tol)
+    # the rotation preserves each pair's norm and leaves the N branch alone
+    if dtype == "fp32":
+        nr = np.hypot(got[:, 0:r_R:2], got[:, 1:r_R:2])
+        y = xe.astype(np.float64) @ Pe.astype(np.float64)
+        assert np.allclose(nr, np.hypot(y[:, 0:r_R:2], y[:, 1:r_R:2]), rtol=1e-5, atol=1e-5)
+
+
+# ------------------------------------------------------------------ absorb ---
+
+@pytest.mark.parametrize("per_head", [False, True])
+@pytest.mark.parametrize("qdt", [torch.float32, torch.bfloat16])
+def test_absorb_matches_oracle(per_head, qdt):
+    say(f"absorb per_head={per_head} q={qdt}")
+    rng = np.random.default_rng(9)
+    n_q, H, d_I, r, no = 3, 64, 128, 256, 64
+    q = rng.standard_normal((n_q, H, d_I)).astype(np.float32)
+    Dt = (rng.standard_normal((H, r, d_I) if per_head else (r, d_I)) / 16).astype(np.float32)
+    b = rng.standard_normal(d_I - no).astype(np.float32)
+    qt_dev = torch.from_numpy(q).cuda().to(qdt)
+    qe = qt_dev.float().cpu().numpy()
+    qt, beta = ops.absorb_queries(qt_dev, torch.from_numpy(Dt).cuda(), torch.from_numpy(b).cuda(),
+                                  no, per_head=per_head)
+    for s in range(n_q):
+        oq, ob = O.absorb(qe[s], Dt, b, no)
+        g = qt[s].cpu().numpy()
+        assert np.max(np.abs(g - oq)) <= 1e-5 * np.abs(oq).max()
+        assert np.max(np.abs(beta[s].cpu().numpy() - ob)) <= 1e-5 * (np.abs(ob).max() + 1)
+
+
+# ------------------------------------------------------------------- score ---
+
+def _scores_vs_oracle(wl, dw, rtol, layers=None, sample=None):
+    layers = range(wl.G) if layers is None else layers
+    for l in layers:
+        say(f"  score layer {l}")
+        dw.absorb(l)
+        dw.score(l)
+        torch.cuda.synchronize()
+        u = dw.scores.cpu().numpy()
+        for s in range(wl.n_q):
+            seq = int(wl.q_seq[s])
+            L = int(wl.q_len[s])
+            C = O.sequence_latent(wl, seq)[:L]
+            rows = np.arange(L) if sample is None else np.unique(
+                np.concatenate([sample(L), wl.planted[seq][wl.planted[seq] < L]]))
+            o = O.layer_scores(C[rows], wl.q[l, s], wl.Dt[l], wl.b[l], wl.nope_off, wl.w[l, s])
+            assert_scores_close(u[s, rows], o, rtol, f"layer {l} query {s}")
+
+
+def test_score_valu_tiny_config_fp32():
+    say("score VALU config 0 (tiny fp32)")
+    wl = W.config(0)
+    dw = DeviceWorkload(wl, hold_last=False)
+    _scores_vs_oracle(wl, dw, RTOL_FP32)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp8"])
+def test_score_small_ragged_with_bias(dtype):
+    say(f"score small ragged with bias dtype={dtype} (H=64, r=256)")
+    wl = W.small_decode(2, n_seq=3, lens=[1, 95, 700], H=64, r=256, d_I=128, G=2, k=16,
+                        cache_dtype=dtype, nope_off=64, bias=True, plant=3, factor=3.0)
+    dw = DeviceWorkload(wl, hold_last=False)
+    _scores_vs_oracle(wl, dw, {"fp32": RTOL_FP32, "bf16": RTOL_BF16, "fp8": RTOL_FP8}[dtype])
+
+
+def test_score_bf16_queries_single_pass():
+    """A stored bf16 q~ (prefill form) is scored exactly as given."""
+    say("score with bf16 q~ input (H=64, r=256)")
+    wl = W.small_decode(3, n_seq=2, lens=[300, 129], H=64, r=256, d_I=128, G=1, k=16,
+                        cache_dtype="bf16")
+    dw = DeviceWorkload(wl, hold_last=False)
+    rng = np.random.default_rng(1)
+    bits = (rng.standard_normal((2, 64, 256)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    qt = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    u = ops.score(qt, dw.w[0], None, dw.q_seq, dw.q_len, dw.max_len, dw.cache)
+    torch.cuda.synchronize()
+    qt64 = O.bf16_decode(bits)
+    for s in range(2):
+        C = O.sequence_latent(wl, s)
+        o = O.absorbed_scores(C, qt64[s], None, wl.w[0, s])
+        assert_scores_close(u[s, :len(o)].cpu().numpy(), o, 1e-5, f"bf16 q~ query {s}")
+
+
+def test_score_config1_32k_bf16():
+    say("score config 1 (32K, H=64, r=256, bf16): all 4 layers")
+    wl = W.config(1)
+    dw = DeviceWorkload(wl, hold_last=False)
+    _scores_vs_oracle(wl, dw, RTOL_BF16)
+
+
+# ------------------------------------------------------------------- top-k ---
+
+def _topk_gpu(u, lens, k):
+    ut = torch.from_numpy(np.ascontiguousarray(u, dtype=np.float32)).cuda()
+    vl = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    idx, val = ops.topk(ut, vl, u.shape[1], k, want_val=True)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), val.cpu().numpy()
+
+
+def _check_topk_exact(u, lens, k):
+    idx, val = _topk_gpu(u, lens, k)
+    for i in range(u.shape[0]):
+        n = int(lens[i])
+        ref = O.pad(O.topk(u[i, :n].astype(np.float64), k), k)
+        assert np.array_equal(idx[i], ref), f"row {i}: n={n} k={k}"
+        m = min(k, n)
+        assert np.array_equal(val[i, :m].view(np.uint32), u[i, ref[:m]].astype(np.float32).view(np.uint32))
+        assert np.all(np.isneginf(val[i, m:]))
+
+
+@pytest.mark.parametrize("k", [1, 7, 256, 2048, 8192])
+def test_topk_exact_random_rows(k):
+    say(f"topk exact random k={k}")
+    rng = np.random.default_rng(k)
+    lens = [0, 1, 5, 1000, 4096, 33333, 70000]
+    u = rng.standard_normal((len(lens), 70000)).astype(np.float32)
+    _check_topk_exact(u, lens, k)
+
+
+def test_topk_exact_ties_and_signed_zero():
+    say("topk exact with heavy ties, signed zeros, all-equal rows")
+    rng = np.random.default_rng(3)
+    n = 20000
+    rows = [np.round(rng.standard_normal(n), 1),
+            np.zeros(n),
+            np.where(rng.random(n) < 0.5, -0.0, 0.0),
+            np.full(n, 3.25),
+            np.concatenate([np.full(n // 2, 1.0), np.full(n - n // 2, 2.0)]),
+            rng.choice([-np.inf, 0.0, 1.0], n)]
+    u = np.stack(rows).astype(np.float32)
+    for k in [1, 100, 2048, 9999, 20000, 30000]:
+        _check_topk_exact(u, [n] * len(rows), k)
+
+
+def test_topk_bucket_overflow_path():
+    """More than the LDS candidate capacity share the threshold bucket."""
+    say("topk with a crowded threshold bucket")
+    rng = np.random.default_rng(4)
+    n = 100000
+    u = (1.0 + rng.random(n) * 1e-3).astype(np.float32)      # one 12-bit bucket
+    _check_topk_exact(u[None, :], [n], 2048)
+
+
+# --------------------------------------------------------------------- HS ---
+
+@pytest.mark.parametrize("dtype,H,r", [("bf16", 64, 256), ("fp32", 8, 32), ("fp8", 64, 256)])
+def test_hs_select_matches_oracle(dtype, H, r):
+    say(f"hs_select dtype={dtype} H={H} r={r}")
+    wl = W.small_decode(6, n_seq=3, lens=[50, 1500, 4000], H=H, r=r, d_I=128 if H == 64 else 16,
+                        G=4, k=64, B=512, cache_dtype=dtype, plant=20, factor=3.0)
+    dw = DeviceWorkload(wl, hold_last=False)
+    dw.hs_step(append=False, keep_scores=True)
+    torch.cuda.synchronize()
+    rtol = {"fp32": RTOL_FP32, "bf16": RTOL_BF16, "fp8": RTOL_FP8}[dtype]
+    cand = dw.cand.cpu().numpy()
+    dw.absorb(0)
+    u0 = dw.score(0).cpu().numpy()
+    for s in range(wl.n_q):
+        L = int(wl.q_len[s])
+        # anchor candidates: bit-exact on the dumped anchor scores
+        ref_c = O.pad(O.hs_candidates(u0[s, :L].astype(np.float64), wl.B), wl.B)
+        assert np.array_equal(cand[s], ref_c)
+        assert np.array_equal(dw.hs_sel[0, s].cpu().numpy(), O.pad(O.topk(u0[s, :L].astype(np.float64), wl.k), wl.k))
+        nc = min(wl.B, L)
+        C = O.sequence_latent(wl, s)
+        for l in range(1, wl.G):
+            cs = dw.cand_scores[l, s].cpu().numpy()
+            assert np.all(np.isneginf(cs[nc:]))
+            o = O.layer_scores(C[cand[s, :nc]], wl.q[l, s], wl.Dt[l], wl.b[l], wl.nope_off, wl.w[l, s])
+            assert_scores_close(cs[:nc], o, rtol, f"follower {l} query {s}")
+            sel = dw.hs_sel[l, s].cpu().numpy()
+            ref = O.pad(O.hs_follower(cand[s, :nc], cs[:nc].astype(np.float64), wl.k), wl.k)
+            assert np.array_equal(sel, ref)                      # bit-exact on dumped scores
+            assert set(sel[sel >= 0]) <= set(cand[s, :nc])        # follower picks inside C
+            full = O.layer_scores(C[:L], wl.q[l, s], wl.Dt[l], wl.b[l], wl.nope_off, wl.w[l, s])
+            if L <= wl.B:                                         # C = everything: HS = full
+                assert_selection_band(sel, full, wl.k, rtol, f"HS=full follower {l} q {s}")
+
+
+# ------------------------------------------------------------ metamorphic ---
+
+def test_determinism_permutation_and_homogeneity():
+    say("metamorphic: determinism, block permutation, x4 homogeneity (bf16, H=64)")
+    wl = W.small_decode(8, n_seq=1, lens=[2000], H=64, r=256, d_I=128, G=1, k=16,
+                        cache_dtype="bf16", permute=True)
+    dw = DeviceWorkload(wl, hold_last=False)
+    dw.absorb(0)
+    a = dw.score(0).clone()
+    b = dw.score(0).clone()
+    assert torch.equal(a, b)
+    wl2 = W.small_decode(8, n_seq=1, lens=[2000], H=64, r=256, d_I=128, G=1, k=16,
+                         cache_dtype="bf16", permute=False)
+    dw2 = DeviceWorkload(wl2, hold_last=False)
+    dw2.absorb(0)
+    c = dw2.score(0).clone()
+    assert torch.equal(a, c)                     # physical layout does not change results
+    # token 5 replaced by 4x token 3 (exact in bf16): its score is exactly 4x
+    lat = wl.latent(0)
+    x = torch.from_numpy(4.0 * lat[3:4]).cuda()
+    ops.append_latent(x, dw.cache, torch.zeros(1, dtype=torch.int32, device="cuda"),
+                      torch.full((1,), 5, dtype=torch.int32, device="cuda"))
+    d = dw.score(0)
+    torch.cuda.synchronize()
+    assert d[0, 5].item() == 4.0 * d[0, 3].item()
