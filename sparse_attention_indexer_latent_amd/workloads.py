@@ -188,6 +188,7 @@ def make_decode(name, cfg_id, seed, *, G, H, r, d_I, k, B, cache_dtype, lens,
     for s in range(n_seq):
         L = int(lens[s])
         n = n_plant if n_plant is not None else int(round(plant_frac * L))
+        n = min(n, L)
         planted.append(_planted_ids(seed, cfg_id, s, L, n, r))
     bt, nphys = _block_table(seed, cfg_id, lens, permute_blocks)
     Dt = _decoders(seed, cfg_id, G, r, d_I)
