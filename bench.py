@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the LatentIndex decode indexer on one MI355X.
+
+One step = one decode step of a 4-layer group under hierarchical selection
+(LatentIndex summary, "Methodology", Hierarchical Selection): append the new
+token's latent, absorb the anchor's queries, scan and score the whole shared
+cache, select the anchor's top-B candidates and top-k, then for each of the
+three followers absorb, rescore the candidates and select top-k.  Workload:
+batch 4, 128K context, H = 64, r = 256, bf16 latent, B = 8192, k = 2048
+(synthetic, seeded).
+
+Printed: one JSON line with the throughput in scored tokens per second
+(L + 3*min(B, L) positions per query per step), the group-step time, the
+dominant kernel's roofline fraction (the anchor's latent scan, timed with HIP
+events on its stream), the same workload's full-scan step for the HS speedup,
+and the CPU oracle timed on a bounded sample of the same step.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK = 8.0e12  # B/s, MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-extra", action="store_true", help="skip full-scan and cold-MALL legs")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="only run warmup + this many steps (for profilers); prints nothing else")
+    return ap.parse_args()
+
+
+def scored_positions(wl, hs: bool) -> int:
+    tot = 0
+    for s in range(wl.n_q):
+        L = int(wl.q_len[s])
+        tot += L + (wl.G - 1) * min(wl.B, L) if hs else wl.G * L
+    return tot
+
+
+def latent_bytes_per_token(wl) -> int:
+    return {"bf16": 2, "fp8": 1, "fp32": 4}[wl.cache_dtype] * wl.r + (4 if wl.cache_dtype == "fp8" else 0)
+
+
+def cpu_baseline(wl, seconds: float):
+    """The oracle's HS group step, query by query, until `seconds` elapse."""
+    from oracle import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    done_pos, n_steps = 0, 0
+    s = 0
+    lat = {}
+    el = 0.0
+    while True:
+        seq = int(wl.q_seq[s])
+        if seq not in lat:   # exact decode of the stored cache, outside the timing
+            lat[seq] = O.sequence_latent(wl, seq)
+        t_a = time.perf_counter()
+        O.decode_group(wl, s, C=lat[seq], layers=[0], hs=True)
+        el += time.perf_counter() - t_a
+        n_steps += 1
+        L = int(wl.q_len[s])
+        done_pos += L + (wl.G - 1) * min(wl.B, L)
+        if el >= seconds:
+            break
+        s = (s + 1) % wl.n_q
+    return {"value": done_pos / el, "unit": "scored tokens/s", "cores": min(cores, blas_threads),
+            "kind": "oracle",
+            "sample": f"{n_steps} single-query HS group steps of this workload (L={int(wl.q_len[0])}, "
+                      f"anchor full scan + top-B + 3 follower rescores, float64 key "
+                      f"reconstruction and stable sort), {el:.1f} s of oracle time (the exact "
+                      f"decode of the stored cache is done once, untimed); host affinity "
+                      f"{cores} cores, BLAS threads {blas_threads}"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU; every GPU box here has one, "
+                                   "so --gpus must be 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_indexer_latent_amd import ops
+    from sparse_attention_indexer_latent_amd import workloads as W
+    from sparse_attention_indexer_latent_amd.runtime import DeviceWorkload
+
+    torch.cuda.set_device(0)
+    if ops.lib().li_check_device() != ops.LI_OK:
+        raise SystemExit(ops.lib().li_last_error().decode())
+    wl = W.config(args.config)
+    hs = wl.B is not None
+    dw = DeviceWorkload(wl, hold_last=True)
+    step = dw.hs_step if hs else dw.full_step
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        return
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(events=evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    el = t1 - t0
+    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    pos = scored_positions(wl, hs)
+    bpt = latent_bytes_per_token(wl)
+    scan_tokens = int(wl.q_len.sum())
+    scan_bytes = scan_tokens * (bpt + 4)            # latent read + fp32 score write
+    step_bytes = scan_tokens * bpt + (sum(min(wl.B, int(L)) for L in wl.q_len) * (wl.G - 1) * bpt
+                                      if hs else scan_tokens * bpt * (wl.G - 1))
+    us_step = el / K * 1e6
+
+    out = {
+        "metric": "indexer scored tokens/s and us/decode step per 4-layer group at 128K; % HBM BW",
+        "value": pos * K / el,
+        "unit": "scored tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": el / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.cache_dtype == "bf16" else wl.cache_dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: HS decode step of a 4-layer group, batch {wl.n_q}, "
+                               f"L={wl.max_len}, H={wl.H}, r={wl.r}, {wl.cache_dtype} latent, "
+                               f"B={wl.B}, k={wl.k}, 64-token pages, random block table",
+                   "global_batch": wl.n_q, "seq_len": wl.max_len, "parallelism": "none (1 GPU)"},
+        "us_per_group_step": us_step,
+        "scored_positions_per_step": pos,
+        "hbm_frac_step": step_bytes / (el / K) / HBM_PEAK,
+        "roofline": {"bound": "hbm", "kernel": "score_mfma_kernel (anchor full scan)",
+                     "achieved": scan_bytes / (scan_ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": scan_bytes / (scan_ms * 1e-3) / HBM_PEAK,
+                     "traffic": None, "avg_kernel_us": scan_ms * 1e3,
+                     "bytes_per_launch": scan_bytes},
+    }
+
+    if not args.no_extra:
+        # Full scan of the same group (every layer scans everything).
+        Kf = max(5, K // 2)
+        for _ in range(2):
+            dw.full_step()
+        fevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(Kf)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(Kf):
+            dw.full_step(events=fevs[i])
+        torch.cuda.synchronize()
+        elf = time.perf_counter() - t0
+        fscan = float(np.mean([a.elapsed_time(b) for a, b in fevs]))
+        fpos = scored_positions(wl, False)
+        out["full_scan"] = {"us_per_group_step": elf / Kf * 1e6,
+                            "scored_tokens_per_s": fpos * Kf / elf,
+                            "hbm_frac_step": scan_tokens * bpt * wl.G / (elf / Kf) / HBM_PEAK,
+                            "scan_kernel_us": fscan * 1e3}
+        out["hs_speedup_vs_full_scan"] = (elf / Kf) / (el / K)
+        # Cold MALL: stream 1 GiB through the memory system before each step.
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        Kc = 10
+        cold = []
+        for i in range(Kc):
+            flush.fill_(float(i))
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            step()
+            b.record()
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        out["cold_mall_us_per_group_step"] = float(np.median(cold)) * 1e3
+        del flush
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        out["gpu_over_cpu"] = out["value"] / out["cpu_baseline"]["value"]
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

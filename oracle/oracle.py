@@ -301,8 +301,9 @@ def decode_group(wl, s: int, C: Optional[np.ndarray] = None, layers=None,
 
     Returns a dict with per-layer score rows 'u' (full scan, [L]) and
     selections 'sel' (ascending ids); with hs=True also 'cand', 'u_f'
-    (follower scores on the candidates) and 'hs_sel'.  rows restricts the
-    scored tokens to a sample (no selection then)."""
+    (follower scores on the candidates) and 'hs_sel'; with hs=True and
+    layers=[0] only the anchor scans the whole cache, as the HS step does.
+    rows restricts the scored tokens to a sample (no selection then)."""
     seq = int(wl.q_seq[s])
     L = int(wl.q_len[s])
     if C is None:

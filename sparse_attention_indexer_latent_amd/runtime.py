@@ -93,24 +93,34 @@ class DeviceWorkload:
         return ops.score(self.q_tilde, self.w[layer], self.beta, self.q_seq, self.q_len,
                          self.max_len, self.cache, scores=self.scores if scores is None else scores)
 
-    def full_step(self, append: bool = True) -> None:
-        """Full-scan decode step of the group: per layer absorb, score, top-k."""
+    def full_step(self, append: bool = True, events=None) -> None:
+        """Full-scan decode step of the group: per layer absorb, score, top-k.
+        events: optional (start, end) CUDA events recorded around layer 0's scan."""
         if append:
             self.append()
         for l in range(self.wl.G):
             self.absorb(l)
+            if events is not None and l == 0:
+                events[0].record()
             self.score(l)
+            if events is not None and l == 0:
+                events[1].record()
             ops.topk(self.scores, self.q_len, self.max_len, self.wl.k, out_idx=self.sel[l],
                      ws=self.topk_ws)
 
-    def hs_step(self, append: bool = True, keep_scores: bool = False) -> None:
+    def hs_step(self, append: bool = True, keep_scores: bool = False, events=None) -> None:
         """Hierarchical-selection decode step: the anchor scans and proposes
-        its top-B, followers rescore and refine within the candidates."""
+        its top-B, followers rescore and refine within the candidates.
+        events: optional (start, end) CUDA events recorded around the anchor scan."""
         wl = self.wl
         if append:
             self.append()
         self.absorb(0)
+        if events is not None:
+            events[0].record()
         self.score(0)
+        if events is not None:
+            events[1].record()
         ops.topk(self.scores, self.q_len, self.max_len, wl.B, out_idx=self.cand, ws=self.topk_ws)
         ops.topk(self.scores, self.q_len, self.max_len, wl.k, out_idx=self.hs_sel[0],
                  ws=self.topk_ws)
