@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip full-scan and cold-MALL legs")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run warmup + this many steps (for profilers); prints nothing else")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel from the host instead of replaying HIP graphs")
     return ap.parse_args()
 
 
@@ -110,7 +112,11 @@ def main():
     wl = W.config(args.config)
     hs = wl.B is not None
     dw = DeviceWorkload(wl, hold_last=True)
-    step = dw.hs_step if hs else dw.full_step
+    if args.eager:
+        step = dw.hs_step if hs else dw.full_step
+    else:
+        graphs = dw.capture(hs)
+        step = graphs.replay
 
     for _ in range(args.warmup):
         step()
@@ -157,7 +163,8 @@ def main():
         "config": {"workload": f"{wl.name}: HS decode step of a 4-layer group, batch {wl.n_q}, "
                                f"L={wl.max_len}, H={wl.H}, r={wl.r}, {wl.cache_dtype} latent, "
                                f"B={wl.B}, k={wl.k}, 64-token pages, random block table",
-                   "global_batch": wl.n_q, "seq_len": wl.max_len, "parallelism": "none (1 GPU)"},
+                   "global_batch": wl.n_q, "seq_len": wl.max_len, "parallelism": "none (1 GPU)",
+                   "launch": "eager" if args.eager else "hipGraph pre | direct anchor scan | hipGraph post"},
         "us_per_group_step": us_step,
         "scored_positions_per_step": pos,
         "hbm_frac_step": step_bytes / (el / K) / HBM_PEAK,
@@ -171,14 +178,15 @@ def main():
     if not args.no_extra:
         # Full scan of the same group (every layer scans everything).
         Kf = max(5, K // 2)
+        fstep = dw.full_step if args.eager else dw.capture(False).replay
         for _ in range(2):
-            dw.full_step()
+            fstep()
         fevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(Kf)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(Kf):
-            dw.full_step(events=fevs[i])
+            fstep(events=fevs[i])
         torch.cuda.synchronize()
         elf = time.perf_counter() - t0
         fscan = float(np.mean([a.elapsed_time(b) for a, b in fevs]))

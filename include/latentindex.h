@@ -124,7 +124,8 @@ li_status li_append_latent(const void *x, li_dtype x_dt, int32_t n_tok, int32_t 
  *            or NULL for b = 0.  0 <= nope_off <= d_I.
  *   q_tilde  device fp32 [n_q, H, r] (out).
  *   beta     device fp32 [n_q, H] (out); may be NULL.
- * Accumulates in fp32.  H <= 1024, d_I <= 1024, r <= 1024.
+ * Accumulates in fp32.  H <= 1024, d_I <= 1024, r <= 1024; d_I and
+ * Dt_head_stride multiples of 4, q and Dt 16-byte aligned.
  */
 li_status li_absorb_queries(const void *q, li_dtype q_dt, int32_t n_q, int32_t H, int32_t d_I,
                             const float *Dt, int64_t Dt_head_stride, const float *b,
@@ -175,6 +176,25 @@ size_t li_topk_workspace_bytes(int32_t n_rows, int32_t max_len, int32_t k);
 li_status li_topk(const float *scores, int64_t ld, int32_t n_rows, const int32_t *valid_len,
                   int32_t max_len, int32_t k, int32_t *out_idx, float *out_val, void *ws,
                   size_t ws_bytes, void *stream);
+
+/*
+ * li_hs_anchor_select -- the anchor layer's part of hierarchical selection
+ * ("Hierarchical Selection" paragraph): from the anchor's full score rows,
+ * the candidate set C = top-min(B, |V|) positions and the anchor's own
+ * selection S = top-min(k, |V|) (S is inside C because B >= k), both in one
+ * pass over the scores.
+ *   scores, ld, n_rows, valid_len, max_len: as for li_topk.
+ *   B, cand    1 <= B <= 65536; cand device int32 [n_rows, B] (out):
+ *              ascending token ids, -1 padded (the input of li_hs_select).
+ *   k, sel     1 <= k <= B; sel device int32 [n_rows, k] (out), ascending,
+ *              -1 padded.  sel may be NULL when only C is wanted.
+ *   ws         device workspace of li_hs_anchor_workspace_bytes() bytes.
+ * Results equal two li_topk calls with k = B and with k.
+ */
+size_t li_hs_anchor_workspace_bytes(int32_t n_rows, int32_t max_len);
+li_status li_hs_anchor_select(const float *scores, int64_t ld, int32_t n_rows,
+                              const int32_t *valid_len, int32_t max_len, int32_t B, int32_t *cand,
+                              int32_t k, int32_t *sel, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * li_hs_select -- a follower layer's hierarchical selection ("Hierarchical

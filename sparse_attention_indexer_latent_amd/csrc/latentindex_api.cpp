@@ -113,6 +113,7 @@ li_status li_absorb_queries(const void *q, li_dtype q_dt, int32_t n_q, int32_t H
     return fail(LI_ERR_INVALID, "H/d_I/r out of range (1..1024)");
   if (nope_off < 0 || nope_off > d_I) return fail(LI_ERR_INVALID, "nope_off out of [0, d_I]");
   if (Dt_head_stride < 0) return fail(LI_ERR_INVALID, "Dt_head_stride < 0");
+  if (d_I % 4 || Dt_head_stride % 4) return fail(LI_ERR_UNSUPPORTED, "d_I and Dt_head_stride must be multiples of 4");
   if (n_q == 0) return LI_OK;
   if (!q || !Dt || !q_tilde) return fail(LI_ERR_INVALID, "q/Dt/q_tilde is NULL");
   li_status s = check_device();
@@ -179,11 +180,37 @@ li_status li_topk(const float *scores, int64_t ld, int32_t n_rows, const int32_t
                     "li_topk launch");
 }
 
+size_t li_hs_anchor_workspace_bytes(int32_t n_rows, int32_t max_len) {
+  if (n_rows <= 0 || max_len <= 0) return 0;
+  return li::topk2_ws_bytes(n_rows, max_len);
+}
+
+li_status li_hs_anchor_select(const float *scores, int64_t ld, int32_t n_rows,
+                              const int32_t *valid_len, int32_t max_len, int32_t B, int32_t *cand,
+                              int32_t k, int32_t *sel, void *ws, size_t ws_bytes, void *stream) {
+  if (n_rows < 0) return fail(LI_ERR_INVALID, "n_rows < 0");
+  if (B <= 0 || B > 65536) return fail(LI_ERR_INVALID, "B = %d out of [1, 65536]", B);
+  if (k <= 0) return fail(LI_ERR_INVALID, "k = %d must be positive", k);
+  if (B < k) return fail(LI_ERR_INVALID, "B (%d) < k (%d): the candidate set must hold k", B, k);
+  if (max_len < 0 || (int64_t)max_len > ld) return fail(LI_ERR_INVALID, "need 0 <= max_len <= ld");
+  if (n_rows == 0) return LI_OK;
+  if (!scores || !valid_len || !cand) return fail(LI_ERR_INVALID, "scores/valid_len/cand is NULL");
+  size_t need = li_hs_anchor_workspace_bytes(n_rows, max_len > 0 ? max_len : 1);
+  if (!ws || ws_bytes < need) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
+  li_status s = check_device();
+  if (s != LI_OK) return s;
+  hipError_t e = sel ? li::launch_topk2(scores, ld, n_rows, valid_len, max_len > 0 ? max_len : 1, B,
+                                        cand, k, sel, ws, (hipStream_t)stream)
+                     : li::launch_topk2(scores, ld, n_rows, valid_len, max_len > 0 ? max_len : 1, B,
+                                        cand, B, cand, ws, (hipStream_t)stream);
+  return hip_status(e, "li_hs_anchor_select launch");
+}
+
 size_t li_hs_workspace_bytes(int32_t n_q, int32_t B, int32_t k) {
   if (n_q <= 0 || B <= 0 || k <= 0) return 0;
-  size_t scores = (size_t)n_q * B * sizeof(float);
-  size_t counts = ((size_t)n_q * sizeof(int32_t) + 255) & ~(size_t)255;
-  return ((scores + 255) & ~(size_t)255) + counts + li::topk_ws_bytes(n_q, B, k);
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return al((size_t)n_q * B * sizeof(float)) + al((size_t)n_q * sizeof(int32_t)) +
+         li::topk_ws_bytes(n_q, B, k);
 }
 
 li_status li_hs_select(const int32_t *cand, int32_t B, const void *q_tilde, li_dtype qt_dt,
@@ -200,26 +227,33 @@ li_status li_hs_select(const int32_t *cand, int32_t B, const void *q_tilde, li_d
   size_t need = li_hs_workspace_bytes(n_q, B, k);
   if (!ws || ws_bytes < need) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
   if ((s = check_device()) != LI_OK) return s;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   char *p = (char *)ws;
   float *sc = (float *)p;
-  p += ((size_t)n_q * B * sizeof(float) + 255) & ~(size_t)255;
-  int32_t *counts = (int32_t *)p;
-  p += ((size_t)n_q * sizeof(int32_t) + 255) & ~(size_t)255;
+  p += al((size_t)n_q * B * sizeof(float));
+  int32_t *lens = (int32_t *)p;
+  p += al((size_t)n_q * sizeof(int32_t));
   void *tws = p;
   float *dst = cand_scores ? cand_scores : sc;
   hipStream_t st = (hipStream_t)stream;
   li::CacheView cv = li::view_of(*cache);
-  hipError_t e = li::launch_count_valid(cand, n_q, B, counts, dst, st);
-  if (e == hipSuccess) {
-    if (li::score_mfma_supported(qt_dt, H, cv))
-      e = li::launch_score_mfma(q_tilde, qt_dt, w, beta, n_q, H, q_seq, counts, B, cv, cand, B, dst,
-                                B, st);
-    else
-      e = li::launch_score_valu(q_tilde, qt_dt, w, beta, n_q, H, q_seq, counts, B, cv, cand, B, dst,
-                                B, st);
+  // 1. the follower's scores of every candidate slot (-inf on padding);
+  // 2. its top-k over all B slots: padding ranks below every candidate and
+  //    maps to id -1, so the output is the top-min(k, |C|) then -1 padding.
+  hipError_t e;
+  if (li::score_mfma_supported(qt_dt, H, cv))
+    e = li::launch_score_mfma(q_tilde, qt_dt, w, beta, n_q, H, q_seq, nullptr, B, cv, cand, B, dst,
+                              B, st);
+  else
+    e = li::launch_score_valu(q_tilde, qt_dt, w, beta, n_q, H, q_seq, nullptr, B, cv, cand, B, dst,
+                              B, st);
+  const int32_t *vl = nullptr;
+  if (e == hipSuccess && B > 16384) {  // the longer-row paths need per-row lengths
+    e = li::launch_fill_i32(lens, n_q, B, st);
+    vl = lens;
   }
   if (e == hipSuccess)
-    e = li::launch_topk(dst, B, n_q, counts, cand, B, B, k, out_idx, nullptr, tws, st);
+    e = li::launch_topk(dst, B, n_q, vl, cand, B, B, k, out_idx, nullptr, tws, st);
   return hip_status(e, "li_hs_select launch");
 }
 

@@ -37,10 +37,11 @@ hipError_t launch_absorb(const void *q, int q_dt, int n_q, int H, int d_I, const
                          int64_t Dt_head_stride, const float *b, int nope_off, int r,
                          float *q_tilde, float *beta, hipStream_t st);
 
+// Scorers.  Page mode (cand == nullptr): token t < q_len[i] of sequence
+// q_seq[i] goes to out[i*ld + t].  Candidate mode: slot j < B of query i
+// scores token cand[i*B + j] (or writes -inf where it is -1) into
+// out[i*ld + j]; q_len is unused.
 // score_valu.hip: generic vector-ALU scorer, any supported dtype.
-// When `cand` is non-null the tokens of query i are cand[i*B + j] (j < B,
-// stopping at the first -1) and results go to out[i*ld + j]; otherwise
-// token t < q_len[i] goes to out[i*ld + t].
 hipError_t launch_score_valu(const void *q_tilde, int qt_dt, const float *w, const float *beta,
                              int n_q, int H, const int32_t *q_seq, const int32_t *q_len,
                              int max_len, const CacheView &cv, const int32_t *cand, int B,
@@ -55,14 +56,21 @@ hipError_t launch_score_mfma(const void *q_tilde, int qt_dt, const float *w, con
 
 // topk.hip.  `ids` (may be null) maps a row position j to the id reported
 // for it (row i uses ids + i*ids_ld); positions are ordered by id exactly as
-// by j (ids ascending), so ties break by position.
+// by j (ids ascending), so ties break by position.  valid_len may be null
+// when every row is valid on [0, max_len) and max_len <= 16384.
 size_t topk_ws_bytes(int n_rows, int max_len, int k);
 hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
                        const int32_t *ids, int64_t ids_ld, int max_len, int k, int32_t *out_idx,
                        float *out_val, void *ws, hipStream_t st);
 
-// hs.hip: count valid candidates per row (entries before the first -1).
-hipError_t launch_count_valid(const int32_t *cand, int n_q, int B, int32_t *counts,
-                              float *cand_scores, hipStream_t st);
+// Two nested selections (k_outer >= k_inner) in one pass; ws of
+// topk2_ws_bytes(n_rows, max_len) bytes.
+size_t topk2_ws_bytes(int n_rows, int max_len);
+hipError_t launch_topk2(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
+                        int max_len, int k_outer, int32_t *out_outer, int k_inner,
+                        int32_t *out_inner, void *ws, hipStream_t st);
+
+// Fill n int32 values with v (device).
+hipError_t launch_fill_i32(int32_t *dst, int n, int32_t v, hipStream_t st);
 
 }  // namespace li

@@ -6,7 +6,7 @@
 // absorbed queries, 2*64*256 = 32768 flop, i.e. 64 flop per byte read, three
 // times the fp32 vector ridge of MI355X (157 TFLOP/s / 8 TB/s).  The product
 // [64 heads x r] x [r x tokens] is a real dense contraction even for a single
-// decode query, so it runs on v_mfma_f32_32x32x16_bf16 and the kernel stays
+// decode query, so it runs on v_mfma_f32_16x16x32_bf16 and the kernel stays
 // bound by the HBM stream of the latent.
 //
 // Precision: an fp32 q~ is carried as bf16 hi + lo (hi = RNE(q~), lo =
@@ -14,23 +14,25 @@
 // MFMA accumulates in fp32, so the only rounding left is ~2^-16 relative in
 // q~ plus fp32 accumulation.  A bf16 q~ input takes a single pass.
 //
-// Structure (one workgroup = 4 wavefronts):
+// Structure (one workgroup = 8 wavefronts, two per SIMD, one per CU):
 //  * The flattened list of 64-token pages of all queries is split into
-//    contiguous ranges, one per workgroup (balances ragged batches).
+//    contiguous ranges, one per workgroup (balances ragged batches).  The
+//    plan and the block ids of the range cost two global round trips; the
+//    first pages' loads are issued before the query operands are fetched.
 //  * Pages stream HBM -> LDS with direct-to-LDS loads
 //    (global_load_lds_dwordx4), NSTAGE pages in flight, completion tracked
 //    with explicit vmcnt waits and a bare s_barrier.  A token row of 512 B
 //    sits in LDS with its 16-byte chunks XOR-swizzled by (row & 15), so the
 //    MFMA operand reads (16 rows x 16 B per pass) are bank-conflict free.
-//  * Wavefront (mb, nb) holds the A operand (heads 32mb..32mb+31, all of r,
-//    hi and lo) in registers for the whole range and computes the 32x32 tile
-//    of heads x tokens 32nb..32nb+31 of each page.
-//  * Epilogue per tile: + beta, ReLU, * w, sum over the lane's 16 heads, one
-//    cross-lane add (lanes l and l^32 hold the other 16 heads), then the two
-//    head halves meet through LDS one page later (no extra barrier).
+//  * Wavefront w holds the A operand of heads 16*(w%4) .. +15 (all of r, hi
+//    and lo: 64 VGPRs) for the whole range and computes heads x tokens
+//    32*(w/4) .. +31 of each page as two 16x16 tiles.
+//  * Epilogue per tile: + beta, ReLU, * w, sum over the lane's 4 heads, two
+//    cross-lane adds (the 16 heads of the group), then the four head groups
+//    meet through LDS one page later (no extra barrier).
 //  * Candidate mode (hierarchical selection): "pages" are 64 candidate slots
-//    whose rows are gathered through the block table; physical rows are
-//    resolved into LDS before streaming.
+//    whose physical rows were resolved beforehand; each query owns exactly
+//    ceil(B/64) such pages, so the range plan needs no loads.
 #include <algorithm>
 
 #include "li_device.h"
@@ -41,9 +43,12 @@ namespace {
 
 #define LDS3 __attribute__((address_space(3)))
 
-constexpr int kThreads = 256;
 constexpr int kMaxPagesPerWG = 512;   // page mode
 constexpr int kMaxPagesGather = 16;   // candidate mode
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding:
+// vmcnt[3:0] at bits 3:0, vmcnt[5:4] at bits 15:14, expcnt and lgkmcnt at max).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -58,45 +63,38 @@ union Frag {
   uint32_t u[4];
 };
 
-template <int R, int NSTAGE>
-struct MfmaShared {
-  static constexpr int kRowBytes = R * 2;
-  __align__(16) char stage[NSTAGE][kPage * kRowBytes];
-  float red[2][2][32];
-  int32_t pq[kMaxPagesPerWG];
-  int32_t ppg[kMaxPagesPerWG];
-  int32_t prow[kMaxPagesPerWG];  // page mode: physical block; candidate mode: see gather_rows
-  int32_t gather_rows[kMaxPagesGather * kPage];
-  int32_t np;
-};
-
 __device__ __forceinline__ int qpages(const int32_t *q_len, int i) { return (q_len[i] + 63) >> 6; }
 
-// Wave 0 works out this workgroup's page range and writes (query, page) per
-// local page into LDS.  Returns nothing; sh.np holds the page count.
+// Wave 0 works out this workgroup's contiguous range of the flattened
+// (query, page) list and writes (query, page, sequence) per local page into
+// LDS.  The lengths and sequence ids of the first 64 queries are loaded once
+// into registers, so the plan costs one global round trip; sh.np receives the
+// page count (clamped to cap, which the host sizing guarantees whenever every
+// q_len honours the bound it was given).
 template <typename SH>
-__device__ void plan_range(SH &sh, int n_q, const int32_t *q_len, int cap) {
+__device__ void plan_range(SH &sh, int n_q, const int32_t *q_len, const int32_t *q_seq, int cap) {
   const int lane = threadIdx.x % kWave;
   if (threadIdx.x >= kWave) return;
+  const int len0 = lane < n_q ? q_len[lane] : 0;
+  const int seq0 = lane < n_q ? q_seq[lane] : 0;
+  const int np0 = (len0 + 63) >> 6;
+  auto pages_of = [&](int q) { return q < kWave ? __shfl(np0, q, kWave) : qpages(q_len, q); };
+  auto seq_of = [&](int q) { return q < kWave ? __shfl(seq0, q, kWave) : q_seq[q]; };
   int64_t T = 0;
   for (int c = 0; c < n_q; c += kWave) {
-    const int i = c + lane;
-    int np = i < n_q ? qpages(q_len, i) : 0;
+    int np = c == 0 ? np0 : (c + lane < n_q ? qpages(q_len, c + lane) : 0);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) np += __shfl_xor(np, o, kWave);
     T += np;
   }
   const int64_t G = gridDim.x, g = blockIdx.x;
   const int64_t f0 = g * T / G, f1 = (g + 1) * T / G;
-  // The host sizes the grid so that cnt <= cap whenever every q_len honours
-  // the bound it was given; the clamp keeps a violating call memory-safe.
   const int cnt = (int)min<int64_t>(f1 - f0, cap);
   int q0 = 0, pg0 = 0;
   int64_t cum = 0;
   if (cnt > 0) {
     for (int c = 0; c < n_q; c += kWave) {
-      const int i = c + lane;
-      const int np = i < n_q ? qpages(q_len, i) : 0;
+      const int np = c == 0 ? np0 : (c + lane < n_q ? qpages(q_len, c + lane) : 0);
       int incl = np;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -115,93 +113,82 @@ __device__ void plan_range(SH &sh, int n_q, const int32_t *q_len, int cap) {
       cum += __shfl(incl, kWave - 1, kWave);
     }
   }
-  if (lane == 0) {
-    int q = q0, pg = pg0, qp = cnt > 0 ? qpages(q_len, q) : 0;
-    for (int p = 0; p < cnt; ++p) {
+  // uniform walk over the range (the whole wavefront executes it)
+  int q = q0, pg = pg0;
+  int qp = cnt > 0 ? pages_of(q) : 0, sq = cnt > 0 ? seq_of(q) : 0;
+  for (int p = 0; p < cnt; ++p) {
+    if (lane == 0) {
       sh.pq[p] = q;
       sh.ppg[p] = pg;
-      if (++pg == qp) {
-        pg = 0;
-        do {
-          ++q;
-        } while (q < n_q && (qp = qpages(q_len, q)) == 0);
-      }
+      sh.pseq[p] = sq;
     }
-    sh.np = cnt;
+    if (++pg == qp) {
+      pg = 0;
+      do {
+        ++q;
+      } while (q < n_q && (qp = pages_of(q)) == 0);
+      if (q < n_q) sq = seq_of(q);
+    }
   }
+  if (lane == 0) sh.np = cnt;
 }
 
-template <int R, int NSTAGE, bool HILO>
+// ---------------------------------------------------------------------------
+// Eight-wavefront variant on v_mfma_f32_16x16x32_bf16: wavefront w owns heads
+// 16*(w%4) .. +15 (its hi/lo operand is 64 VGPRs) and tokens 32*(w/4) .. +31
+// of every page (two 16-token tiles).  Two wavefronts per SIMD hide the LDS,
+// MFMA-result and barrier latencies that a single wavefront per SIMD exposes.
+// The four head groups meet through LDS one page later.
+// ---------------------------------------------------------------------------
+template <int R, int NSTAGE>
+struct MfmaShared {
+  static constexpr int kRowBytes = R * 2;
+  __align__(16) char stage[NSTAGE][kPage * kRowBytes];
+  float red[2][4][kPage];
+  int32_t pq[kMaxPagesPerWG];
+  int32_t ppg[kMaxPagesPerWG];
+  int32_t pseq[kMaxPagesPerWG];
+  int32_t prow[kMaxPagesPerWG];
+  int32_t gather_rows[kMaxPagesGather * kPage];
+  int32_t np;
+};
+
+constexpr int kThreads = 512;
+
+template <int R, int NSTAGE, bool HILO, bool GATHER>
 __global__ void __launch_bounds__(kThreads, 1)
 score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
-                  const float *__restrict__ beta, int n_q, const int32_t *__restrict__ q_seq,
-                  const int32_t *__restrict__ q_len, CacheView cv, const int32_t *__restrict__ cand,
-                  int B, float *__restrict__ out, int64_t ld) {
+                    const float *__restrict__ beta, int n_q, const int32_t *__restrict__ q_seq,
+                    const int32_t *__restrict__ q_len, CacheView cv,
+                    const int32_t *__restrict__ cand, int B, float *__restrict__ out, int64_t ld) {
   using SH = MfmaShared<R, NSTAGE>;
   constexpr int kRowBytes = SH::kRowBytes;
-  constexpr int kChunks = R / 8;                 // 16-byte chunks per token row
-  constexpr int kRowsPerInst = kWave / kChunks;  // token rows per wave-wide 1 KB load
+  constexpr int kChunks = R / 8;
+  constexpr int kRowsPerInst = kWave / kChunks;
   constexpr int kInstPerPage = kPage / kRowsPerInst;
-  constexpr int kInstPerWave = kInstPerPage / 4;
+  constexpr int kWaves = kThreads / kWave;
+  constexpr int kInstPerWave = kInstPerPage / kWaves;
   constexpr int kSwz = kChunks - 1 < 15 ? kChunks - 1 : 15;
-  constexpr int KB = R / 16;  // MFMA k-steps
-  static_assert(kInstPerWave * 4 == kInstPerPage, "page must split over 4 waves");
+  constexpr int KB = R / 32;  // MFMA k-steps of 32
+  static_assert(kInstPerWave * kWaves == kInstPerPage, "page must split over the waves");
 
   __shared__ SH sh;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int mb = wave & 1, nb = wave >> 1;
-  const bool gather = cand != nullptr;
+  const int hg = wave & 3, nh = wave >> 2;
+  constexpr bool gather = GATHER;
 
-  plan_range(sh, n_q, q_len, gather ? kMaxPagesGather : kMaxPagesPerWG);
-  __syncthreads();
-  const int np = sh.np;
-  if (np == 0) return;
-  if (!gather) {
-    for (int p = tid; p < np; p += kThreads)
-      sh.prow[p] = cv.block_table[(int64_t)q_seq[sh.pq[p]] * cv.max_blocks + sh.ppg[p]];
-  } else {
-    for (int e = tid; e < np * kPage; e += kThreads) {
-      const int p = e >> 6, row = e & 63;
-      const int q = sh.pq[p];
-      const int n = q_len[q];
-      const int slot = min(sh.ppg[p] * kPage + row, n - 1);
-      const int t = cand[(int64_t)q * B + slot];
-      sh.gather_rows[e] =
-          cv.block_table[(int64_t)q_seq[q] * cv.max_blocks + (t >> 6)] * kPage + (t & 63);
-    }
-  }
-  __syncthreads();
-
-  const char *gdata = (const char *)cv.data;
-  auto issue_page = [&](int p, int s) {
-    LDS3 char *dst = (LDS3 char *)sh.stage[s];
-#pragma unroll
-    for (int m = 0; m < kInstPerWave; ++m) {
-      const int gi = wave * kInstPerWave + m;
-      const int row = gi * kRowsPerInst + lane / kChunks;
-      const int chunk = (lane % kChunks) ^ (row & kSwz);
-      int64_t grow;
-      if (!gather)
-        grow = (int64_t)sh.prow[p] * kPage + row;
-      else
-        grow = sh.gather_rows[p * kPage + row];
-      const char *src = gdata + grow * kRowBytes + chunk * 16;
-      __builtin_amdgcn_global_load_lds((const void *)src, (LDS3 void *)(dst + gi * 1024), 16, 0, 0);
-    }
-  };
-
-  // A operand of this wavefront: heads 32*mb + (lane % 32), k = kb*16 + (lane/32)*8 + [0, 8)
+  // A operand: head 16*hg + (lane % 16), k = kb*32 + (lane/16)*8 + [0, 8)
   Frag ahi[KB], alo[HILO ? KB : 1];
-  float wv[16], bv[16];
+  float wv[4], bv[4];
   int cur_q = -1;
-  auto load_query = [&](int q) {
-    const int head = 32 * mb + (lane & 31);
+  auto load_query = [&](int q, bool drain) {
+    const int head = 16 * hg + (lane & 15);
     if constexpr (HILO) {
-      const float *src = (const float *)q_tilde + ((int64_t)q * 64 + head) * R + (lane >> 5) * 8;
+      const float *src = (const float *)q_tilde + ((int64_t)q * 64 + head) * R + (lane >> 4) * 8;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const float4 x0 = *(const float4 *)(src + kb * 16);
-        const float4 x1 = *(const float4 *)(src + kb * 16 + 4);
+        const float4 x0 = *(const float4 *)(src + kb * 32);
+        const float4 x1 = *(const float4 *)(src + kb * 32 + 4);
         const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -213,10 +200,10 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
         }
       }
     } else {
-      const uint16_t *src = (const uint16_t *)q_tilde + ((int64_t)q * 64 + head) * R + (lane >> 5) * 8;
+      const uint16_t *src = (const uint16_t *)q_tilde + ((int64_t)q * 64 + head) * R + (lane >> 4) * 8;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const uint4 x = *(const uint4 *)(src + kb * 16);
+        const uint4 x = *(const uint4 *)(src + kb * 32);
         ahi[kb].u[0] = x.x;
         ahi[kb].u[1] = x.y;
         ahi[kb].u[2] = x.z;
@@ -224,84 +211,173 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
       }
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int h = 32 * mb + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-      wv[j] = w[(int64_t)q * 64 + h];
-      bv[j] = beta ? beta[(int64_t)q * 64 + h] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int h = 16 * hg + 4 * (lane >> 4) + i;
+      wv[i] = w[(int64_t)q * 64 + h];
+      bv[i] = beta ? beta[(int64_t)q * 64 + h] : 0.f;
     }
     cur_q = q;
+    // Complete these loads here, with a wait the compiler sees: otherwise its
+    // merged view of the page loop makes every later use of them wait for all
+    // outstanding loads, in-flight latent pages included.
+    if (drain) __builtin_amdgcn_s_waitcnt(0);
   };
 
-  load_query(sh.pq[0]);
-#pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < np) issue_page(s, s);
+  if constexpr (!gather) {
+    plan_range(sh, n_q, q_len, q_seq, kMaxPagesPerWG);
+    __syncthreads();
+  } else {
+    // Every query owns exactly ceil(B / 64) candidate slots pages: the range
+    // needs no loads.  Padding slots (cand == -1) read pool row 0 and store
+    // -inf.
+    const int PB = (B + kPage - 1) / kPage;
+    const int64_t T = (int64_t)n_q * PB, G = gridDim.x, g = blockIdx.x;
+    const int64_t f0 = g * T / G;
+    const int cnt = (int)min<int64_t>((g + 1) * T / G - f0, kMaxPagesGather);
+    for (int p = tid; p < cnt; p += kThreads) {
+      sh.pq[p] = (int)((f0 + p) / PB);
+      sh.ppg[p] = (int)((f0 + p) % PB);
+    }
+    if (tid == 0) sh.np = cnt;
+    __syncthreads();
+  }
+  const int np = sh.np;
+  if (np == 0) return;
+  // candidate mode knows its first query without loads: fetch its operands
+  // now, in parallel with the candidate -> row lookups below
+  if constexpr (gather) load_query(sh.pq[0], false);
+  if constexpr (!gather) {
+    for (int p = tid; p < np; p += kThreads)
+      sh.prow[p] = cv.block_table[(int64_t)sh.pseq[p] * cv.max_blocks + sh.ppg[p]];
+  } else {
+    for (int e = tid; e < np * kPage; e += kThreads) {
+      const int p = e >> 6, row = e & 63;
+      const int q = sh.pq[p];
+      const int slot = min(sh.ppg[p] * kPage + row, B - 1);
+      const int t = cand[(int64_t)q * B + slot];
+      sh.gather_rows[e] =
+          t >= 0 ? cv.block_table[(int64_t)q_seq[q] * cv.max_blocks + (t >> 6)] * kPage + (t & 63)
+                 : -1;
+    }
+  }
+  __syncthreads();
 
-  float carry = 0.f;  // mb == 0: this wave's half of the previous page's scores
+  const char *gdata = (const char *)cv.data;
+  auto issue_page = [&](int p, int s) {
+    LDS3 char *dst = (LDS3 char *)sh.stage[s];
+    const char *page_base = gdata;
+    if constexpr (!gather) page_base += (int64_t)sh.prow[p] * kPage * kRowBytes;
+#pragma unroll
+    for (int m = 0; m < kInstPerWave; ++m) {
+      const int gi = wave * kInstPerWave + m;
+      const int row = gi * kRowsPerInst + lane / kChunks;
+      const int chunk = (lane % kChunks) ^ (row & kSwz);
+      const char *src;
+      if constexpr (!gather)
+        src = page_base + row * kRowBytes + chunk * 16;
+      else
+        src = gdata + (int64_t)max(sh.gather_rows[p * kPage + row], 0) * kRowBytes + chunk * 16;
+      __builtin_amdgcn_global_load_lds((const void *)src, (LDS3 void *)(dst + gi * 1024), 16, 0, 0);
+    }
+  };
+
+  // Prologue: page 0's loads, then this query's operands, then the next
+  // pages; waiting until at most the last pages' loads remain outstanding
+  // completes page 0 and the operands (loads return in order).
+  issue_page(0, 0);
+  if constexpr (!gather) load_query(sh.pq[0], false);
+#pragma unroll
+  for (int s = 1; s < NSTAGE - 1; ++s)
+    if (s < np) issue_page(s, s);
+  {
+    const int later = min(NSTAGE - 2, np - 1);
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kInstPerWave));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kInstPerWave));
+    else __builtin_amdgcn_s_waitcnt(0);
+  }
+
+  // Final score of token (or slot) nh*32 + lane of local page pp: this
+  // wave's head-group share plus the other three groups' shares from LDS.
+  auto store_score = [&](int pp, float own) {
+    const int q = sh.pq[pp];
+    const int tk = nh * 32 + lane;
+    const int t = sh.ppg[pp] * kPage + tk;
+    const float *rd = &sh.red[pp & 1][0][0];
+    const float v = ((own + rd[kPage + tk]) + rd[2 * kPage + tk]) + rd[3 * kPage + tk];
+    if constexpr (!gather) {
+      if (t < q_len[q]) out[(int64_t)q * ld + t] = v;
+    } else {
+      if (t < B) out[(int64_t)q * ld + t] = sh.gather_rows[pp * kPage + tk] >= 0 ? v : -INFINITY;
+    }
+  };
+  float carry = 0.f;  // hg == 0: this wave's head group share of the previous page
   for (int p = 0; p < np; ++p) {
-    // pages issued after p and still possibly in flight: p+1 .. min(p+NSTAGE-2, np-1)
     const int after = min(NSTAGE - 2, np - 1 - p);
     if (after >= 2) wait_vmcnt<2 * kInstPerWave>();
     else if (after == 1) wait_vmcnt<kInstPerWave>();
     else wait_vmcnt<0>();
     lds_barrier();
 
-    if (mb == 0 && p > 0 && lane < 32) {
-      const int pp = p - 1, q = sh.pq[pp];
-      const int t = sh.ppg[pp] * kPage + nb * 32 + lane;
-      if (t < q_len[q]) out[(int64_t)q * ld + t] = carry + sh.red[pp & 1][nb][lane];
-    }
-    if (sh.pq[p] != cur_q) load_query(sh.pq[p]);
+    if (hg == 0 && p > 0 && lane < 32) store_score(p - 1, carry);
+    if (sh.pq[p] != cur_q) load_query(sh.pq[p], true);
     if (p + NSTAGE - 1 < np) issue_page(p + NSTAGE - 1, (p + NSTAGE - 1) % NSTAGE);
 
     const char *sp = sh.stage[p % NSTAGE];
-    const int row = nb * 32 + (lane & 31);
-    const char *rp = sp + row * kRowBytes;
-    f32x16 acc = {};
+    const int row0 = nh * 32 + (lane & 15), row1 = row0 + 16;
+    const char *rp0 = sp + row0 * kRowBytes, *rp1 = sp + row1 * kRowBytes;
+    f32x4 acc0 = {}, acc1 = {};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const int chunk = (kb * 2 + (lane >> 5)) ^ (row & kSwz);
-      const bf16x8 b = *(const bf16x8 *)(rp + chunk * 16);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[kb].v, b, acc, 0, 0, 0);
-      if constexpr (HILO) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[kb].v, b, acc, 0, 0, 0);
+      const int chunk = kb * 4 + (lane >> 4);
+      const bf16x8 b0 = *(const bf16x8 *)(rp0 + ((chunk ^ (row0 & kSwz)) * 16));
+      const bf16x8 b1 = *(const bf16x8 *)(rp1 + ((chunk ^ (row1 & kSwz)) * 16));
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[kb].v, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[kb].v, b1, acc1, 0, 0, 0);
+      if constexpr (HILO) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[kb].v, b0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[kb].v, b1, acc1, 0, 0, 0);
+      }
     }
-    float part = 0.f;
+    float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) part = fmaf(wv[j], fmaxf(acc[j] + bv[j], 0.f), part);
-    part += __shfl_xor(part, 32, kWave);
-    if (mb == 1) {
-      if (lane < 32) sh.red[p & 1][nb][lane] = part;
+    for (int i = 0; i < 4; ++i) {
+      p0 = fmaf(wv[i], fmaxf(acc0[i] + bv[i], 0.f), p0);
+      p1 = fmaf(wv[i], fmaxf(acc1[i] + bv[i], 0.f), p1);
+    }
+    p0 += __shfl_xor(p0, 16, kWave);
+    p1 += __shfl_xor(p1, 16, kWave);
+    p0 += __shfl_xor(p0, 32, kWave);
+    p1 += __shfl_xor(p1, 32, kWave);
+    const float mine = lane < 16 ? p0 : p1;  // lanes 0..31: token nh*32 + lane
+    if (hg != 0) {
+      if (lane < 32) sh.red[p & 1][hg][nh * 32 + lane] = mine;
     } else {
-      carry = part;
+      carry = mine;
     }
   }
   lds_barrier();
-  if (mb == 0 && lane < 32) {
-    const int pp = np - 1, q = sh.pq[pp];
-    const int t = sh.ppg[pp] * kPage + nb * 32 + lane;
-    if (t < q_len[q]) out[(int64_t)q * ld + t] = carry + sh.red[pp & 1][nb][lane];
-  }
+  if (hg == 0 && lane < 32) store_score(np - 1, carry);
 }
 
 int g_num_cu = 0;
 
-template <int R, int NSTAGE, bool HILO>
+template <int R, int NSTAGE, bool HILO, bool GATHER>
 hipError_t launch_t(const void *q_tilde, const float *w, const float *beta, int n_q,
-                    const int32_t *q_seq, const int32_t *q_len, int max_len, const CacheView &cv,
-                    const int32_t *cand, int B, float *out, int64_t ld, hipStream_t st) {
+                      const int32_t *q_seq, const int32_t *q_len, int max_len, const CacheView &cv,
+                      const int32_t *cand, int B, float *out, int64_t ld, hipStream_t st) {
   if (g_num_cu == 0) {
     int dev = 0;
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&g_num_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (g_num_cu <= 0) g_num_cu = 256;
   }
-  const int64_t per_q = cand ? (B + 63) / 64 : (max_len + 63) / 64;
+  const int64_t per_q = GATHER ? (B + 63) / 64 : (max_len + 63) / 64;
   const int64_t T_ub = (int64_t)n_q * per_q;
-  const int cap = cand ? kMaxPagesGather : kMaxPagesPerWG;
+  const int cap = GATHER ? kMaxPagesGather : kMaxPagesPerWG;
   int64_t G = std::min<int64_t>(T_ub, g_num_cu);
   G = std::max<int64_t>(G, (T_ub + cap - 1) / cap);
   if (G <= 0) return hipSuccess;
-  score_mfma_kernel<R, NSTAGE, HILO><<<(unsigned)G, kThreads, 0, st>>>(
+  score_mfma_kernel<R, NSTAGE, HILO, GATHER><<<(unsigned)G, kThreads, 0, st>>>(
       q_tilde, w, beta, n_q, q_seq, q_len, cv, cand, B, out, ld);
   return hipGetLastError();
 }
@@ -317,11 +393,18 @@ hipError_t launch_score_mfma(const void *q_tilde, int qt_dt, const float *w, con
                              int max_len, const CacheView &cv, const int32_t *cand, int B,
                              float *out, int64_t ld, hipStream_t st) {
   (void)H;
-  if (qt_dt == LI_FP32)
-    return launch_t<256, 4, true>(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, cand, B, out,
-                                  ld, st);
-  return launch_t<256, 4, false>(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, cand, B, out,
-                                 ld, st);
+  if (qt_dt == LI_FP32) {
+    if (cand)
+      return launch_t<256, 4, true, true>(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, cand,
+                                            B, out, ld, st);
+    return launch_t<256, 4, true, false>(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, cand,
+                                           B, out, ld, st);
+  }
+  if (cand)
+    return launch_t<256, 4, false, true>(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, cand,
+                                           B, out, ld, st);
+  return launch_t<256, 4, false, false>(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, cand,
+                                          B, out, ld, st);
 }
 
 }  // namespace li

@@ -24,7 +24,7 @@ score_valu_kernel(const void *__restrict__ q_tilde, int qt_dt, const float *__re
   const int r = cv.r;
   const int i = blockIdx.y;
   const int t0 = blockIdx.x * TT;
-  const int n = q_len[i];
+  const int n = cand ? B : q_len[i];
   if (t0 >= n) return;  // uniform across the workgroup, before any barrier
   const int nt = min(TT, n - t0);
   float *qs = lds;                      // [H][r]
@@ -44,22 +44,22 @@ score_valu_kernel(const void *__restrict__ q_tilde, int qt_dt, const float *__re
   }
   const int seq = q_seq[i];
   const int32_t *bt = cv.block_table + (int64_t)seq * cv.max_blocks;
+  // token of a slot: the position itself, or the candidate (-1: padding,
+  // which reads pool row 0 and stores -inf)
+  auto token_of = [&](int slot) -> int { return cand ? cand[(int64_t)i * B + slot] : slot; };
+  auto phys_row = [&](int slot) -> int64_t {
+    const int t = token_of(slot);
+    return t >= 0 ? (int64_t)bt[t / kPage] * kPage + t % kPage : 0;
+  };
   for (int tok = tid; tok < TT; tok += 256) {
     float sc = 1.f;
-    if (tok < nt && cv.dtype == LI_FP8_E4M3) {
-      const int t = cand ? cand[(int64_t)i * B + t0 + tok] : t0 + tok;
-      sc = cv.scale[(int64_t)bt[t / kPage] * kPage + t % kPage];
-    }
+    if (tok < nt && cv.dtype == LI_FP8_E4M3) sc = cv.scale[phys_row(t0 + tok)];
     ssm[tok] = sc;
   }
   for (int e = tid; e < TT * r; e += 256) {
     const int tok = e / r, j = e % r;
     float v = 0.f;
-    if (tok < nt) {
-      const int t = cand ? cand[(int64_t)i * B + t0 + tok] : t0 + tok;
-      const int64_t row = (int64_t)bt[t / kPage] * kPage + t % kPage;
-      v = load_latent(cv.data, cv.dtype, row * r + j);
-    }
+    if (tok < nt) v = load_latent(cv.data, cv.dtype, phys_row(t0 + tok) * r + j);
     cs[tok * (r + 1) + j] = v;
   }
   __syncthreads();
@@ -80,7 +80,7 @@ score_valu_kernel(const void *__restrict__ q_tilde, int qt_dt, const float *__re
   if (tid < nt) {
     float s = 0.f;
     for (int g = 0; g < n_groups; ++g) s += red[g * TT + tid];
-    out[(int64_t)i * ld + t0 + tid] = s;
+    out[(int64_t)i * ld + t0 + tid] = (cand && token_of(t0 + tid) < 0) ? -INFINITY : s;
   }
 }
 

@@ -59,6 +59,8 @@ _SIGS = {
                         ctypes.POINTER(LiCacheStruct), _P, _I64, _P]),
     "li_topk_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "li_topk": (_I32, [_P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "li_hs_anchor_workspace_bytes": (_SZ, [_I32, _I32]),
+    "li_hs_anchor_select": (_I32, [_P, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _SZ, _P]),
     "li_hs_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "li_hs_select": (_I32, [_P, _I32, _P, _I32, _P, _P, _I32, _I32, _P,
                             ctypes.POINTER(LiCacheStruct), _I32, _P, _P, _P, _SZ, _P]),
@@ -219,6 +221,24 @@ def score(q_tilde: torch.Tensor, w: torch.Tensor, beta: Optional[torch.Tensor],
     return scores
 
 
+def prepared_score(q_tilde: torch.Tensor, w: torch.Tensor, beta: Optional[torch.Tensor],
+                   q_seq: torch.Tensor, q_len: torch.Tensor, max_len: int, cache: Cache,
+                   scores: torch.Tensor):
+    """A zero-argument callable that enqueues li_score on the current stream
+    with every argument marshalled once (for tight decode loops)."""
+    _need(q_tilde, "q_tilde", (torch.float32, torch.bfloat16))
+    _need(scores, "scores", torch.float32)
+    n_q, H, _ = q_tilde.shape
+    fn = lib().li_score
+    args = (q_tilde.data_ptr(), _dtype_code(q_tilde), w.data_ptr(), _ptr(beta), n_q, H,
+            q_seq.data_ptr(), q_len.data_ptr(), max_len, cache.struct(), scores.data_ptr(),
+            scores.shape[1])
+
+    def call():
+        _check(fn(*args, _stream()))
+    return call
+
+
 def topk(scores: torch.Tensor, valid_len: torch.Tensor, max_len: int, k: int,
          out_idx: Optional[torch.Tensor] = None, out_val: Optional[torch.Tensor] = None,
          ws: Optional[torch.Tensor] = None, want_val: bool = False):
@@ -236,6 +256,30 @@ def topk(scores: torch.Tensor, valid_len: torch.Tensor, max_len: int, k: int,
                          k, out_idx.data_ptr(), _ptr(out_val), _ptr(ws),
                          0 if ws is None else ws.numel(), _stream()))
     return (out_idx, out_val) if want_val else out_idx
+
+
+def hs_anchor_workspace(n_rows: int, max_len: int, device="cuda") -> torch.Tensor:
+    return torch.empty(lib().li_hs_anchor_workspace_bytes(n_rows, max_len), dtype=torch.uint8,
+                       device=device)
+
+
+def hs_anchor_select(scores: torch.Tensor, valid_len: torch.Tensor, max_len: int, B: int, k: int,
+                     cand: Optional[torch.Tensor] = None, sel: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None, want_sel: bool = True):
+    """The anchor's candidate set (top-B) and own selection (top-k) in one pass."""
+    _need(scores, "scores", torch.float32)
+    _need(valid_len, "valid_len", torch.int32)
+    n_rows = scores.shape[0]
+    if cand is None:
+        cand = torch.empty((n_rows, B), dtype=torch.int32, device=scores.device)
+    if sel is None and want_sel:
+        sel = torch.empty((n_rows, k), dtype=torch.int32, device=scores.device)
+    if ws is None:
+        ws = hs_anchor_workspace(n_rows, max_len, scores.device)
+    _check(lib().li_hs_anchor_select(scores.data_ptr(), scores.shape[1], n_rows,
+                                     valid_len.data_ptr(), max_len, B, cand.data_ptr(), k,
+                                     _ptr(sel), ws.data_ptr(), ws.numel(), _stream()))
+    return cand, sel
 
 
 def hs_workspace(n_q: int, B: int, k: int, device="cuda") -> torch.Tensor:

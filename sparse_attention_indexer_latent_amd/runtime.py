@@ -64,6 +64,7 @@ class DeviceWorkload:
             self.hs_sel = torch.empty((G, n_q, wl.k), dtype=torch.int32, device=device)
             self.cand_scores = torch.empty((G, n_q, wl.B), dtype=torch.float32, device=device)
             self.hs_ws = ops.hs_workspace(n_q, wl.B, wl.k, device)
+            self.anchor_ws = ops.hs_anchor_workspace(n_q, self.max_len, device)
 
     def _ws(self, n):
         return torch.empty(n, dtype=torch.uint8, device=self.device) if n else None
@@ -93,43 +94,101 @@ class DeviceWorkload:
         return ops.score(self.q_tilde, self.w[layer], self.beta, self.q_seq, self.q_len,
                          self.max_len, self.cache, scores=self.scores if scores is None else scores)
 
-    def full_step(self, append: bool = True, events=None) -> None:
-        """Full-scan decode step of the group: per layer absorb, score, top-k.
-        events: optional (start, end) CUDA events recorded around layer 0's scan."""
-        if append:
-            self.append()
-        for l in range(self.wl.G):
-            self.absorb(l)
-            if events is not None and l == 0:
-                events[0].record()
-            self.score(l)
-            if events is not None and l == 0:
-                events[1].record()
-            ops.topk(self.scores, self.q_len, self.max_len, self.wl.k, out_idx=self.sel[l],
-                     ws=self.topk_ws)
-
-    def hs_step(self, append: bool = True, keep_scores: bool = False, events=None) -> None:
-        """Hierarchical-selection decode step: the anchor scans and proposes
-        its top-B, followers rescore and refine within the candidates.
-        events: optional (start, end) CUDA events recorded around the anchor scan."""
-        wl = self.wl
+    # A decode step is split into three parts so that a scan of the whole
+    # cache (the dominant kernel) can be timed with events on its stream:
+    # pre (append + layer-0 absorb), scan (layer-0 score), post (the rest).
+    def _pre(self, append: bool) -> None:
         if append:
             self.append()
         self.absorb(0)
-        if events is not None:
-            events[0].record()
-        self.score(0)
-        if events is not None:
-            events[1].record()
-        ops.topk(self.scores, self.q_len, self.max_len, wl.B, out_idx=self.cand, ws=self.topk_ws)
-        ops.topk(self.scores, self.q_len, self.max_len, wl.k, out_idx=self.hs_sel[0],
-                 ws=self.topk_ws)
+
+    def _full_post(self) -> None:
+        wl = self.wl
+        ops.topk(self.scores, self.q_len, self.max_len, wl.k, out_idx=self.sel[0], ws=self.topk_ws)
+        for l in range(1, wl.G):
+            self.absorb(l)
+            self.score(l)
+            ops.topk(self.scores, self.q_len, self.max_len, wl.k, out_idx=self.sel[l],
+                     ws=self.topk_ws)
+
+    def _hs_post(self, keep_scores: bool = False) -> None:
+        wl = self.wl
+        ops.hs_anchor_select(self.scores, self.q_len, self.max_len, wl.B, wl.k, cand=self.cand,
+                             sel=self.hs_sel[0], ws=self.anchor_ws)
         for l in range(1, wl.G):
             self.absorb(l)
             ops.hs_select(self.cand, self.q_tilde, self.w[l], self.beta, self.q_seq, self.cache,
                           wl.k, out_idx=self.hs_sel[l],
                           cand_scores=self.cand_scores[l] if keep_scores else None,
                           ws=self.hs_ws)
+
+    def full_step(self, append: bool = True, events=None) -> None:
+        """Full-scan decode step of the group: per layer absorb, score, top-k.
+        events: optional (start, end) CUDA events recorded around layer 0's scan."""
+        self._pre(append)
+        if events is not None:
+            events[0].record()
+        self.score(0)
+        if events is not None:
+            events[1].record()
+        self._full_post()
+
+    def hs_step(self, append: bool = True, keep_scores: bool = False, events=None) -> None:
+        """Hierarchical-selection decode step: the anchor scans and proposes
+        its top-B, followers rescore and refine within the candidates.
+        events: optional (start, end) CUDA events recorded around the anchor scan."""
+        self._pre(append)
+        if events is not None:
+            events[0].record()
+        self.score(0)
+        if events is not None:
+            events[1].record()
+        self._hs_post(keep_scores)
+
+    def capture(self, hs: bool, append: bool = True, keep_scores: bool = False) -> "StepGraphs":
+        """Capture one decode step as graphs around the scan (see StepGraphs)."""
+        return StepGraphs(self, hs, append, keep_scores)
+
+
+class StepGraphs:
+    """A decode step as two HIP graphs around one direct launch of the scan.
+
+    pre (append + layer-0 absorb) and post (selections and the other layers)
+    are captured graphs; the layer-0 scan between them is launched directly
+    through a pre-marshalled call, so events recorded around it time exactly
+    that kernel on its stream.  The library allocates nothing, so every replay
+    reuses the same buffers and reproduces an eager step."""
+
+    def __init__(self, dw: DeviceWorkload, hs: bool, append: bool = True,
+                 keep_scores: bool = False):
+        post = (lambda: dw._hs_post(keep_scores)) if hs else dw._full_post
+        self.scan = ops.prepared_score(dw.q_tilde, dw.w[0], dw.beta, dw.q_seq, dw.q_len,
+                                       dw.max_len, dw.cache, dw.scores)
+        parts = [lambda: dw._pre(append), post]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm-up outside capture (one-time attributes)
+            for f in parts:
+                f()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graphs = []
+        for f in parts:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                f()
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def replay(self, events=None) -> None:
+        pre, post = self.graphs
+        pre.replay()
+        if events is not None:
+            events[0].record()
+        self.scan()
+        if events is not None:
+            events[1].record()
+        post.replay()
 
 
 def read_cache_rows(cache: ops.Cache, block_table: np.ndarray, s: int, L: int):

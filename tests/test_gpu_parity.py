@@ -220,6 +220,37 @@ def test_topk_exact_ties_and_signed_zero():
         _check_topk_exact(u, [n] * len(rows), k)
 
 
+@pytest.mark.parametrize("B,k", [(8192, 2048), (300, 300), (5000, 1)])
+def test_hs_anchor_select_nested_exact(B, k):
+    say(f"hs_anchor_select B={B} k={k}")
+    rng = np.random.default_rng(B + k)
+    lens = [0, 17, 4096, 60000, 131072]
+    u = np.round(rng.standard_normal((len(lens), 131072)), 2).astype(np.float32)  # ties
+    ut = torch.from_numpy(u).cuda()
+    vl = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    cand, sel = ops.hs_anchor_select(ut, vl, 131072, B, k)
+    torch.cuda.synchronize()
+    cand, sel = cand.cpu().numpy(), sel.cpu().numpy()
+    for i, n in enumerate(lens):
+        row = u[i, :n].astype(np.float64)
+        assert np.array_equal(cand[i], O.pad(O.hs_candidates(row, B), B)), i
+        assert np.array_equal(sel[i], O.pad(O.topk(row, k), k)), i
+
+
+@pytest.mark.parametrize("n", [16384, 9000])
+def test_topk_exact_short_rows_in_lds(n):
+    """Rows of at most 16K elements take the LDS-resident path."""
+    say(f"topk exact, LDS-resident rows n={n}")
+    rng = np.random.default_rng(n)
+    rows = [rng.standard_normal(n), np.round(rng.standard_normal(n), 1), np.zeros(n),
+            np.where(rng.random(n) < 0.5, -0.0, 0.0), rng.choice([-np.inf, 0.0, 1.0], n),
+            np.full(n, 7.0)]
+    u = np.stack(rows).astype(np.float32)
+    lens = [n, n - 1, n, 1, n // 2, 0]
+    for k in [1, 64, 2048, n - 3, n + 5]:
+        _check_topk_exact(u, lens, k)
+
+
 def test_topk_bucket_overflow_path():
     """More than the LDS candidate capacity share the threshold bucket."""
     say("topk with a crowded threshold bucket")
@@ -227,6 +258,8 @@ def test_topk_bucket_overflow_path():
     n = 100000
     u = (1.0 + rng.random(n) * 1e-3).astype(np.float32)      # one 12-bit bucket
     _check_topk_exact(u[None, :], [n], 2048)
+    rows = np.stack([u, np.full(n, 2.0, np.float32)])        # many rows: single-workgroup path
+    _check_topk_exact(np.repeat(rows, 40, axis=0), [n] * 80, 2048)
 
 
 # --------------------------------------------------------------------- HS ---
@@ -290,3 +323,33 @@ def test_determinism_permutation_and_homogeneity():
     d = dw.score(0)
     torch.cuda.synchronize()
     assert d[0, 5].item() == 4.0 * d[0, 3].item()
+
+
+def test_graph_replays_match_eager():
+    """The captured HS and full-scan steps reproduce the eager results on
+    every replay, with eager work and synchronisations in between."""
+    say("graph capture of the HS and full-scan steps vs eager")
+    wl = W.small_decode(12, n_seq=3, lens=[900, 3000, 5000], H=64, r=256, d_I=128, G=4, k=64,
+                        B=512, cache_dtype="bf16", plant=20, factor=3.0)
+    dw = DeviceWorkload(wl, hold_last=True)
+    dw.hs_step(append=True, keep_scores=True)
+    dw.full_step(append=False)
+    torch.cuda.synchronize()
+    ref_hs = dw.hs_sel.clone()
+    ref_cs = dw.cand_scores.clone()
+    ref_full = dw.sel.clone()
+    g_hs = dw.capture(hs=True, keep_scores=True)
+    g_full = dw.capture(hs=False, append=False)
+    for rep in range(3):
+        dw.hs_sel.fill_(-7)
+        dw.sel.fill_(-7)
+        dw.cand_scores.fill_(0.5)
+        torch.cuda.synchronize()
+        g_hs.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dw.hs_sel, ref_hs), rep
+        assert torch.equal(dw.cand_scores[1:], ref_cs[1:]), rep
+        _ = (dw.scores * 2).sum().item()          # eager work between replays
+        g_full.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dw.sel, ref_full), rep
