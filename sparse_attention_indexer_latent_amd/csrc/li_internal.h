@@ -20,10 +20,13 @@ struct CacheView {
   int32_t max_blocks;
   int32_t r;
   int32_t dtype;  // li_dtype
+  int32_t n_seq;
+  int32_t n_blocks;
 };
 
 inline CacheView view_of(const li_cache &c) {
-  return CacheView{c.data, c.scale, c.block_table, c.max_blocks, c.r, (int32_t)c.dtype};
+  return CacheView{c.data, c.scale, c.block_table, c.max_blocks, c.r, (int32_t)c.dtype, c.n_seq,
+                   c.n_blocks};
 }
 
 // append.hip

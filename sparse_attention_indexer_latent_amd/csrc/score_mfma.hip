@@ -17,8 +17,9 @@
 // Structure (one workgroup = 8 wavefronts, two per SIMD, one per CU):
 //  * The flattened list of 64-token pages of all queries is split into
 //    contiguous ranges, one per workgroup (balances ragged batches).  The
-//    plan and the block ids of the range cost two global round trips; the
-//    first pages' loads are issued before the query operands are fetched.
+//    exact plan and the block ids of the range cost two global round trips;
+//    the common decode shape (every query max_len long, query q on
+//    sequence q) is guessed at entry, so its first pages stream after one.
 //  * Pages stream HBM -> LDS with direct-to-LDS loads
 //    (global_load_lds_dwordx4), NSTAGE pages in flight, completion tracked
 //    with explicit vmcnt waits and a bare s_barrier.  A token row of 512 B
@@ -67,16 +68,14 @@ __device__ __forceinline__ int qpages(const int32_t *q_len, int i) { return (q_l
 
 // Wave 0 works out this workgroup's contiguous range of the flattened
 // (query, page) list and writes (query, page, sequence) per local page into
-// LDS.  The lengths and sequence ids of the first 64 queries are loaded once
-// into registers, so the plan costs one global round trip; sh.np receives the
-// page count (clamped to cap, which the host sizing guarantees whenever every
-// q_len honours the bound it was given).
+// LDS.  len0/seq0 hold the lengths and sequence ids of the first 64 queries
+// (lane i: query i), loaded by the caller; later queries are read from
+// memory.  sh.np receives the page count, clamped to cap (the host sizing
+// guarantees the range fits whenever every q_len honours its bound).
 template <typename SH>
-__device__ void plan_range(SH &sh, int n_q, const int32_t *q_len, const int32_t *q_seq, int cap) {
+__device__ void plan_range(SH &sh, int n_q, const int32_t *q_len, const int32_t *q_seq, int cap,
+                           int len0, int seq0) {
   const int lane = threadIdx.x % kWave;
-  if (threadIdx.x >= kWave) return;
-  const int len0 = lane < n_q ? q_len[lane] : 0;
-  const int seq0 = lane < n_q ? q_seq[lane] : 0;
   const int np0 = (len0 + 63) >> 6;
   auto pages_of = [&](int q) { return q < kWave ? __shfl(np0, q, kWave) : qpages(q_len, q); };
   auto seq_of = [&](int q) { return q < kWave ? __shfl(seq0, q, kWave) : q_seq[q]; };
@@ -151,15 +150,17 @@ struct MfmaShared {
   int32_t prow[kMaxPagesPerWG];
   int32_t gather_rows[kMaxPagesGather * kPage];
   int32_t np;
+  int32_t spec_ok;
 };
 
 constexpr int kThreads = 512;
+static_assert(kMaxPagesPerWG <= kThreads, "one block id per thread in the speculative plan");
 
 template <int R, int NSTAGE, bool HILO, bool GATHER>
 __global__ void __launch_bounds__(kThreads, 1)
 score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
                     const float *__restrict__ beta, int n_q, const int32_t *__restrict__ q_seq,
-                    const int32_t *__restrict__ q_len, CacheView cv,
+                    const int32_t *__restrict__ q_len, int max_len, CacheView cv,
                     const int32_t *__restrict__ cand, int B, float *__restrict__ out, int64_t ld) {
   using SH = MfmaShared<R, NSTAGE>;
   constexpr int kRowBytes = SH::kRowBytes;
@@ -223,45 +224,6 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
     if (drain) __builtin_amdgcn_s_waitcnt(0);
   };
 
-  if constexpr (!gather) {
-    plan_range(sh, n_q, q_len, q_seq, kMaxPagesPerWG);
-    __syncthreads();
-  } else {
-    // Every query owns exactly ceil(B / 64) candidate slots pages: the range
-    // needs no loads.  Padding slots (cand == -1) read pool row 0 and store
-    // -inf.
-    const int PB = (B + kPage - 1) / kPage;
-    const int64_t T = (int64_t)n_q * PB, G = gridDim.x, g = blockIdx.x;
-    const int64_t f0 = g * T / G;
-    const int cnt = (int)min<int64_t>((g + 1) * T / G - f0, kMaxPagesGather);
-    for (int p = tid; p < cnt; p += kThreads) {
-      sh.pq[p] = (int)((f0 + p) / PB);
-      sh.ppg[p] = (int)((f0 + p) % PB);
-    }
-    if (tid == 0) sh.np = cnt;
-    __syncthreads();
-  }
-  const int np = sh.np;
-  if (np == 0) return;
-  // candidate mode knows its first query without loads: fetch its operands
-  // now, in parallel with the candidate -> row lookups below
-  if constexpr (gather) load_query(sh.pq[0], false);
-  if constexpr (!gather) {
-    for (int p = tid; p < np; p += kThreads)
-      sh.prow[p] = cv.block_table[(int64_t)sh.pseq[p] * cv.max_blocks + sh.ppg[p]];
-  } else {
-    for (int e = tid; e < np * kPage; e += kThreads) {
-      const int p = e >> 6, row = e & 63;
-      const int q = sh.pq[p];
-      const int slot = min(sh.ppg[p] * kPage + row, B - 1);
-      const int t = cand[(int64_t)q * B + slot];
-      sh.gather_rows[e] =
-          t >= 0 ? cv.block_table[(int64_t)q_seq[q] * cv.max_blocks + (t >> 6)] * kPage + (t & 63)
-                 : -1;
-    }
-  }
-  __syncthreads();
-
   const char *gdata = (const char *)cv.data;
   auto issue_page = [&](int p, int s) {
     LDS3 char *dst = (LDS3 char *)sh.stage[s];
@@ -281,14 +243,102 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
     }
   };
 
+  int issued = 0;  // local pages whose loads are in flight
+  if constexpr (!gather) {
+    // Speculative plan for the common decode case, every query with
+    // ceil(max_len / 64) pages and query q reading sequence q: its block ids
+    // and first query operands load together with the real lengths, and the
+    // first pages stream at once.  Block ids are clamped into the pool, so a
+    // wrong guess costs bandwidth only; it is detected below, drained, and
+    // the exact plan replaces it.
+    const int PPQ = (max_len + kPage - 1) / kPage;
+    const bool try_spec = n_q <= kWave && n_q <= cv.n_seq && PPQ > 0 && PPQ <= cv.max_blocks;
+    int cnt_s = 0;
+    int64_t f0s = 0;
+    if (try_spec) {
+      const int64_t T = (int64_t)n_q * PPQ, G = gridDim.x, g = blockIdx.x;
+      f0s = g * T / G;
+      cnt_s = (int)min<int64_t>((g + 1) * T / G - f0s, kMaxPagesPerWG);
+    }
+    int len0 = 0, seq0 = 0;
+    if (wave == 0) {  // real lengths and sequence ids of the first 64 queries
+      len0 = lane < n_q ? q_len[lane] : 0;
+      seq0 = lane < n_q ? q_seq[lane] : 0;
+    }
+    int sq = 0, spg = 0, sblk = 0;
+    if (tid < cnt_s) {
+      sq = (int)((f0s + tid) / PPQ);
+      spg = (int)((f0s + tid) % PPQ);
+      sblk = cv.block_table[(int64_t)sq * cv.max_blocks + spg];
+    }
+    if (cnt_s > 0) load_query((int)(f0s / PPQ), false);
+    if (tid < cnt_s) {
+      sh.prow[tid] = (sblk >= 0 && sblk < cv.n_blocks) ? sblk : 0;
+      sh.pq[tid] = sq;
+      sh.ppg[tid] = spg;
+    }
+    lds_barrier();
+    for (; issued < NSTAGE - 1 && issued < cnt_s; ++issued) issue_page(issued, issued);
+    if (wave == 0) {
+      // the guess is the exact plan iff every query has PPQ pages and reads
+      // its own sequence
+      const bool bad = lane < n_q && (((len0 + kPage - 1) / kPage) != PPQ || seq0 != lane);
+      const bool ok = try_spec && __ballot(bad) == 0ull;
+      if (lane == 0) sh.spec_ok = ok ? 1 : 0;
+      if (!ok) plan_range(sh, n_q, q_len, q_seq, kMaxPagesPerWG, len0, seq0);
+      else if (lane == 0) sh.np = cnt_s;
+    }
+    lds_barrier();
+    if (!sh.spec_ok) {
+      // drain the speculative page loads before their LDS slots are reused
+      // (the operands of a query do not depend on the plan: cur_q stays)
+      __builtin_amdgcn_s_waitcnt(0);
+      issued = 0;
+      for (int p = tid; p < sh.np; p += kThreads)
+        sh.prow[p] = cv.block_table[(int64_t)sh.pseq[p] * cv.max_blocks + sh.ppg[p]];
+      __syncthreads();
+    }
+  } else {
+    // Every query owns exactly ceil(B / 64) candidate slot pages: the range
+    // needs no loads.  Padding slots (cand == -1) read pool row 0 and store
+    // -inf.
+    const int PB = (B + kPage - 1) / kPage;
+    const int64_t T = (int64_t)n_q * PB, G = gridDim.x, g = blockIdx.x;
+    const int64_t f0 = g * T / G;
+    const int cnt = (int)min<int64_t>((g + 1) * T / G - f0, kMaxPagesGather);
+    for (int p = tid; p < cnt; p += kThreads) {
+      sh.pq[p] = (int)((f0 + p) / PB);
+      sh.ppg[p] = (int)((f0 + p) % PB);
+    }
+    if (tid == 0) sh.np = cnt;
+    // the first query is known without loads: fetch its operands now, in
+    // parallel with the candidate -> row lookups below
+    if (cnt > 0) load_query((int)(f0 / PB), false);
+    __syncthreads();
+    for (int e = tid; e < sh.np * kPage; e += kThreads) {
+      const int p = e >> 6, row = e & 63;
+      const int q = sh.pq[p];
+      const int slot = min(sh.ppg[p] * kPage + row, B - 1);
+      const int t = cand[(int64_t)q * B + slot];
+      sh.gather_rows[e] =
+          t >= 0 ? cv.block_table[(int64_t)q_seq[q] * cv.max_blocks + (t >> 6)] * kPage + (t & 63)
+                 : -1;
+    }
+    __syncthreads();
+  }
+  const int np = sh.np;
+  if (np == 0) return;
+
   // Prologue: page 0's loads, then this query's operands, then the next
   // pages; waiting until at most the last pages' loads remain outstanding
-  // completes page 0 and the operands (loads return in order).
-  issue_page(0, 0);
-  if constexpr (!gather) load_query(sh.pq[0], false);
-#pragma unroll
-  for (int s = 1; s < NSTAGE - 1; ++s)
-    if (s < np) issue_page(s, s);
+  // completes page 0 and the operands (loads return in order).  A correct
+  // guess has already issued them.
+  if (issued == 0) {
+    issue_page(0, 0);
+    if (cur_q != sh.pq[0]) load_query(sh.pq[0], false);
+    issued = 1;
+  }
+  for (; issued < NSTAGE - 1 && issued < np; ++issued) issue_page(issued, issued);
   {
     const int later = min(NSTAGE - 2, np - 1);
     if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kInstPerWave));
@@ -378,7 +428,7 @@ hipError_t launch_t(const void *q_tilde, const float *w, const float *beta, int 
   G = std::max<int64_t>(G, (T_ub + cap - 1) / cap);
   if (G <= 0) return hipSuccess;
   score_mfma_kernel<R, NSTAGE, HILO, GATHER><<<(unsigned)G, kThreads, 0, st>>>(
-      q_tilde, w, beta, n_q, q_seq, q_len, cv, cand, B, out, ld);
+      q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, cand, B, out, ld);
   return hipGetLastError();
 }
 

@@ -175,6 +175,36 @@ def test_score_config1_32k_bf16():
     _scores_vs_oracle(wl, dw, RTOL_BF16)
 
 
+def test_score_plan_guess_holds_and_falls_back():
+    """The matrix-core scorer guesses the common decode plan (every query
+    ceil(max_len/64) pages long, query q on sequence q).  Scores must match
+    the oracle whether the guess holds or not: remapped sequences, a larger
+    max_len, and lengths that differ only inside the last page."""
+    say("score plan guess: holds / wrong sequence map / wrong page count / last-page raggedness")
+    L = 1000  # 16 pages; sequence 3 is longer, so the block table has room for 18
+    wl = W.small_decode(11, n_seq=4, lens=[L, L, L, L + 100], H=64, r=256, d_I=128, G=1, k=16,
+                        cache_dtype="bf16", nope_off=64, bias=True)
+    dw = DeviceWorkload(wl, hold_last=False)
+    dw.absorb(0)
+    lat = [O.sequence_latent(wl, s) for s in range(4)]
+
+    def run(q_seq, q_len, max_len, case):
+        qs = torch.tensor(q_seq, dtype=torch.int32, device="cuda")
+        ql = torch.tensor(q_len, dtype=torch.int32, device="cuda")
+        u = ops.score(dw.q_tilde, dw.w[0], dw.beta, qs, ql, max_len, dw.cache).cpu().numpy()
+        for s in range(len(q_seq)):
+            n = q_len[s]
+            o = O.layer_scores(lat[q_seq[s]][:n], wl.q[0, s], wl.Dt[0], wl.b[0], wl.nope_off,
+                               wl.w[0, s])
+            assert_scores_close(u[s, :n], o, RTOL_BF16, f"{case}: query {s}")
+
+    run([0, 1, 2, 3], [L, L, L, L], L, "guess holds")
+    run([3, 0, 1, 2], [L, L, L, L], L, "sequences remapped")
+    run([0, 1, 2, 3], [L, L, L, L], L + 64, "max_len one page larger")
+    run([0, 1, 2, 3], [L, L - 7, L - 30, L - 1], L, "lengths differ inside the last page")
+    run([1, 1, 1, 3], [L - 500, L, 64, L + 100], L + 100, "ragged, shared sequence")
+
+
 # ------------------------------------------------------------------- top-k ---
 
 def _topk_gpu(u, lens, k):
