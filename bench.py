@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip full-scan and cold-MALL legs")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run warmup + this many steps (for profilers); prints nothing else")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="with --profile-steps: also run a plain device copy of this many MiB "
+                         "three times (calibrates hardware byte counters)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host instead of replaying HIP graphs")
     return ap.parse_args()
@@ -55,6 +58,37 @@ def scored_positions(wl, hs: bool) -> int:
 
 def latent_bytes_per_token(wl) -> int:
     return {"bf16": 2, "fp8": 1, "fp32": 4}[wl.cache_dtype] * wl.r + (4 if wl.cache_dtype == "fp8" else 0)
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "anchor_scan_128k_b4_hbm_traffic.md")
+SCAN_SOURCES = ["sparse_attention_indexer_latent_amd/csrc/score_mfma.hip",
+                "sparse_attention_indexer_latent_amd/csrc/li_device.h"]
+
+
+def measured_traffic(wl):
+    """HBM bytes per anchor-scan launch from the committed counter summary
+    (calibrated FETCH_SIZE + WRITE_SIZE), or None when that summary covers
+    another workload or the scan kernel's source changed since it was taken."""
+    import hashlib
+    if wl.name != "hs-128k-b4" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith(("#", "|", "-", " ")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for f in SCAN_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl, seconds: float):
@@ -124,6 +158,11 @@ def main():
     if args.profile_steps:
         for _ in range(args.profile_steps):
             step()
+        if args.copy_mib:
+            x = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
+            y = torch.empty_like(x)
+            for _ in range(3):
+                torch.neg(x, out=y)  # reads and writes copy_mib MiB
         torch.cuda.synchronize()
         return
 
@@ -171,7 +210,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "score_mfma_kernel (anchor full scan)",
                      "achieved": scan_bytes / (scan_ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": scan_bytes / (scan_ms * 1e-3) / HBM_PEAK,
-                     "traffic": None, "avg_kernel_us": scan_ms * 1e3,
+                     "traffic": measured_traffic(wl), "avg_kernel_us": scan_ms * 1e3,
                      "bytes_per_launch": scan_bytes},
     }
 
