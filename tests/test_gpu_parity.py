@@ -205,6 +205,85 @@ def test_score_plan_guess_holds_and_falls_back():
     run([1, 1, 1, 3], [L - 500, L, 64, L + 100], L + 100, "ragged, shared sequence")
 
 
+def test_score_config2_fp8_sampled():
+    """Config 2 at full size (16 ragged sequences, 8K-128K, fp8 cache behind a
+    random block table) on the matrix-core path: sampled tokens of every
+    query, first and last pages included, against the oracle."""
+    say("score config 2 (16 ragged sequences, fp8 E4M3 + per-token scale): layers 0 and 3, sampled")
+    wl = W.config(2)
+    dw = DeviceWorkload(wl, hold_last=False)
+    rng = np.random.default_rng(2)
+    for l in (0, 3):
+        dw.absorb(l)
+        u = dw.score(l).cpu().numpy()
+        for s in range(wl.n_q):
+            seq, L = int(wl.q_seq[s]), int(wl.q_len[s])
+            rows = np.unique(np.concatenate([rng.integers(0, L, 1500), np.arange(64),
+                                             np.arange(L - 64, L),
+                                             wl.planted[seq][wl.planted[seq] < L]]))
+            C = O.store_latent(wl.latent(seq)[rows], wl.cache_dtype)[2]  # per-token quantiser
+            o = O.layer_scores(C, wl.q[l, s], wl.Dt[l], wl.b[l], wl.nope_off, wl.w[l, s])
+            assert_scores_close(u[s, rows], o, RTOL_FP8, f"layer {l} query {s} (L={L})")
+
+
+@pytest.mark.parametrize("qdt", ["fp32", "bf16"])
+def test_score_fp8_wide_head_range(qdt):
+    """fp8 cache with q~ whose heads span 2^-20 .. 2^20 in magnitude, one head
+    all zero and one holding a single non-zero: each head's fp8 split is scaled
+    on its own."""
+    say(f"score fp8 cache, q~ {qdt} with heads of very different magnitudes")
+    wl = W.small_decode(12, n_seq=2, lens=[777, 130], H=64, r=256, d_I=128, G=1, k=16,
+                        cache_dtype="fp8")
+    dw = DeviceWorkload(wl, hold_last=False)
+    rng = np.random.default_rng(3)
+    qt = rng.standard_normal((2, 64, 256)) * np.exp2(rng.integers(-20, 21, (2, 64, 1)))
+    qt[:, 5] = 0.0
+    qt[:, 9] = 0.0
+    qt[:, 9, 17] = 3.0
+    if qdt == "bf16":
+        bits = (qt.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        qt64 = O.bf16_decode(bits)
+        qdev = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        qt64 = qt.astype(np.float32).astype(np.float64)
+        qdev = torch.from_numpy(qt.astype(np.float32)).cuda()
+    w = rng.standard_normal((2, 64)).astype(np.float32)
+    beta = rng.standard_normal((2, 64)).astype(np.float32) * 1e-3
+    u = ops.score(qdev, torch.from_numpy(w).cuda(), torch.from_numpy(beta).cuda(), dw.q_seq,
+                  dw.q_len, dw.max_len, dw.cache).cpu().numpy()
+    for s in range(2):
+        C = O.sequence_latent(wl, s)
+        o = O.absorbed_scores(C, qt64[s], beta[s].astype(np.float64), w[s])
+        assert_scores_close(u[s, :len(o)], o, RTOL_FP8, f"query {s}")
+
+
+def test_score_more_than_64_queries():
+    """Batches above 64 queries take the workgroup scorer; both paths agree
+    with the oracle."""
+    say("score with 70 queries over 3 sequences (bf16, H=64)")
+    lens = [300, 1000, 64]
+    wl = W.small_decode(13, n_seq=3, lens=lens, H=64, r=256, d_I=128, G=1, k=16,
+                        cache_dtype="bf16", nope_off=64, bias=True)
+    dw = DeviceWorkload(wl, hold_last=False)
+    rng = np.random.default_rng(5)
+    n_q = 70
+    qs = rng.integers(0, 3, n_q).astype(np.int32)
+    ql = np.array([rng.integers(1, lens[s] + 1) for s in qs], dtype=np.int32)
+    qt = rng.standard_normal((n_q, 64, 256)).astype(np.float32) * 0.1
+    w = rng.standard_normal((n_q, 64)).astype(np.float32)
+    beta = rng.standard_normal((n_q, 64)).astype(np.float32) * 0.1
+    for nq in (n_q, 64):
+        u = ops.score(torch.from_numpy(qt[:nq]).cuda(), torch.from_numpy(w[:nq]).cuda(),
+                      torch.from_numpy(beta[:nq]).cuda(), torch.from_numpy(qs[:nq]).cuda(),
+                      torch.from_numpy(ql[:nq]).cuda(), int(ql[:nq].max()), dw.cache).cpu().numpy()
+        lat = [O.sequence_latent(wl, s) for s in range(3)]
+        for i in range(nq):
+            n = int(ql[i])
+            o = O.absorbed_scores(lat[qs[i]][:n], qt[i].astype(np.float64),
+                                  beta[i].astype(np.float64), w[i])
+            assert_scores_close(u[i, :n], o, RTOL_BF16, f"n_q={nq} query {i}")
+
+
 # ------------------------------------------------------------------- top-k ---
 
 def _topk_gpu(u, lens, k):
