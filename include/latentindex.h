@@ -115,22 +115,26 @@ li_status li_append_latent(const void *x, li_dtype x_dt, int32_t n_tok, int32_t 
 
 /*
  * li_absorb_queries -- query-side decoder absorption ("Methodology", eq. 6):
- * q~_{s,h} = D^T q_{s,h} and beta_{s,h} = q_{s,h}[nope_off:] . b.
- *   q        device [n_q, H, d_I] of q_dt (FP32 or BF16).
- *   Dt       device fp32 D transposed, [r, d_I] row-major; head h uses
- *            Dt + h * Dt_head_stride (elements; 0 = one decoder for all
- *            heads, the per-layer decoder of eq. 3).
- *   b        device fp32 [d_I - nope_off] key bias on the NoPE coordinates,
- *            or NULL for b = 0.  0 <= nope_off <= d_I.
- *   q_tilde  device fp32 [n_q, H, r] (out).
- *   beta     device fp32 [n_q, H] (out); may be NULL.
- * Accumulates in fp32.  H <= 1024, d_I <= 1024, r <= 1024; d_I and
- * Dt_head_stride multiples of 4, q and Dt 16-byte aligned.
+ * q~_{s,h} = D^T q_{s,h} and beta_{s,h} = q_{s,h}[nope_off:] . b, for
+ * n_layers layers in one call (each with its own decoder; every operand is
+ * stacked layer-major).
+ *   q        device [n_layers, n_q, H, d_I] of q_dt (FP32 or BF16).
+ *   Dt       device fp32 D transposed, per layer [r, d_I] row-major; head h
+ *            uses the layer's Dt + h * Dt_head_stride (elements; 0 = one
+ *            decoder for all heads, the per-layer decoder of eq. 3, else a
+ *            layer holds H * Dt_head_stride elements).
+ *   b        device fp32 [n_layers, d_I - nope_off] key bias on the NoPE
+ *            coordinates, or NULL for b = 0.  0 <= nope_off <= d_I.
+ *   q_tilde  device fp32 [n_layers, n_q, H, r] (out).
+ *   beta     device fp32 [n_layers, n_q, H] (out); may be NULL.
+ * Accumulates in fp32.  1 <= n_layers <= 64, H <= 1024, d_I <= 1024,
+ * r <= 1024; d_I and Dt_head_stride multiples of 4, q and Dt 16-byte
+ * aligned.
  */
-li_status li_absorb_queries(const void *q, li_dtype q_dt, int32_t n_q, int32_t H, int32_t d_I,
-                            const float *Dt, int64_t Dt_head_stride, const float *b,
-                            int32_t nope_off, int32_t r, float *q_tilde, float *beta,
-                            void *stream);
+li_status li_absorb_queries(const void *q, li_dtype q_dt, int32_t n_layers, int32_t n_q,
+                            int32_t H, int32_t d_I, const float *Dt, int64_t Dt_head_stride,
+                            const float *b, int32_t nope_off, int32_t r, float *q_tilde,
+                            float *beta, void *stream);
 
 /*
  * li_score -- score the shared cache for n_q queries ("Methodology", eq. 8):
@@ -197,23 +201,29 @@ li_status li_hs_anchor_select(const float *scores, int64_t ld, int32_t n_rows,
                               int32_t k, int32_t *sel, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * li_hs_select -- a follower layer's hierarchical selection ("Hierarchical
- * Selection" paragraph): rescore only the anchor's candidate set with the
- * follower's own absorbed queries, then keep its top-k within the set.
+ * li_hs_select -- the follower layers' hierarchical selection ("Hierarchical
+ * Selection" paragraph): rescore only the anchor's candidate set with each
+ * follower's own absorbed queries, then keep each follower's top-k within
+ * the set.  The n_f followers of a group share the candidate set, so one
+ * call serves them all (operands stacked follower-major).
  *   cand        device int32 [n_q, B]: ascending token ids of query i's
  *               candidates (e.g. li_topk with k = B on the anchor's scores),
  *               padded at the end with -1.
- *   q_tilde, qt_dt, w, beta, q_seq, H, cache: as for li_score.
+ *   n_f         followers, 1 <= n_f <= 64.
+ *   q_tilde     device [n_f, n_q, H, r] of qt_dt (FP32 or BF16).
+ *   w, beta     device fp32 [n_f, n_q, H]; beta may be NULL.
+ *   q_seq, H, cache: as for li_score.
  *   k           1 <= k <= B.
- *   out_idx     device int32 [n_q, k] (out): ascending token ids, -1 padded.
- *   cand_scores device fp32 [n_q, B] (out, may be NULL): the follower's score
- *               of each candidate slot; -inf in padding slots.
+ *   out_idx     device int32 [n_f, n_q, k] (out): ascending token ids, -1
+ *               padded.
+ *   cand_scores device fp32 [n_f, n_q, B] (out, may be NULL): each
+ *               follower's score of each candidate slot; -inf in padding.
  *   ws          device workspace of li_hs_workspace_bytes() bytes.
  * Ties are broken by token id (equivalently by candidate slot).
  */
-size_t li_hs_workspace_bytes(int32_t n_q, int32_t B, int32_t k);
-li_status li_hs_select(const int32_t *cand, int32_t B, const void *q_tilde, li_dtype qt_dt,
-                       const float *w, const float *beta, int32_t n_q, int32_t H,
+size_t li_hs_workspace_bytes(int32_t n_f, int32_t n_q, int32_t B, int32_t k);
+li_status li_hs_select(const int32_t *cand, int32_t B, int32_t n_f, const void *q_tilde,
+                       li_dtype qt_dt, const float *w, const float *beta, int32_t n_q, int32_t H,
                        const int32_t *q_seq, const li_cache *cache, int32_t k, int32_t *out_idx,
                        float *cand_scores, void *ws, size_t ws_bytes, void *stream);
 

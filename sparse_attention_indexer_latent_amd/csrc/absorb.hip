@@ -4,7 +4,8 @@
 //
 // For a decoder shared by the heads this is one small GEMM,
 // [n_q*H x d_I] x [d_I x r]; with per-head decoders it is one GEMM per head
-// over that head's queries.  Each workgroup computes a 32 x 32 output tile in
+// over that head's queries.  Several layers (each with its own decoder) go
+// in one launch: blockIdx.z enumerates (layer, head).  Each workgroup computes a 32 x 32 output tile in
 // fp32 from LDS-staged 32 x 128 slices of q and Dt (each thread 2 x 2
 // outputs); a decode layer (4 x 64 heads, r = 256) spreads over 64 workgroups,
 // so the call costs about one load round trip.  The work is applied once per
@@ -44,17 +45,25 @@ __global__ void __launch_bounds__(256)
 absorb_kernel(const void *__restrict__ q, int n_q, int H, int d_I, const float *__restrict__ Dt,
               int64_t head_stride, const float *__restrict__ b, int nope_off, int r,
               float *__restrict__ q_tilde, float *__restrict__ beta) {
+  // layer-major stacking of every operand
+  const bool per_head = head_stride != 0;
+  const int zH = per_head ? H : 1;
+  const int layer = blockIdx.z / zH;
+  const int64_t q_layer = (int64_t)layer * n_q * H * d_I;  // elements
+  Dt += (int64_t)layer * (per_head ? (int64_t)H * head_stride : (int64_t)r * d_I);
+  if (b) b += (int64_t)layer * (d_I - nope_off);
+  q_tilde += (int64_t)layer * n_q * H * r;
+  if (beta) beta += (int64_t)layer * n_q * H;
   __shared__ float As[kKC][kT + 4];  // As[d][row]
   __shared__ float Bs[kKC][kT + 4];  // Bs[d][j]
   constexpr int kPer4 = kT * kKC / 4 / 256;  // float4 loads of each operand per thread
-  const bool per_head = head_stride != 0;
-  const int h_fixed = blockIdx.z;
+  const int h_fixed = blockIdx.z % zH;
   const int n_rows = per_head ? n_q : n_q * H;
   const int row0 = blockIdx.y * kT, j0 = blockIdx.x * kT;
   const float *D = Dt + (per_head ? (int64_t)h_fixed * head_stride : 0);
   const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
   auto qrow = [&](int slot) -> int64_t {  // element offset of q row `slot`
-    return per_head ? ((int64_t)slot * H + h_fixed) * d_I : (int64_t)slot * d_I;
+    return q_layer + (per_head ? ((int64_t)slot * H + h_fixed) * d_I : (int64_t)slot * d_I);
   };
   float acc[2][2] = {};
   for (int d0 = 0; d0 < d_I; d0 += kKC) {
@@ -129,12 +138,12 @@ absorb_kernel(const void *__restrict__ q, int n_q, int H, int d_I, const float *
 
 }  // namespace
 
-hipError_t launch_absorb(const void *q, int q_dt, int n_q, int H, int d_I, const float *Dt,
+hipError_t launch_absorb(const void *q, int q_dt, int n_layers, int n_q, int H, int d_I, const float *Dt,
                          int64_t Dt_head_stride, const float *b, int nope_off, int r,
                          float *q_tilde, float *beta, hipStream_t st) {
   const bool per_head = Dt_head_stride != 0;
   const int n_rows = per_head ? n_q : n_q * H;
-  dim3 grid((r + kT - 1) / kT, (n_rows + kT - 1) / kT, per_head ? H : 1);
+  dim3 grid((r + kT - 1) / kT, (n_rows + kT - 1) / kT, n_layers * (per_head ? H : 1));
   if (q_dt == LI_BF16)
     absorb_kernel<true><<<grid, 256, 0, st>>>(q, n_q, H, d_I, Dt, Dt_head_stride, b, nope_off, r,
                                               q_tilde, beta);

@@ -103,11 +103,12 @@ li_status li_append_latent(const void *x, li_dtype x_dt, int32_t n_tok, int32_t 
                     "li_append_latent launch");
 }
 
-li_status li_absorb_queries(const void *q, li_dtype q_dt, int32_t n_q, int32_t H, int32_t d_I,
-                            const float *Dt, int64_t Dt_head_stride, const float *b,
-                            int32_t nope_off, int32_t r, float *q_tilde, float *beta,
-                            void *stream) {
+li_status li_absorb_queries(const void *q, li_dtype q_dt, int32_t n_layers, int32_t n_q,
+                            int32_t H, int32_t d_I, const float *Dt, int64_t Dt_head_stride,
+                            const float *b, int32_t nope_off, int32_t r, float *q_tilde,
+                            float *beta, void *stream) {
   if (q_dt != LI_FP32 && q_dt != LI_BF16) return fail(LI_ERR_INVALID, "q dtype must be FP32 or BF16");
+  if (n_layers < 1 || n_layers > 64) return fail(LI_ERR_INVALID, "n_layers = %d out of [1, 64]", n_layers);
   if (n_q < 0) return fail(LI_ERR_INVALID, "n_q < 0");
   if (H <= 0 || H > 1024 || d_I <= 0 || d_I > 1024 || r <= 0 || r > 1024)
     return fail(LI_ERR_INVALID, "H/d_I/r out of range (1..1024)");
@@ -118,7 +119,7 @@ li_status li_absorb_queries(const void *q, li_dtype q_dt, int32_t n_q, int32_t H
   if (!q || !Dt || !q_tilde) return fail(LI_ERR_INVALID, "q/Dt/q_tilde is NULL");
   li_status s = check_device();
   if (s != LI_OK) return s;
-  return hip_status(li::launch_absorb(q, q_dt, n_q, H, d_I, Dt, Dt_head_stride, b, nope_off, r,
+  return hip_status(li::launch_absorb(q, q_dt, n_layers, n_q, H, d_I, Dt, Dt_head_stride, b, nope_off, r,
                                       q_tilde, beta, (hipStream_t)stream),
                     "li_absorb_queries launch");
 }
@@ -151,10 +152,10 @@ li_status li_score(const void *q_tilde, li_dtype qt_dt, const float *w, const fl
   hipError_t e;
   if (li::score_mfma_supported(qt_dt, H, cv))
     e = li::launch_score_mfma(q_tilde, qt_dt, w, beta, n_q, H, q_seq, q_len, max_len, cv, nullptr,
-                              0, scores, ld, (hipStream_t)stream);
+                              0, 1, scores, ld, (hipStream_t)stream);
   else
     e = li::launch_score_valu(q_tilde, qt_dt, w, beta, n_q, H, q_seq, q_len, max_len, cv, nullptr,
-                              0, scores, ld, (hipStream_t)stream);
+                              0, 1, scores, ld, (hipStream_t)stream);
   return hip_status(e, "li_score launch");
 }
 
@@ -175,7 +176,7 @@ li_status li_topk(const float *scores, int64_t ld, int32_t n_rows, const int32_t
   if (need && (!ws || ws_bytes < need)) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
   li_status s = check_device();
   if (s != LI_OK) return s;
-  return hip_status(li::launch_topk(scores, ld, n_rows, valid_len, nullptr, 0, max_len, k, out_idx,
+  return hip_status(li::launch_topk(scores, ld, n_rows, valid_len, nullptr, 0, 1, max_len, k, out_idx,
                                     out_val, ws, (hipStream_t)stream),
                     "li_topk launch");
 }
@@ -206,54 +207,61 @@ li_status li_hs_anchor_select(const float *scores, int64_t ld, int32_t n_rows,
   return hip_status(e, "li_hs_anchor_select launch");
 }
 
-size_t li_hs_workspace_bytes(int32_t n_q, int32_t B, int32_t k) {
-  if (n_q <= 0 || B <= 0 || k <= 0) return 0;
+size_t li_hs_workspace_bytes(int32_t n_f, int32_t n_q, int32_t B, int32_t k) {
+  if (n_f <= 0 || n_q <= 0 || B <= 0 || k <= 0) return 0;
+  const int64_t rows = (int64_t)n_f * n_q;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return al((size_t)n_q * B * sizeof(float)) + al((size_t)n_q * sizeof(int32_t)) +
-         li::topk_ws_bytes(n_q, B, k);
+  return al((size_t)rows * B * sizeof(float)) + al((size_t)rows * sizeof(int32_t)) +
+         li::topk_ws_bytes((int)rows, B, k);
 }
 
-li_status li_hs_select(const int32_t *cand, int32_t B, const void *q_tilde, li_dtype qt_dt,
-                       const float *w, const float *beta, int32_t n_q, int32_t H,
+li_status li_hs_select(const int32_t *cand, int32_t B, int32_t n_f, const void *q_tilde,
+                       li_dtype qt_dt, const float *w, const float *beta, int32_t n_q, int32_t H,
                        const int32_t *q_seq, const li_cache *cache, int32_t k, int32_t *out_idx,
                        float *cand_scores, void *ws, size_t ws_bytes, void *stream) {
   li_status s = check_score_args(q_tilde, qt_dt, w, n_q, H, q_seq, cache);
   if (s != LI_OK) return s;
   if (B <= 0 || B > 65536) return fail(LI_ERR_INVALID, "B = %d out of [1, 65536]", B);
+  if (n_f < 1 || n_f > 64) return fail(LI_ERR_INVALID, "n_f = %d out of [1, 64]", n_f);
   if (k <= 0) return fail(LI_ERR_INVALID, "k = %d must be positive", k);
   if (B < k) return fail(LI_ERR_INVALID, "B (%d) < k (%d): the candidate set must hold k", B, k);
+  if ((int64_t)n_f * n_q > (1 << 20)) return fail(LI_ERR_INVALID, "n_f * n_q too large");
   if (n_q == 0) return LI_OK;
   if (!cand || !out_idx) return fail(LI_ERR_INVALID, "cand/out_idx is NULL");
-  size_t need = li_hs_workspace_bytes(n_q, B, k);
+  size_t need = li_hs_workspace_bytes(n_f, n_q, B, k);
   if (!ws || ws_bytes < need) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
   if ((s = check_device()) != LI_OK) return s;
+  const int rows = n_f * n_q;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   char *p = (char *)ws;
   float *sc = (float *)p;
-  p += al((size_t)n_q * B * sizeof(float));
+  p += al((size_t)rows * B * sizeof(float));
   int32_t *lens = (int32_t *)p;
-  p += al((size_t)n_q * sizeof(int32_t));
+  p += al((size_t)rows * sizeof(int32_t));
   void *tws = p;
   float *dst = cand_scores ? cand_scores : sc;
   hipStream_t st = (hipStream_t)stream;
   li::CacheView cv = li::view_of(*cache);
-  // 1. the follower's scores of every candidate slot (-inf on padding);
-  // 2. its top-k over all B slots: padding ranks below every candidate and
-  //    maps to id -1, so the output is the top-min(k, |C|) then -1 padding.
+  // Rows are (follower, query) pairs, follower-major; row i reads query
+  // i % n_q's candidate list.
+  // 1. each follower's scores of every candidate slot (-inf on padding);
+  // 2. each row's top-k over all B slots: padding ranks below every
+  //    candidate and maps to id -1, so the output is the top-min(k, |C|)
+  //    then -1 padding.
   hipError_t e;
   if (li::score_mfma_supported(qt_dt, H, cv))
-    e = li::launch_score_mfma(q_tilde, qt_dt, w, beta, n_q, H, q_seq, nullptr, B, cv, cand, B, dst,
-                              B, st);
+    e = li::launch_score_mfma(q_tilde, qt_dt, w, beta, rows, H, q_seq, nullptr, B, cv, cand, B,
+                              n_q, dst, B, st);
   else
-    e = li::launch_score_valu(q_tilde, qt_dt, w, beta, n_q, H, q_seq, nullptr, B, cv, cand, B, dst,
-                              B, st);
+    e = li::launch_score_valu(q_tilde, qt_dt, w, beta, rows, H, q_seq, nullptr, B, cv, cand, B,
+                              n_q, dst, B, st);
   const int32_t *vl = nullptr;
   if (e == hipSuccess && B > 16384) {  // the longer-row paths need per-row lengths
-    e = li::launch_fill_i32(lens, n_q, B, st);
+    e = li::launch_fill_i32(lens, rows, B, st);
     vl = lens;
   }
   if (e == hipSuccess)
-    e = li::launch_topk(dst, B, n_q, vl, cand, B, B, k, out_idx, nullptr, tws, st);
+    e = li::launch_topk(dst, B, rows, vl, cand, B, n_q, B, k, out_idx, nullptr, tws, st);
   return hip_status(e, "li_hs_select launch");
 }
 

@@ -36,34 +36,37 @@ hipError_t launch_append(const void *x, int x_dt, int n_tok, int d_model, const 
                          const int32_t *pos, const li_cache &cache, void *ws, hipStream_t st);
 
 // absorb.hip
-hipError_t launch_absorb(const void *q, int q_dt, int n_q, int H, int d_I, const float *Dt,
+hipError_t launch_absorb(const void *q, int q_dt, int n_layers, int n_q, int H, int d_I,
+                         const float *Dt,
                          int64_t Dt_head_stride, const float *b, int nope_off, int r,
                          float *q_tilde, float *beta, hipStream_t st);
 
 // Scorers.  Page mode (cand == nullptr): token t < q_len[i] of sequence
-// q_seq[i] goes to out[i*ld + t].  Candidate mode: slot j < B of query i
-// scores token cand[i*B + j] (or writes -inf where it is -1) into
-// out[i*ld + j]; q_len is unused.
+// q_seq[i] goes to out[i*ld + t].  Candidate mode: with c = i % cand_rows,
+// slot j < B of query i scores token cand[c*B + j] of sequence q_seq[c] (or
+// writes -inf where it is -1) into out[i*ld + j]; q_len is unused.  Several
+// layers' queries (i = layer * cand_rows + c) thus share one candidate list.
 // score_valu.hip: generic vector-ALU scorer, any supported dtype.
 hipError_t launch_score_valu(const void *q_tilde, int qt_dt, const float *w, const float *beta,
                              int n_q, int H, const int32_t *q_seq, const int32_t *q_len,
                              int max_len, const CacheView &cv, const int32_t *cand, int B,
-                             float *out, int64_t ld, hipStream_t st);
+                             int cand_rows, float *out, int64_t ld, hipStream_t st);
 
 // score_mfma.hip: matrix-core scorer for H == 64 and bf16/fp8 caches.
 bool score_mfma_supported(int qt_dt, int H, const CacheView &cv);
 hipError_t launch_score_mfma(const void *q_tilde, int qt_dt, const float *w, const float *beta,
                              int n_q, int H, const int32_t *q_seq, const int32_t *q_len,
                              int max_len, const CacheView &cv, const int32_t *cand, int B,
-                             float *out, int64_t ld, hipStream_t st);
+                             int cand_rows, float *out, int64_t ld, hipStream_t st);
 
 // topk.hip.  `ids` (may be null) maps a row position j to the id reported
-// for it (row i uses ids + i*ids_ld); positions are ordered by id exactly as
+// for it (row i uses ids + (i % ids_rows)*ids_ld); positions are ordered by id exactly as
 // by j (ids ascending), so ties break by position.  valid_len may be null
 // when every row is valid on [0, max_len) and max_len <= 16384.
 size_t topk_ws_bytes(int n_rows, int max_len, int k);
 hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
-                       const int32_t *ids, int64_t ids_ld, int max_len, int k, int32_t *out_idx,
+                       const int32_t *ids, int64_t ids_ld, int ids_rows, int max_len, int k,
+                       int32_t *out_idx,
                        float *out_val, void *ws, hipStream_t st);
 
 // Two nested selections (k_outer >= k_inner) in one pass; ws of

@@ -212,7 +212,8 @@ __global__ void __launch_bounds__(TOK * 8, 64 / TOK)
 score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
                     const float *__restrict__ beta, int n_q, const int32_t *__restrict__ q_seq,
                     const int32_t *__restrict__ q_len, int max_len, CacheView cv,
-                    const int32_t *__restrict__ cand, int B, float *__restrict__ out, int64_t ld) {
+                    const int32_t *__restrict__ cand, int B, int cand_rows, float *__restrict__ out,
+                    int64_t ld) {
   constexpr int kRowBytes = C8 ? R : 2 * R;
   using SH = MfmaShared<kRowBytes, NSTAGE, TOK>;
   constexpr int kThreads = TOK * 8;  // one wavefront per (head group, 32 tokens)
@@ -519,11 +520,11 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
     __syncthreads();
     for (int e = tid; e < sh.np * TOK; e += kThreads) {
       const int p = e / TOK, row = e % TOK;
-      const int q = sh.pq[p];
+      const int qc = sh.pq[p] % cand_rows;  // candidate lists repeat every cand_rows queries
       const int slot = min(sh.ppg[p] * TOK + row, B - 1);
-      const int t = cand[(int64_t)q * B + slot];
+      const int t = cand[(int64_t)qc * B + slot];
       sh.gather_rows[e] =
-          t >= 0 ? cv.block_table[(int64_t)q_seq[q] * cv.max_blocks + (t >> 6)] * kPage + (t & 63)
+          t >= 0 ? cv.block_table[(int64_t)q_seq[qc] * cv.max_blocks + (t >> 6)] * kPage + (t & 63)
                  : -1;
     }
     __syncthreads();
@@ -672,7 +673,8 @@ int g_num_cu = 0;
 template <int R, int NSTAGE, bool C8, bool QF32, bool GATHER, int TOK>
 hipError_t launch_t(const void *q_tilde, const float *w, const float *beta, int n_q,
                       const int32_t *q_seq, const int32_t *q_len, int max_len, const CacheView &cv,
-                      const int32_t *cand, int B, float *out, int64_t ld, hipStream_t st) {
+                      const int32_t *cand, int B, int cand_rows, float *out, int64_t ld,
+                      hipStream_t st) {
   if (g_num_cu == 0) {
     int dev = 0;
     (void)hipGetDevice(&dev);
@@ -686,15 +688,15 @@ hipError_t launch_t(const void *q_tilde, const float *w, const float *beta, int 
   G = std::max<int64_t>(G, (T_ub + cap - 1) / cap);
   if (G <= 0) return hipSuccess;
   score_mfma_kernel<R, NSTAGE, C8, QF32, GATHER, TOK><<<(unsigned)G, TOK * 8, 0, st>>>(
-      q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, cand, B, out, ld);
+      q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, cand, B, std::max(cand_rows, 1), out, ld);
   return hipGetLastError();
 }
 
 template <bool C8, bool QF32>
 hipError_t launch_mode(const void *q_tilde, const float *w, const float *beta, int n_q,
                        const int32_t *q_seq, const int32_t *q_len, int max_len,
-                       const CacheView &cv, const int32_t *cand, int B, float *out, int64_t ld,
-                       hipStream_t st) {
+                       const CacheView &cv, const int32_t *cand, int B, int cand_rows, float *out,
+                       int64_t ld, hipStream_t st) {
   // Workgroups of four wavefronts over 32-token units, two per CU: one can
   // compute while the other waits at its barrier.  fp8 units are half as
   // large: more of them in flight.
@@ -702,9 +704,10 @@ hipError_t launch_mode(const void *q_tilde, const float *w, const float *beta, i
   constexpr int kStages = C8 ? 6 : 4;
   if (cand)
     return launch_t<256, kStages, C8, QF32, true, kTok>(q_tilde, w, beta, n_q, q_seq, q_len,
-                                                        max_len, cv, cand, B, out, ld, st);
+                                                        max_len, cv, cand, B, cand_rows, out, ld,
+                                                        st);
   return launch_t<256, kStages, C8, QF32, false, kTok>(q_tilde, w, beta, n_q, q_seq, q_len, max_len,
-                                                       cv, cand, B, out, ld, st);
+                                                       cv, cand, B, cand_rows, out, ld, st);
 }
 
 }  // namespace
@@ -717,18 +720,18 @@ bool score_mfma_supported(int qt_dt, int H, const CacheView &cv) {
 hipError_t launch_score_mfma(const void *q_tilde, int qt_dt, const float *w, const float *beta,
                              int n_q, int H, const int32_t *q_seq, const int32_t *q_len,
                              int max_len, const CacheView &cv, const int32_t *cand, int B,
-                             float *out, int64_t ld, hipStream_t st) {
+                             int cand_rows, float *out, int64_t ld, hipStream_t st) {
   (void)H;
   const bool f32 = qt_dt == LI_FP32;
   if (cv.dtype == LI_FP8_E4M3)
     return f32 ? launch_mode<true, true>(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, cand,
-                                         B, out, ld, st)
+                                         B, cand_rows, out, ld, st)
                : launch_mode<true, false>(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, cand,
-                                          B, out, ld, st);
+                                          B, cand_rows, out, ld, st);
   return f32 ? launch_mode<false, true>(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, cand, B,
-                                        out, ld, st)
+                                        cand_rows, out, ld, st)
              : launch_mode<false, false>(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, cand,
-                                         B, out, ld, st);
+                                         B, cand_rows, out, ld, st);
 }
 
 }  // namespace li

@@ -19,7 +19,7 @@ __global__ void __launch_bounds__(256)
 score_valu_kernel(const void *__restrict__ q_tilde, int qt_dt, const float *__restrict__ w,
                   const float *__restrict__ beta, int H, const int32_t *__restrict__ q_seq,
                   const int32_t *__restrict__ q_len, CacheView cv, const int32_t *__restrict__ cand,
-                  int B, float *__restrict__ out, int64_t ld, int TT) {
+                  int B, int cand_rows, float *__restrict__ out, int64_t ld, int TT) {
   extern __shared__ float lds[];
   const int r = cv.r;
   const int i = blockIdx.y;
@@ -42,11 +42,12 @@ score_valu_kernel(const void *__restrict__ q_tilde, int qt_dt, const float *__re
     wsm[h] = w[(int64_t)i * H + h];
     bsm[h] = beta ? beta[(int64_t)i * H + h] : 0.f;
   }
-  const int seq = q_seq[i];
+  const int ci = cand ? i % cand_rows : i;  // candidate lists repeat every cand_rows queries
+  const int seq = q_seq[ci];
   const int32_t *bt = cv.block_table + (int64_t)seq * cv.max_blocks;
   // token of a slot: the position itself, or the candidate (-1: padding,
   // which reads pool row 0 and stores -inf)
-  auto token_of = [&](int slot) -> int { return cand ? cand[(int64_t)i * B + slot] : slot; };
+  auto token_of = [&](int slot) -> int { return cand ? cand[(int64_t)ci * B + slot] : slot; };
   auto phys_row = [&](int slot) -> int64_t {
     const int t = token_of(slot);
     return t >= 0 ? (int64_t)bt[t / kPage] * kPage + t % kPage : 0;
@@ -93,7 +94,7 @@ size_t valu_lds_bytes(int H, int r, int TT) {
 hipError_t launch_score_valu(const void *q_tilde, int qt_dt, const float *w, const float *beta,
                              int n_q, int H, const int32_t *q_seq, const int32_t *q_len,
                              int max_len, const CacheView &cv, const int32_t *cand, int B,
-                             float *out, int64_t ld, hipStream_t st) {
+                             int cand_rows, float *out, int64_t ld, hipStream_t st) {
   int TT = 64;
   while (TT > 4 && valu_lds_bytes(H, cv.r, TT) > 160 * 1024) TT >>= 1;
   const size_t lds = valu_lds_bytes(H, cv.r, TT);
@@ -106,7 +107,7 @@ hipError_t launch_score_valu(const void *q_tilde, int qt_dt, const float *w, con
   }
   dim3 grid((max_len + TT - 1) / TT, n_q);
   score_valu_kernel<<<grid, 256, lds, st>>>(q_tilde, qt_dt, w, beta, H, q_seq, q_len, cv, cand, B,
-                                            out, ld, TT);
+                                            max(cand_rows, 1), out, ld, TT);
   return hipGetLastError();
 }
 

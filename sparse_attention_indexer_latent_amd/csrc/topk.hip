@@ -81,7 +81,7 @@ __device__ void find_bin(TopkShared &sh, int nb, uint32_t need) {
 
 __global__ void __launch_bounds__(kThreads)
 topk_row_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ valid_len,
-                const int32_t *__restrict__ ids, int64_t ids_ld, int k,
+                const int32_t *__restrict__ ids, int64_t ids_ld, int ids_rows, int k,
                 int32_t *__restrict__ out_idx, float *__restrict__ out_val) {
   extern __shared__ __align__(16) unsigned char smem[];
   TopkShared &sh = *reinterpret_cast<TopkShared *>(smem);
@@ -89,7 +89,7 @@ topk_row_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
   const int tid = threadIdx.x;
   const int n = valid_len[row];
   const float *u = scores + (int64_t)row * ld;
-  const int32_t *idm = ids ? ids + (int64_t)row * ids_ld : nullptr;
+  const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
   int32_t *oi = out_idx + (int64_t)row * k;
   float *ov = out_val ? out_val + (int64_t)row * k : nullptr;
   const int m = min(k, n);
@@ -551,12 +551,12 @@ struct FinOut {
 __global__ void __launch_bounds__(kThreads)
 topk_finalize_kernel(const float *__restrict__ scores, int64_t ld,
                      const int32_t *__restrict__ valid_len, const int32_t *__restrict__ ids,
-                     int64_t ids_ld, FinOut o0, FinOut o1, int n_out, MultiWs m) {
+                     int64_t ids_ld, int ids_rows, FinOut o0, FinOut o1, int n_out, MultiWs m) {
   extern __shared__ __align__(16) unsigned char smem[];
   FinShared &sh = *reinterpret_cast<FinShared *>(smem);
   const int row = blockIdx.x, tid = threadIdx.x;
   const int n = valid_len[row];
-  const int32_t *idm = ids ? ids + (int64_t)row * ids_ld : nullptr;
+  const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
   const float *u = scores + (int64_t)row * ld;
   // padding of both outputs
   for (int j = 0; j < n_out; ++j) {
@@ -661,14 +661,14 @@ struct LdsRowShared {
 
 __global__ void __launch_bounds__(kThreads)
 topk_lds_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ valid_len,
-                int const_len, const int32_t *__restrict__ ids, int64_t ids_ld, int k,
+                int const_len, const int32_t *__restrict__ ids, int64_t ids_ld, int ids_rows, int k,
                 int32_t *__restrict__ out_idx, float *__restrict__ out_val) {
   extern __shared__ __align__(16) unsigned char smem[];
   LdsRowShared &sh = *reinterpret_cast<LdsRowShared *>(smem);
   const int row = blockIdx.x, tid = threadIdx.x;
   const int n = min(valid_len ? valid_len[row] : const_len, kLdsRow);
   const float *u = scores + (int64_t)row * ld;
-  const int32_t *idm = ids ? ids + (int64_t)row * ids_ld : nullptr;
+  const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
   int32_t *oi = out_idx + (int64_t)row * k;
   float *ov = out_val ? out_val + (int64_t)row * k : nullptr;
   const int m = min(k, n);
@@ -706,7 +706,7 @@ topk_lds_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
 }
 
 hipError_t launch_multi(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
-                        const int32_t *ids, int64_t ids_ld, int max_len, FinOut o0, FinOut o1,
+                        const int32_t *ids, int64_t ids_ld, int ids_rows, int max_len, FinOut o0, FinOut o1,
                         int n_out, void *ws, hipStream_t st) {
   MultiWs m = carve(ws, n_rows, max_len);
   const int kmax = n_out == 2 ? max(o0.k, o1.k) : o0.k;
@@ -722,7 +722,7 @@ hipError_t launch_multi(const float *scores, int64_t ld, int n_rows, const int32
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  topk_finalize_kernel<<<n_rows, kThreads, lds, st>>>(scores, ld, valid_len, ids, ids_ld, o0, o1,
+  topk_finalize_kernel<<<n_rows, kThreads, lds, st>>>(scores, ld, valid_len, ids, ids_ld, ids_rows, o0, o1,
                                                       n_out, m);
   return hipGetLastError();
 }
@@ -734,7 +734,7 @@ size_t topk_ws_bytes(int n_rows, int max_len, int) {
 }
 
 hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
-                       const int32_t *ids, int64_t ids_ld, int max_len, int k, int32_t *out_idx,
+                       const int32_t *ids, int64_t ids_ld, int ids_rows, int max_len, int k, int32_t *out_idx,
                        float *out_val, void *ws, hipStream_t st) {
   if (max_len <= kLdsRow) {
     const size_t lds = sizeof(LdsRowShared);
@@ -744,12 +744,12 @@ hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       attr_lds = true;
     }
-    topk_lds_kernel<<<n_rows, kThreads, lds, st>>>(scores, ld, valid_len, max_len, ids, ids_ld, k,
+    topk_lds_kernel<<<n_rows, kThreads, lds, st>>>(scores, ld, valid_len, max_len, ids, ids_ld, ids_rows, k,
                                                    out_idx, out_val);
     return hipGetLastError();
   }
   if (use_multi(n_rows, max_len))
-    return launch_multi(scores, ld, n_rows, valid_len, ids, ids_ld, max_len,
+    return launch_multi(scores, ld, n_rows, valid_len, ids, ids_ld, ids_rows, max_len,
                         FinOut{k, out_idx, out_val}, FinOut{0, nullptr, nullptr}, 1, ws, st);
   const size_t lds = sizeof(TopkShared);
   static bool attr_set = false;
@@ -758,7 +758,7 @@ hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  topk_row_kernel<<<n_rows, kThreads, lds, st>>>(scores, ld, valid_len, ids, ids_ld, k, out_idx,
+  topk_row_kernel<<<n_rows, kThreads, lds, st>>>(scores, ld, valid_len, ids, ids_ld, ids_rows, k, out_idx,
                                                  out_val);
   return hipGetLastError();
 }
@@ -780,7 +780,7 @@ hipError_t launch_fill_i32(int32_t *dst, int n, int32_t v, hipStream_t st) {
 hipError_t launch_topk2(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
                         int max_len, int k_outer, int32_t *out_outer, int k_inner,
                         int32_t *out_inner, void *ws, hipStream_t st) {
-  return launch_multi(scores, ld, n_rows, valid_len, nullptr, 0, max_len,
+  return launch_multi(scores, ld, n_rows, valid_len, nullptr, 0, 1, max_len,
                       FinOut{k_outer, out_outer, nullptr}, FinOut{k_inner, out_inner, nullptr}, 2,
                       ws, st);
 }

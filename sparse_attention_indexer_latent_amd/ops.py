@@ -54,15 +54,16 @@ _SIGS = {
     "li_append_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "li_append_latent": (_I32, [_P, _I32, _I32, _I32, _P, _P, _I32, _P, _P,
                                 ctypes.POINTER(LiCacheStruct), _P, _SZ, _P]),
-    "li_absorb_queries": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _I64, _P, _I32, _I32, _P, _P, _P]),
+    "li_absorb_queries": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _I32, _I32, _P, _P,
+                                 _P]),
     "li_score": (_I32, [_P, _I32, _P, _P, _I32, _I32, _P, _P, _I32,
                         ctypes.POINTER(LiCacheStruct), _P, _I64, _P]),
     "li_topk_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "li_topk": (_I32, [_P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "li_hs_anchor_workspace_bytes": (_SZ, [_I32, _I32]),
     "li_hs_anchor_select": (_I32, [_P, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _SZ, _P]),
-    "li_hs_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
-    "li_hs_select": (_I32, [_P, _I32, _P, _I32, _P, _P, _I32, _I32, _P,
+    "li_hs_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "li_hs_select": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P,
                             ctypes.POINTER(LiCacheStruct), _I32, _P, _P, _P, _SZ, _P]),
 }
 
@@ -183,20 +184,25 @@ def append_latent(x: torch.Tensor, cache: Cache, seq_idx: torch.Tensor, pos: tor
 def absorb_queries(q: torch.Tensor, Dt: torch.Tensor, b: Optional[torch.Tensor] = None,
                    nope_off: Optional[int] = None, q_tilde: Optional[torch.Tensor] = None,
                    beta: Optional[torch.Tensor] = None, per_head: bool = False):
-    """q [n_q, H, d_I]; Dt [r, d_I] (or [H, r, d_I] with per_head) -> (q~ [n_q,H,r], beta [n_q,H])."""
+    """One layer: q [n_q, H, d_I], Dt [r, d_I] (or [H, r, d_I] with per_head),
+    b [d_I - nope_off] -> (q~ [n_q, H, r], beta [n_q, H]).  Several layers in
+    one call: every operand gains a leading layer dimension."""
     _need(q, "q", (torch.float32, torch.bfloat16))
     _need(Dt, "Dt", torch.float32)
-    n_q, H, d_I = q.shape
+    layered = q.dim() == 4
+    L = q.shape[0] if layered else 1
+    n_q, H, d_I = q.shape[-3:]
     r = Dt.shape[-2]
     stride = r * d_I if per_head else 0
     no = d_I if nope_off is None else nope_off
     if b is not None:
         _need(b, "b", torch.float32)
+    lead = (L,) if layered else ()
     if q_tilde is None:
-        q_tilde = torch.empty((n_q, H, r), dtype=torch.float32, device=q.device)
+        q_tilde = torch.empty(lead + (n_q, H, r), dtype=torch.float32, device=q.device)
     if beta is None:
-        beta = torch.empty((n_q, H), dtype=torch.float32, device=q.device)
-    _check(lib().li_absorb_queries(q.data_ptr(), _dtype_code(q), n_q, H, d_I, Dt.data_ptr(),
+        beta = torch.empty(lead + (n_q, H), dtype=torch.float32, device=q.device)
+    _check(lib().li_absorb_queries(q.data_ptr(), _dtype_code(q), L, n_q, H, d_I, Dt.data_ptr(),
                                    stride, _ptr(b), no, r, q_tilde.data_ptr(), _ptr(beta),
                                    _stream()))
     return q_tilde, beta
@@ -282,25 +288,32 @@ def hs_anchor_select(scores: torch.Tensor, valid_len: torch.Tensor, max_len: int
     return cand, sel
 
 
-def hs_workspace(n_q: int, B: int, k: int, device="cuda") -> torch.Tensor:
-    return torch.empty(lib().li_hs_workspace_bytes(n_q, B, k), dtype=torch.uint8, device=device)
+def hs_workspace(n_q: int, B: int, k: int, device="cuda", n_f: int = 1) -> torch.Tensor:
+    return torch.empty(lib().li_hs_workspace_bytes(n_f, n_q, B, k), dtype=torch.uint8,
+                       device=device)
 
 
 def hs_select(cand: torch.Tensor, q_tilde: torch.Tensor, w: torch.Tensor,
               beta: Optional[torch.Tensor], q_seq: torch.Tensor, cache: Cache, k: int,
               out_idx: Optional[torch.Tensor] = None, cand_scores: Optional[torch.Tensor] = None,
               ws: Optional[torch.Tensor] = None, want_scores: bool = False):
+    """One follower: q_tilde [n_q, H, r], w/beta [n_q, H] -> out_idx [n_q, k].
+    n_f followers sharing the candidates: q_tilde [n_f, n_q, H, r], w/beta
+    [n_f, n_q, H] -> out_idx [n_f, n_q, k] (cand_scores likewise)."""
     _need(cand, "cand", torch.int32)
     _need(q_tilde, "q_tilde", (torch.float32, torch.bfloat16))
     n_q, B = cand.shape
-    H = q_tilde.shape[1]
+    layered = q_tilde.dim() == 4
+    n_f = q_tilde.shape[0] if layered else 1
+    H = q_tilde.shape[-2]
+    lead = (n_f,) if layered else ()
     if out_idx is None:
-        out_idx = torch.empty((n_q, k), dtype=torch.int32, device=cand.device)
+        out_idx = torch.empty(lead + (n_q, k), dtype=torch.int32, device=cand.device)
     if cand_scores is None and want_scores:
-        cand_scores = torch.empty((n_q, B), dtype=torch.float32, device=cand.device)
+        cand_scores = torch.empty(lead + (n_q, B), dtype=torch.float32, device=cand.device)
     if ws is None:
-        ws = hs_workspace(n_q, B, k, cand.device)
-    _check(lib().li_hs_select(cand.data_ptr(), B, q_tilde.data_ptr(), _dtype_code(q_tilde),
+        ws = hs_workspace(n_q, B, k, cand.device, n_f=n_f)
+    _check(lib().li_hs_select(cand.data_ptr(), B, n_f, q_tilde.data_ptr(), _dtype_code(q_tilde),
                               w.data_ptr(), _ptr(beta), n_q, H, q_seq.data_ptr(), cache.struct(),
                               k, out_idx.data_ptr(), _ptr(cand_scores), ws.data_ptr(), ws.numel(),
                               _stream()))

@@ -41,10 +41,11 @@ class DeviceWorkload:
         self.q_len = _t(wl.q_len, torch.int32, device)
         self.max_len = int(wl.q_len.max())
         G, H = wl.G, wl.H
-        self.Dt = [_t(wl.Dt[l], torch.float32, device) for l in range(G)]
-        self.b = [_t(wl.b[l], torch.float32, device) if wl.b.shape[1] else None for l in range(G)]
-        self.w = [_t(wl.w[l], torch.float32, device) for l in range(G)]
-        self.q = [_t(wl.q[l], torch.float32, device) for l in range(G)] if wl.q is not None else None
+        # every per-layer operand is stacked layer-major (index [l] is layer l)
+        self.Dt = _t(wl.Dt, torch.float32, device)
+        self.b = _t(wl.b, torch.float32, device) if wl.b.shape[1] else None
+        self.w = _t(wl.w, torch.float32, device)
+        self.q = _t(wl.q, torch.float32, device) if wl.q is not None else None
         self.fill_cache(hold_last)
         n_q = wl.n_q
         # last token of every sequence: appended by each decode step
@@ -54,8 +55,8 @@ class DeviceWorkload:
         self.new_pos = _t((wl.lens - 1).astype(np.int32), torch.int32, device)
         # per-step buffers
         r = wl.r
-        self.q_tilde = torch.empty((n_q, H, r), dtype=torch.float32, device=device)
-        self.beta = torch.empty((n_q, H), dtype=torch.float32, device=device)
+        self.q_tilde = torch.empty((G, n_q, H, r), dtype=torch.float32, device=device)
+        self.beta = torch.empty((G, n_q, H), dtype=torch.float32, device=device)
         self.scores = torch.empty((n_q, self.max_len), dtype=torch.float32, device=device)
         self.sel = torch.empty((G, n_q, wl.k), dtype=torch.int32, device=device)
         self.topk_ws = self._ws(ops.lib().li_topk_workspace_bytes(n_q, self.max_len, max(wl.k, wl.B or 0)))
@@ -63,7 +64,7 @@ class DeviceWorkload:
             self.cand = torch.empty((n_q, wl.B), dtype=torch.int32, device=device)
             self.hs_sel = torch.empty((G, n_q, wl.k), dtype=torch.int32, device=device)
             self.cand_scores = torch.empty((G, n_q, wl.B), dtype=torch.float32, device=device)
-            self.hs_ws = ops.hs_workspace(n_q, wl.B, wl.k, device)
+            self.hs_ws = ops.hs_workspace(n_q, wl.B, wl.k, device, n_f=max(G - 1, 1))
             self.anchor_ws = ops.hs_anchor_workspace(n_q, self.max_len, device)
 
     def _ws(self, n):
@@ -86,27 +87,33 @@ class DeviceWorkload:
     def append(self) -> None:
         ops.append_latent(self.x_new, self.cache, self.new_seq, self.new_pos)
 
-    def absorb(self, layer: int) -> None:
-        ops.absorb_queries(self.q[layer], self.Dt[layer], self.b[layer], self.wl.nope_off,
-                           q_tilde=self.q_tilde, beta=self.beta)
+    def absorb(self, layer: Optional[int] = None) -> None:
+        """Absorb one layer's queries, or (layer None) all layers in one call."""
+        if layer is None:
+            ops.absorb_queries(self.q, self.Dt, self.b, self.wl.nope_off,
+                               q_tilde=self.q_tilde, beta=self.beta)
+        else:
+            ops.absorb_queries(self.q[layer], self.Dt[layer],
+                               None if self.b is None else self.b[layer], self.wl.nope_off,
+                               q_tilde=self.q_tilde[layer], beta=self.beta[layer])
 
     def score(self, layer: int, scores: Optional[torch.Tensor] = None) -> torch.Tensor:
-        return ops.score(self.q_tilde, self.w[layer], self.beta, self.q_seq, self.q_len,
-                         self.max_len, self.cache, scores=self.scores if scores is None else scores)
+        return ops.score(self.q_tilde[layer], self.w[layer], self.beta[layer], self.q_seq,
+                         self.q_len, self.max_len, self.cache,
+                         scores=self.scores if scores is None else scores)
 
     # A decode step is split into three parts so that a scan of the whole
     # cache (the dominant kernel) can be timed with events on its stream:
-    # pre (append + layer-0 absorb), scan (layer-0 score), post (the rest).
+    # pre (append + every layer's absorb), scan (layer-0 score), post (the rest).
     def _pre(self, append: bool) -> None:
         if append:
             self.append()
-        self.absorb(0)
+        self.absorb()
 
     def _full_post(self) -> None:
         wl = self.wl
         ops.topk(self.scores, self.q_len, self.max_len, wl.k, out_idx=self.sel[0], ws=self.topk_ws)
         for l in range(1, wl.G):
-            self.absorb(l)
             self.score(l)
             ops.topk(self.scores, self.q_len, self.max_len, wl.k, out_idx=self.sel[l],
                      ws=self.topk_ws)
@@ -115,11 +122,10 @@ class DeviceWorkload:
         wl = self.wl
         ops.hs_anchor_select(self.scores, self.q_len, self.max_len, wl.B, wl.k, cand=self.cand,
                              sel=self.hs_sel[0], ws=self.anchor_ws)
-        for l in range(1, wl.G):
-            self.absorb(l)
-            ops.hs_select(self.cand, self.q_tilde, self.w[l], self.beta, self.q_seq, self.cache,
-                          wl.k, out_idx=self.hs_sel[l],
-                          cand_scores=self.cand_scores[l] if keep_scores else None,
+        if wl.G > 1:  # every follower at once: they share the candidate set
+            ops.hs_select(self.cand, self.q_tilde[1:], self.w[1:],
+                          self.beta[1:], self.q_seq, self.cache, wl.k, out_idx=self.hs_sel[1:],
+                          cand_scores=self.cand_scores[1:] if keep_scores else None,
                           ws=self.hs_ws)
 
     def full_step(self, append: bool = True, events=None) -> None:
@@ -153,7 +159,7 @@ class DeviceWorkload:
 class StepGraphs:
     """A decode step as two HIP graphs around one direct launch of the scan.
 
-    pre (append + layer-0 absorb) and post (selections and the other layers)
+    pre (append + every layer's absorb) and post (selections and the other layers)
     are captured graphs; the layer-0 scan between them is launched directly
     through a pre-marshalled call, so events recorded around it time exactly
     that kernel on its stream.  The library allocates nothing, so every replay
@@ -162,7 +168,7 @@ class StepGraphs:
     def __init__(self, dw: DeviceWorkload, hs: bool, append: bool = True,
                  keep_scores: bool = False):
         post = (lambda: dw._hs_post(keep_scores)) if hs else dw._full_post
-        self.scan = ops.prepared_score(dw.q_tilde, dw.w[0], dw.beta, dw.q_seq, dw.q_len,
+        self.scan = ops.prepared_score(dw.q_tilde[0], dw.w[0], dw.beta[0], dw.q_seq, dw.q_len,
                                        dw.max_len, dw.cache, dw.scores)
         parts = [lambda: dw._pre(append), post]
         side = torch.cuda.Stream()

@@ -52,19 +52,24 @@ def test_validation_errors_are_host_side(L):
     assert L.li_score(FAKE, ops.LI_FP8_E4M3, FAKE, None, 1, 64, FAKE, FAKE, 64, ctypes.byref(c),
                       FAKE, 64, None) == ops.LI_ERR_INVALID     # q~ cannot be fp8
     # HS: B < k is invalid (the candidate set must hold k)
-    assert L.li_hs_select(FAKE, 100, FAKE, ops.LI_FP32, FAKE, None, 1, 64, FAKE, ctypes.byref(c),
+    assert L.li_hs_select(FAKE, 100, 3, FAKE, ops.LI_FP32, FAKE, None, 1, 64, FAKE, ctypes.byref(c),
                           200, FAKE, None, FAKE, 1 << 30, None) == ops.LI_ERR_INVALID
     assert b"B (100) < k (200)" in L.li_last_error()
+    assert L.li_hs_select(FAKE, 100, 0, FAKE, ops.LI_FP32, FAKE, None, 1, 64, FAKE, ctypes.byref(c),
+                          50, FAKE, None, FAKE, 1 << 30, None) == ops.LI_ERR_INVALID  # n_f < 1
     # append: P NULL requires d_model == r; odd r_R
     assert L.li_append_latent(FAKE, ops.LI_FP32, 4, 100, None, None, 0, FAKE, FAKE,
                               ctypes.byref(c), None, 0, None) == ops.LI_ERR_INVALID
     assert L.li_append_latent(FAKE, ops.LI_FP32, 4, 256, None, FAKE, 3, FAKE, FAKE,
                               ctypes.byref(c), None, 0, None) == ops.LI_ERR_INVALID
-    assert L.li_absorb_queries(FAKE, ops.LI_FP32, 1, 64, 128, FAKE, 0, None, 129, 256, FAKE, None,
-                               None) == ops.LI_ERR_INVALID
+    assert L.li_absorb_queries(FAKE, ops.LI_FP32, 1, 1, 64, 128, FAKE, 0, None, 129, 256, FAKE,
+                               None, None) == ops.LI_ERR_INVALID  # nope_off > d_I
+    assert L.li_absorb_queries(FAKE, ops.LI_FP32, 0, 1, 64, 128, FAKE, 0, None, 64, 256, FAKE,
+                               None, None) == ops.LI_ERR_INVALID  # n_layers < 1
 
 
 def test_workspace_sizes(L):
     assert L.li_append_workspace_bytes(4, 7168, 256, 0) == 0
     assert L.li_append_workspace_bytes(4, 7168, 256, 1) > 0
-    assert L.li_hs_workspace_bytes(4, 8192, 2048) >= 4 * 8192 * 4
+    assert L.li_hs_workspace_bytes(1, 4, 8192, 2048) >= 4 * 8192 * 4
+    assert L.li_hs_workspace_bytes(3, 4, 8192, 2048) >= 3 * 4 * 8192 * 4

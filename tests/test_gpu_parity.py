@@ -96,22 +96,32 @@ def test_append_projection_and_rope(dtype, xdt):
 
 @pytest.mark.parametrize("per_head", [False, True])
 @pytest.mark.parametrize("qdt", [torch.float32, torch.bfloat16])
-def test_absorb_matches_oracle(per_head, qdt):
-    say(f"absorb per_head={per_head} q={qdt}")
-    rng = np.random.default_rng(9)
+@pytest.mark.parametrize("n_layers", [1, 3])
+def test_absorb_matches_oracle(per_head, qdt, n_layers):
+    """One layer, or several layers (each with its own decoder and bias)
+    stacked into one call."""
+    say(f"absorb per_head={per_head} q={qdt} layers={n_layers}")
+    rng = np.random.default_rng(9 + n_layers)
     n_q, H, d_I, r, no = 3, 64, 128, 256, 64
-    q = rng.standard_normal((n_q, H, d_I)).astype(np.float32)
-    Dt = (rng.standard_normal((H, r, d_I) if per_head else (r, d_I)) / 16).astype(np.float32)
-    b = rng.standard_normal(d_I - no).astype(np.float32)
-    qt_dev = torch.from_numpy(q).cuda().to(qdt)
-    qe = qt_dev.float().cpu().numpy()
-    qt, beta = ops.absorb_queries(qt_dev, torch.from_numpy(Dt).cuda(), torch.from_numpy(b).cuda(),
-                                  no, per_head=per_head)
-    for s in range(n_q):
-        oq, ob = O.absorb(qe[s], Dt, b, no)
-        g = qt[s].cpu().numpy()
-        assert np.max(np.abs(g - oq)) <= 1e-5 * np.abs(oq).max()
-        assert np.max(np.abs(beta[s].cpu().numpy() - ob)) <= 1e-5 * (np.abs(ob).max() + 1)
+    q = rng.standard_normal((n_layers, n_q, H, d_I)).astype(np.float32)
+    Dt = (rng.standard_normal((n_layers, H, r, d_I) if per_head else (n_layers, r, d_I)) / 16
+          ).astype(np.float32)
+    b = rng.standard_normal((n_layers, d_I - no)).astype(np.float32)
+    q_dev = torch.from_numpy(q).cuda().to(qdt)
+    qe = q_dev.float().cpu().numpy()
+    if n_layers == 1:
+        qt, beta = ops.absorb_queries(q_dev[0], torch.from_numpy(Dt[0]).cuda(),
+                                      torch.from_numpy(b[0]).cuda(), no, per_head=per_head)
+        qt, beta = qt[None], beta[None]
+    else:
+        qt, beta = ops.absorb_queries(q_dev, torch.from_numpy(Dt).cuda(), torch.from_numpy(b).cuda(),
+                                      no, per_head=per_head)
+    qt, beta = qt.cpu().numpy(), beta.cpu().numpy()
+    for l in range(n_layers):
+        for s in range(n_q):
+            oq, ob = O.absorb(qe[l, s], Dt[l], b[l], no)
+            assert np.max(np.abs(qt[l, s] - oq)) <= 1e-5 * np.abs(oq).max(), (l, s)
+            assert np.max(np.abs(beta[l, s] - ob)) <= 1e-5 * (np.abs(ob).max() + 1), (l, s)
 
 
 # ------------------------------------------------------------------- score ---
@@ -191,7 +201,7 @@ def test_score_plan_guess_holds_and_falls_back():
     def run(q_seq, q_len, max_len, case):
         qs = torch.tensor(q_seq, dtype=torch.int32, device="cuda")
         ql = torch.tensor(q_len, dtype=torch.int32, device="cuda")
-        u = ops.score(dw.q_tilde, dw.w[0], dw.beta, qs, ql, max_len, dw.cache).cpu().numpy()
+        u = ops.score(dw.q_tilde[0], dw.w[0], dw.beta[0], qs, ql, max_len, dw.cache).cpu().numpy()
         for s in range(len(q_seq)):
             n = q_len[s]
             o = O.layer_scores(lat[q_seq[s]][:n], wl.q[0, s], wl.Dt[0], wl.b[0], wl.nope_off,
@@ -405,6 +415,12 @@ def test_hs_select_matches_oracle(dtype, H, r):
             full = O.layer_scores(C[:L], wl.q[l, s], wl.Dt[l], wl.b[l], wl.nope_off, wl.w[l, s])
             if L <= wl.B:                                         # C = everything: HS = full
                 assert_selection_band(sel, full, wl.k, rtol, f"HS=full follower {l} q {s}")
+    # one follower per call gives the same bits as all followers in one call
+    for l in range(1, wl.G):
+        one, one_cs = ops.hs_select(dw.cand, dw.q_tilde[l], dw.w[l], dw.beta[l], dw.q_seq,
+                                    dw.cache, wl.k, want_scores=True)
+        assert torch.equal(one, dw.hs_sel[l]), l
+        assert torch.equal(one_cs, dw.cand_scores[l]), l
 
 
 # ------------------------------------------------------------ metamorphic ---
