@@ -207,28 +207,30 @@ topk_row_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
 
 // ---------------------------------------------------------------------------
 // Multi-workgroup path for few, long rows (decode: one row per query).
-//   clear:    zero the per-row 4096-bin histogram in the workspace
-//   hist:     one workgroup per 2048-element segment: LDS histogram of the
-//             top 12 key bits, merged into the row histogram with atomics
-//             (integer counts: the result does not depend on their order)
-//   extract:  one workgroup per segment finds the bucket b1 of the largest
-//             requested k from the row histogram and writes, in position
-//             order, every (key, position) with top-12 bits >= b1
-//   finalize: one workgroup per row gathers the extracted lists (about
-//             k + one bucket entries) into LDS, refines the exact k-th key
-//             for each requested k and emits ascending positions.
+//   clear:   zero the per-row histograms in the workspace
+//   hist:    one workgroup per 2048-element segment: LDS histogram of the
+//            top 12 key bits, merged into the row histogram with atomics
+//            (integer counts: the result does not depend on their order)
+//   extract: one workgroup per segment finds, from the row histogram, the
+//            12-bit bucket of each requested k; writes, in position order,
+//            every (key, position) at or above the bucket of the largest k;
+//            and counts the keys of each threshold bucket into a global
+//            histogram of their next 10 bits
+//   select:  one workgroup per segment derives the exact thresholds, its
+//            output offset and emits its own selected positions (below).
 // ---------------------------------------------------------------------------
 
 constexpr int kSeg = 2048;
 constexpr int kSegThreads = 256;
 constexpr int kSegPer = kSeg / kSegThreads;  // 8 consecutive positions per thread
-constexpr int kFinCap = 12288;               // LDS list capacity of the finalize step
 constexpr int kMaxSegs = 1024;
 
 struct MultiWs {
   uint32_t *hist;     // [n_rows][kBins]
+  uint32_t *h10;      // [n_rows][2][1024]: next 10 bits of each output's threshold bucket
   uint32_t *seg_cnt;  // [n_rows][S]
-  uint2 *list;        // [n_rows][S][kSeg]  (key, position)
+  uint32_t *lkey;     // [n_rows][S][kSeg]
+  int32_t *lpos;      // [n_rows][S][kSeg]
   int S;
 };
 
@@ -238,18 +240,22 @@ MultiWs carve(void *ws, int n_rows, int max_len) {
   MultiWs m;
   m.S = (max_len + kSeg - 1) / kSeg;
   char *p = (char *)ws;
-  m.hist = (uint32_t *)p;
-  p += align256((size_t)n_rows * kBins * 4);
+  m.hist = (uint32_t *)p;  // hist and h10 are adjacent: one clear covers both
+  p += (size_t)n_rows * kBins * 4;
+  m.h10 = (uint32_t *)p;
+  p += align256((size_t)n_rows * 2 * 1024 * 4);
   m.seg_cnt = (uint32_t *)p;
   p += align256((size_t)n_rows * m.S * 4);
-  m.list = (uint2 *)p;
+  m.lkey = (uint32_t *)p;
+  p += align256((size_t)n_rows * m.S * kSeg * 4);
+  m.lpos = (int32_t *)p;
   return m;
 }
 
 size_t multi_ws_bytes(int n_rows, int max_len) {
   const size_t S = (max_len + kSeg - 1) / kSeg;
-  return align256((size_t)n_rows * kBins * 4) + align256((size_t)n_rows * S * 4) +
-         (size_t)n_rows * S * kSeg * sizeof(uint2);
+  return (size_t)n_rows * kBins * 4 + align256((size_t)n_rows * 2 * 1024 * 4) +
+         align256((size_t)n_rows * S * 4) + 2 * align256((size_t)n_rows * S * kSeg * 4);
 }
 
 bool use_multi(int n_rows, int max_len) {
@@ -288,9 +294,10 @@ topk_hist_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__
     if (h[b]) atomicAdd(&g[b], h[b]);
 }
 
-// Block-wide exclusive scan for kSegThreads threads.
-__device__ __forceinline__ uint32_t seg_scan(uint32_t v, uint32_t *wt, uint32_t *total) {
-  constexpr int W = kSegThreads / kWave;
+// Block-wide exclusive scan for NT threads.
+template <int NT>
+__device__ __forceinline__ uint32_t nt_scan(uint32_t v, uint32_t *wt, uint32_t *total) {
+  constexpr int W = NT / kWave;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const uint32_t x = wave_incl_scan(v);
   if (lane == kWave - 1) wt[wave] = x;
@@ -306,11 +313,41 @@ __device__ __forceinline__ uint32_t seg_scan(uint32_t v, uint32_t *wt, uint32_t 
   return before + x - v;
 }
 
+// Bin of the nd-th largest entry of hist[0 .. nb) (nb a multiple of NT,
+// highest bins to thread 0).  Returns the bin; *above gets the count in
+// higher bins, *count the bin's own count.
+template <int NT>
+__device__ uint32_t nt_find(const uint32_t *hist, int nb, uint32_t nd, uint32_t *wt, uint32_t *res,
+                            uint32_t *above, uint32_t *count) {
+  const int tid = threadIdx.x;
+  const int per = nb / NT;
+  const int top = nb - 1 - tid * per;
+  uint32_t sum = 0;
+  for (int e = 0; e < per; ++e) sum += hist[top - e];
+  uint32_t tot;
+  uint32_t run = nt_scan<NT>(sum, wt, &tot);
+  for (int e = 0; e < per; ++e) {
+    const uint32_t c = hist[top - e];
+    if (run < nd && nd <= run + c) {
+      res[0] = top - e;
+      res[1] = run;
+      res[2] = c;
+    }
+    run += c;
+  }
+  lds_sync();
+  const uint32_t b = res[0];
+  *above = res[1];
+  *count = res[2];
+  lds_sync();
+  return b;
+}
+
 __global__ void __launch_bounds__(kSegThreads)
 topk_extract_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ valid_len,
-                    int kmax, MultiWs m) {
+                    int k0, int k1, MultiWs m) {
   __shared__ uint32_t wt[kSegThreads / kWave];
-  __shared__ uint32_t s_b1;
+  __shared__ uint32_t res[4];
   const int row = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
   const int n = valid_len[row];
   const int p0 = seg * kSeg;
@@ -318,29 +355,13 @@ topk_extract_kernel(const float *__restrict__ scores, int64_t ld, const int32_t 
     if (tid == 0) m.seg_cnt[(int64_t)row * m.S + seg] = 0;
     return;
   }
-  uint32_t b1 = 0;
-  if (n > kmax) {
-    // bucket of the kmax-th largest key: suffix scan of the row histogram,
-    // highest bins first (16 per thread)
-    const uint32_t *g = m.hist + (int64_t)row * kBins;
-    constexpr int per = kBins / kSegThreads;
-    const int top = kBins - 1 - tid * per;
-    uint32_t c[per], sum = 0;
-#pragma unroll
-    for (int e = 0; e < per; ++e) {
-      c[e] = g[top - e];
-      sum += c[e];
-    }
-    uint32_t tot;
-    uint32_t run = seg_scan(sum, wt, &tot);
-#pragma unroll
-    for (int e = 0; e < per; ++e) {
-      if (run < (uint32_t)kmax && (uint32_t)kmax <= run + c[e]) s_b1 = top - e;
-      run += c[e];
-    }
-    lds_sync();
-    b1 = s_b1;
-  }
+  const uint32_t *g = m.hist + (int64_t)row * kBins;
+  // threshold buckets of both outputs (all ones: the output takes every key)
+  uint32_t bk[2] = {0xFFFFFFFFu, 0xFFFFFFFFu}, above, c;
+  if (k0 < n) bk[0] = nt_find<kSegThreads>(g, kBins, (uint32_t)k0, wt, res, &above, &c);
+  if (k1 > 0 && k1 < n) bk[1] = nt_find<kSegThreads>(g, kBins, (uint32_t)k1, wt, res, &above, &c);
+  const int kmax = max(k0, k1);
+  const uint32_t b1 = kmax < n ? (k1 > k0 ? bk[1] : bk[0]) : 0u;  // extraction bucket
   const float *u = scores + (int64_t)row * ld;
   const int pb = p0 + tid * kSegPer;
   uint32_t key[kSegPer];
@@ -352,26 +373,23 @@ topk_extract_kernel(const float *__restrict__ scores, int64_t ld, const int32_t 
     cnt += (p < n && (key[e] >> 20) >= b1) ? 1u : 0u;
   }
   uint32_t tot;
-  uint32_t pos = seg_scan(cnt, wt, &tot);
-  uint2 *out = m.list + ((int64_t)row * m.S + seg) * kSeg;
+  uint32_t pos = nt_scan<kSegThreads>(cnt, wt, &tot);
+  const int64_t off = ((int64_t)row * m.S + seg) * kSeg;
+  uint32_t *h10 = m.h10 + (int64_t)row * 2 * 1024;
 #pragma unroll
   for (int e = 0; e < kSegPer; ++e) {
     const int p = pb + e;
-    if (p < n && (key[e] >> 20) >= b1) out[pos++] = make_uint2(key[e], (uint32_t)p);
+    if (p < n && (key[e] >> 20) >= b1) {
+      m.lkey[off + pos] = key[e];
+      m.lpos[off + pos] = p;
+      ++pos;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (p < n && (key[e] >> 20) == bk[j]) atomicAdd(&h10[j * 1024 + ((key[e] >> 10) & 1023u)], 1u);
   }
   if (tid == 0) m.seg_cnt[(int64_t)row * m.S + seg] = tot;
 }
-
-struct FinShared {
-  uint32_t lkey[kFinCap];
-  int32_t lpos[kFinCap];
-  uint32_t hist[kBins];
-  uint32_t hist12[kBins];  // the row's top-12-bit histogram, kept for every output
-  uint32_t small[4096];
-  uint32_t seg_off[kMaxSegs + 1];
-  uint32_t wtot[kWaves];
-  uint32_t sel_bin, sel_above, sel_count, n_small;
-};
 
 // Radix refinement of the `need`-th largest key among the entries given by
 // `get(i)` for i < M.  Returns theta; *need_eq receives how many entries equal
@@ -548,99 +566,216 @@ struct FinOut {
   float *val;
 };
 
-__global__ void __launch_bounds__(kThreads)
-topk_finalize_kernel(const float *__restrict__ scores, int64_t ld,
-                     const int32_t *__restrict__ valid_len, const int32_t *__restrict__ ids,
-                     int64_t ids_ld, int ids_rows, FinOut o0, FinOut o1, int n_out, MultiWs m) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  FinShared &sh = *reinterpret_cast<FinShared *>(smem);
-  const int row = blockIdx.x, tid = threadIdx.x;
+// ---------------------------------------------------------------------------
+// Select step of the multi-workgroup path, one workgroup per (row, segment).
+// Every workgroup derives the exact thresholds itself: the 12-bit bucket from
+// the row histogram, the next 10 bits from the bucket's histogram built by the
+// extract step, the last 10 bits from the row's extracted keys that share
+// those 22 bits.  The same pass over the extracted keys counts, in the
+// segments before its own, the keys above each threshold and those equal to
+// it, which fixes the output offset of the segment's first selected key; the
+// segment then emits its own selected keys in ascending positions.  Two
+// outputs share every pass (their per-thread counts ride in the two halves
+// of a 32-bit word where they are bounded by 2048).
+// ---------------------------------------------------------------------------
+constexpr int kSelThreads = 512;
+constexpr int kSelBatch = 16;       // extracted keys per thread in flight
+constexpr int kMaxChunks = 4096;    // chunk (16 keys) -> segment table
+
+struct SelShared {
+  uint32_t seg_off[kMaxSegs + 1];
+  uint16_t cseg[kMaxChunks];
+  uint32_t hlow[2][1024];  // low 10 bits of the keys sharing the 22-bit prefix: whole row
+  uint32_t hbef[2][1024];  // ... in segments before this one
+  uint32_t wt[kSelThreads / kWave];
+  uint32_t res[4];
+};
+
+__global__ void __launch_bounds__(kSelThreads)
+topk_select_kernel(const float *__restrict__ scores, int64_t ld,
+                   const int32_t *__restrict__ valid_len, const int32_t *__restrict__ ids,
+                   int64_t ids_ld, int ids_rows, FinOut o0, FinOut o1, int n_out, MultiWs m) {
+  __shared__ SelShared sh;
+  const int row = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
   const int n = valid_len[row];
-  const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
-  const float *u = scores + (int64_t)row * ld;
-  // padding of both outputs
-  for (int j = 0; j < n_out; ++j) {
-    const FinOut &o = j ? o1 : o0;
-    const int mm = min(o.k, n);
-    for (int t = mm + tid; t < o.k; t += kThreads) {
-      o.idx[(int64_t)row * o.k + t] = -1;
-      if (o.val) o.val[(int64_t)row * o.k + t] = -INFINITY;
+  const FinOut out[2] = {o0, o1};
+  if (seg == 0) {  // padding of the outputs
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (j >= n_out) continue;
+      for (int t = min(out[j].k, n) + tid; t < out[j].k; t += kSelThreads) {
+        out[j].idx[(int64_t)row * out[j].k + t] = -1;
+        if (out[j].val) out[j].val[(int64_t)row * out[j].k + t] = -INFINITY;
+      }
     }
   }
-  if (n <= 0) return;
   const int S = (n + kSeg - 1) / kSeg;
+  if (n <= 0 || seg >= S) return;  // uniform per workgroup
+  const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
+  const float *u = scores + (int64_t)row * ld;
+  // offsets of the segments' lists in the row's flattened extracted keys
   const uint32_t *cnt = m.seg_cnt + (int64_t)row * m.S;
-  // exclusive prefix of the segment counts (S <= kMaxSegs)
   uint32_t carry = 0;
-  for (int b = 0; b < S; b += kThreads) {
+  for (int b = 0; b < S; b += kSelThreads) {
     const uint32_t c = (b + tid < S) ? cnt[b + tid] : 0u;
     uint32_t tot;
-    const uint32_t ex = block_exclusive_scan(c, sh.wtot, &tot);
+    const uint32_t ex = nt_scan<kSelThreads>(c, sh.wt, &tot);
     if (b + tid < S) sh.seg_off[b + tid] = carry + ex;
     carry += tot;
   }
   if (tid == 0) sh.seg_off[S] = carry;
+  for (int b = tid; b < 2 * 1024; b += kSelThreads) {
+    (&sh.hlow[0][0])[b] = 0;
+    (&sh.hbef[0][0])[b] = 0;
+  }
   lds_sync();
   const uint32_t M = carry;
-  const uint2 *glist = m.list + (int64_t)row * m.S * kSeg;
-  const bool in_lds = M <= (uint32_t)kFinCap;
+  // chunk -> segment table (segment of flat index 16c)
+  const uint32_t n_chunks = min((M + 15) / 16, (uint32_t)kMaxChunks);
+  for (int s = tid; s < S; s += kSelThreads) {
+    const uint32_t c0 = (sh.seg_off[s] + 15) / 16, c1 = min((sh.seg_off[s + 1] + 15) / 16, n_chunks);
+    for (uint32_t c = c0; c < c1; ++c) sh.cseg[c] = (uint16_t)s;
+  }
+  // thresholds: top 12 bits, then the next 10
+  bool act[2];
+  uint32_t pre22[2] = {0, 0}, need[2] = {0, 0};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) act[j] = j < n_out && out[j].k < n;  // else every key is taken
   const uint32_t *g12 = m.hist + (int64_t)row * kBins;
-  for (int b = tid; b < kBins; b += kThreads) sh.hist12[b] = g12[b];
-  if (in_lds) {
-    // flat copy in batches of 16 independent loads per thread, all in flight
-    // at once (one round trip per batch instead of one per segment)
-    constexpr int CP = 16;
-    for (uint32_t base = 0; base < M; base += kThreads * CP) {
-      uint2 v[CP];
+  const uint32_t *g10 = m.h10 + (int64_t)row * 2 * 1024;
 #pragma unroll
-      for (int j = 0; j < CP; ++j) {
-        const uint32_t i = base + j * kThreads + tid;
+  for (int j = 0; j < 2; ++j) {
+    if (!act[j]) continue;
+    uint32_t above, c;
+    const uint32_t b12 = nt_find<kSelThreads>(g12, kBins, (uint32_t)out[j].k, sh.wt, sh.res, &above, &c);
+    const uint32_t nd = (uint32_t)out[j].k - above;
+    const uint32_t d10 = nt_find<kSelThreads>(g10 + j * 1024, 1024, nd, sh.wt, sh.res, &above, &c);
+    need[j] = nd - above;
+    pre22[j] = (b12 << 10) | d10;
+  }
+  lds_sync();  // cseg complete
+  // one pass over the row's extracted keys
+  const uint32_t *lkey = m.lkey + (int64_t)row * m.S * kSeg;
+  const uint32_t my0 = sh.seg_off[seg];
+  uint32_t gt_bef[2] = {0, 0};
+  if (act[0] || act[1]) {
+    for (uint32_t base = 0; base < M; base += kSelThreads * kSelBatch) {
+      uint32_t key[kSelBatch];
+#pragma unroll
+      for (int e = 0; e < kSelBatch; ++e) {
+        const uint32_t i = base + e * kSelThreads + tid;
+        key[e] = 0;
         if (i < M) {
-          int lo = 0;  // segment holding flat index i: fixed-step search (unrollable)
-#pragma unroll
-          for (int step = kMaxSegs / 2; step > 0; step >>= 1)
-            if (lo + step < S && sh.seg_off[lo + step] <= i) lo += step;
-          v[j] = glist[(int64_t)lo * kSeg + (i - sh.seg_off[lo])];
+          int s;
+          if ((i >> 4) < n_chunks) {
+            s = sh.cseg[i >> 4];
+          } else {  // beyond the table: binary search
+            int lo = 0, hi = S - 1;
+            while (lo < hi) {
+              const int mid = (lo + hi + 1) >> 1;
+              if (sh.seg_off[mid] <= i) lo = mid; else hi = mid - 1;
+            }
+            s = lo;
+          }
+          while (sh.seg_off[s + 1] <= i) ++s;
+          key[e] = lkey[(int64_t)s * kSeg + (i - sh.seg_off[s])];
         }
       }
 #pragma unroll
-      for (int j = 0; j < CP; ++j) {
-        const uint32_t i = base + j * kThreads + tid;
-        if (i < M) {
-          sh.lkey[i] = v[j].x;
-          sh.lpos[i] = (int32_t)v[j].y;
+      for (int e = 0; e < kSelBatch; ++e) {
+        const uint32_t i = base + e * kSelThreads + tid;
+        if (i >= M) continue;
+        const bool before = i < my0;
+        const uint32_t hi22 = key[e] >> 10;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (!act[j]) continue;
+          if (hi22 == pre22[j]) {
+            atomicAdd(&sh.hlow[j][key[e] & 1023u], 1u);
+            if (before) atomicAdd(&sh.hbef[j][key[e] & 1023u], 1u);
+          } else if (before && hi22 > pre22[j]) {
+            ++gt_bef[j];
+          }
         }
       }
     }
   }
   lds_sync();
-  auto get_lds = [&](uint32_t i) { return make_uint2(sh.lkey[i], (uint32_t)sh.lpos[i]); };
-  auto get_glb = [&](uint32_t i) {
-    int lo = 0, hi = S - 1;  // segment holding flat index i
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sh.seg_off[mid] <= i) lo = mid; else hi = mid - 1;
+  uint32_t theta[2] = {0, 0}, need_eq[2] = {0, 0}, sel_before[2] = {my0, my0},
+           eq_before[2] = {0, 0};
+  bool all_eq[2] = {true, true};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (!act[j]) continue;  // every key is taken: offset = extracted keys before
+    uint32_t gtb, above, c, gt_low = 0, t2;
+    (void)nt_scan<kSelThreads>(gt_bef[j], sh.wt, &gtb);
+    const uint32_t d = nt_find<kSelThreads>(sh.hlow[j], 1024, need[j], sh.wt, sh.res, &above, &c);
+    theta[j] = (pre22[j] << 10) | d;
+    need_eq[j] = need[j] - above;
+    all_eq[j] = need_eq[j] == c;
+    for (int b = tid; b < 1024; b += kSelThreads)
+      if ((uint32_t)b > d) gt_low += sh.hbef[j][b];
+    (void)nt_scan<kSelThreads>(gt_low, sh.wt, &t2);
+    eq_before[j] = sh.hbef[j][d];
+    sel_before[j] = gtb + t2 + min(eq_before[j], need_eq[j]);
+  }
+  // emit this segment's selected keys in ascending positions
+  constexpr int kOwn = kSeg / kSelThreads;  // own entries per thread
+  const uint32_t mc = sh.seg_off[seg + 1] - my0;
+  const int64_t own = ((int64_t)row * m.S + seg) * kSeg;
+  const uint32_t i0 = tid * kOwn;
+  uint32_t ek[kOwn];
+  int32_t ep[kOwn];
+#pragma unroll
+  for (int t = 0; t < kOwn; ++t) {
+    ek[t] = i0 + t < mc ? m.lkey[own + i0 + t] : 0u;
+    ep[t] = i0 + t < mc ? m.lpos[own + i0 + t] : 0;
+  }
+  uint32_t eqb[2] = {eq_before[0], eq_before[1]};
+  if ((act[0] && !all_eq[0]) || (act[1] && !all_eq[1])) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int t = 0; t < kOwn; ++t) {
+      const bool valid = i0 + t < mc;
+      c += (valid && act[0] && ek[t] == theta[0]) ? 1u : 0u;
+      c += (valid && act[1] && ek[t] == theta[1]) ? 0x10000u : 0u;
     }
-    return glist[(int64_t)lo * kSeg + (i - sh.seg_off[lo])];
-  };
-  for (int j = 0; j < n_out; ++j) {
-    const FinOut &o = j ? o1 : o0;
-    const int mm = min(o.k, n);
-    int32_t *oi = o.idx + (int64_t)row * o.k;
-    float *ov = o.val ? o.val + (int64_t)row * o.k : nullptr;
-    const bool take_all = o.k >= n;  // then every element was extracted
-    uint32_t theta = 0, need_eq = 0;
-    bool all_eq = true;
-    if (!take_all) {
-      // pass 1 from the whole row's histogram (exact for every k <= kmax)
-      for (int b = tid; b < kBins; b += kThreads) sh.hist[b] = sh.hist12[b];
-      lds_sync();
-      if (in_lds) theta = refine(sh, M, (uint32_t)o.k, get_lds, &need_eq, &all_eq, true);
-      else theta = refine(sh, M, (uint32_t)o.k, get_glb, &need_eq, &all_eq, true);
+    uint32_t tot;
+    const uint32_t ex = nt_scan<kSelThreads>(c, sh.wt, &tot);
+    eqb[0] += ex & 0xFFFFu;
+    eqb[1] += ex >> 16;
+  }
+  uint32_t selm[2] = {0, 0}, c_sel = 0;
+#pragma unroll
+  for (int t = 0; t < kOwn; ++t) {
+    const bool valid = i0 + t < mc;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (j >= n_out) continue;
+      const bool eq = valid && act[j] && ek[t] == theta[j];
+      const bool s = valid && (!act[j] || ek[t] > theta[j] ||
+                               (eq && (all_eq[j] || eqb[j] < need_eq[j])));
+      eqb[j] += eq ? 1u : 0u;
+      selm[j] |= s ? (1u << t) : 0u;
+      c_sel += s ? (j ? 0x10000u : 1u) : 0u;
     }
-    if (in_lds) emit(sh, M, theta, need_eq, all_eq, take_all, get_lds, idm, u, oi, ov, mm);
-    else emit(sh, M, theta, need_eq, all_eq, take_all, get_glb, idm, u, oi, ov, mm);
-    lds_sync();
+  }
+  uint32_t tot;
+  const uint32_t ex = nt_scan<kSelThreads>(c_sel, sh.wt, &tot);
+  uint32_t pos[2] = {sel_before[0] + (ex & 0xFFFFu), sel_before[1] + (ex >> 16)};
+#pragma unroll
+  for (int t = 0; t < kOwn; ++t) {
+    const int p = ep[t];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (j >= n_out || !((selm[j] >> t) & 1u)) continue;
+      const uint32_t mm = (uint32_t)min(out[j].k, n);
+      if (pos[j] < mm) {
+        out[j].idx[(int64_t)row * out[j].k + pos[j]] = idm ? idm[p] : p;
+        if (out[j].val) out[j].val[(int64_t)row * out[j].k + pos[j]] = u[p];
+      }
+      ++pos[j];
+    }
   }
 }
 
@@ -706,24 +841,17 @@ topk_lds_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
 }
 
 hipError_t launch_multi(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
-                        const int32_t *ids, int64_t ids_ld, int ids_rows, int max_len, FinOut o0, FinOut o1,
-                        int n_out, void *ws, hipStream_t st) {
+                        const int32_t *ids, int64_t ids_ld, int ids_rows, int max_len, FinOut o0,
+                        FinOut o1, int n_out, void *ws, hipStream_t st) {
   MultiWs m = carve(ws, n_rows, max_len);
-  const int kmax = n_out == 2 ? max(o0.k, o1.k) : o0.k;
-  const int nh = n_rows * kBins;
+  const int nh = n_rows * (kBins + 2 * 1024);  // hist and h10
   topk_clear_kernel<<<(nh + 255) / 256, 256, 0, st>>>(m.hist, nh);
   dim3 g(m.S, n_rows);
   topk_hist_kernel<<<g, kSegThreads, 0, st>>>(scores, ld, valid_len, m.hist);
-  topk_extract_kernel<<<g, kSegThreads, 0, st>>>(scores, ld, valid_len, kmax, m);
-  const size_t lds = sizeof(FinShared);
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)topk_finalize_kernel,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    attr_set = true;
-  }
-  topk_finalize_kernel<<<n_rows, kThreads, lds, st>>>(scores, ld, valid_len, ids, ids_ld, ids_rows, o0, o1,
-                                                      n_out, m);
+  topk_extract_kernel<<<g, kSegThreads, 0, st>>>(scores, ld, valid_len, o0.k,
+                                                 n_out == 2 ? o1.k : 0, m);
+  topk_select_kernel<<<g, kSelThreads, 0, st>>>(scores, ld, valid_len, ids, ids_ld, ids_rows, o0,
+                                                o1, n_out, m);
   return hipGetLastError();
 }
 
