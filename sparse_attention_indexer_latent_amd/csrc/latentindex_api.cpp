@@ -150,7 +150,10 @@ li_status li_score(const void *q_tilde, li_dtype qt_dt, const float *w, const fl
   if ((s = check_device()) != LI_OK) return s;
   li::CacheView cv = li::view_of(*cache);
   hipError_t e;
-  if (li::score_mfma_supported(qt_dt, H, cv))
+  if (li::score_prefill_supported(qt_dt, H, n_q, cv))
+    e = li::launch_score_prefill(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, scores, ld,
+                                 (hipStream_t)stream);
+  else if (li::score_mfma_supported(qt_dt, H, cv))
     e = li::launch_score_mfma(q_tilde, qt_dt, w, beta, n_q, H, q_seq, q_len, max_len, cv, nullptr,
                               0, 1, scores, ld, (hipStream_t)stream);
   else

@@ -59,6 +59,13 @@ hipError_t launch_score_mfma(const void *q_tilde, int qt_dt, const float *w, con
                              int max_len, const CacheView &cv, const int32_t *cand, int B,
                              int cand_rows, float *out, int64_t ld, hipStream_t st);
 
+// score_prefill.hip: matrix-core scorer for many bf16 queries per sequence
+// (a prefill chunk), page mode only.
+bool score_prefill_supported(int qt_dt, int H, int n_q, const CacheView &cv);
+hipError_t launch_score_prefill(const void *q_tilde, const float *w, const float *beta, int n_q,
+                                const int32_t *q_seq, const int32_t *q_len, int max_len,
+                                const CacheView &cv, float *out, int64_t ld, hipStream_t st);
+
 // topk.hip.  `ids` (may be null) maps a row position j to the id reported
 // for it (row i uses ids + (i % ids_rows)*ids_ld); positions are ordered by id exactly as
 // by j (ids ascending), so ties break by position.  valid_len may be null

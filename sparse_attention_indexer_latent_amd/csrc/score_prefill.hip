@@ -1,0 +1,230 @@
+// Matrix-core scorer for many queries over one shared cache (prefill chunk):
+// eq. (8) of the LatentIndex summary ("Methodology"),
+// u_{s,t} = sum_h w_{s,h} ReLU(q~_{s,h} . c_t + beta_{s,h}) for t < q_len[s],
+// with bf16 absorbed queries, H = 64, r = 256 and a bf16 cache.
+//
+// This is a dense contraction ([queries x 64 heads] x [256] x [tokens]) with a
+// ReLU and a head reduction in the epilogue, bound by the matrix cores
+// (2 * 64 * 256 flop per (query, token) pair against 512 B per token shared
+// by every query), so the design maximises reuse of each staged latent page:
+//  * A workgroup holds 8 queries (one per wavefront, all 64 heads of its
+//    query's q~ in registers: 4 head tiles x 8 k-steps of
+//    v_mfma_f32_16x16x32_bf16 operands) and one token range.
+//  * Pages (64 tokens, 32 KB) stream HBM/L2 -> LDS with direct-to-LDS loads
+//    (XOR-swizzled 16-byte chunks, NSTAGE stages); every wavefront reads each
+//    page once from LDS and computes 64 heads x 64 tokens (128 MFMAs).
+//  * beta enters as the accumulator's initial value; the epilogue (ReLU, x w,
+//    the 64-head sum: 16 heads per lane, then two cross-lane adds) stays in
+//    registers and each wavefront writes one 64-token row segment per page.
+//  * Token ranges are XCD-aware: workgroups are dealt round-robin over the 8
+//    XCDs, so workgroup g runs on XCD g % 8; range (g % 8) + 8 j is served by
+//    XCD g % 8 only, all of its query groups before range j + 1 starts, which
+//    keeps the pages a range streams in that XCD's own L2.
+//  * Queries of a workgroup that read different sequences are served in
+//    separate rounds (one per distinct sequence); a prefill chunk has one.
+#include <algorithm>
+
+#include "li_device.h"
+#include "li_internal.h"
+
+namespace li {
+namespace {
+
+#define LDS3 __attribute__((address_space(3)))
+#define INL __attribute__((always_inline))
+
+constexpr int kQ = 8;             // queries (wavefronts) per workgroup
+constexpr int kThr = kQ * kWave;  // 512
+constexpr int kRowB = 512;        // bf16 latent row bytes (r = 256)
+constexpr int kChunks = kRowB / 16;
+constexpr int kSwz = 15;
+constexpr int kMaxRangePages = 256;  // pages per token range
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int NSTAGE>
+struct PrefillShared {
+  __align__(16) char stage[NSTAGE][kPage * kRowB];
+  int32_t blk[kMaxRangePages];
+  int32_t qseq[kQ], qlen[kQ];
+  int32_t round_seq, round_len;
+};
+
+union Frag {
+  bf16x8 v;
+  uint32_t u[4];
+};
+
+template <int NSTAGE>
+__global__ void __launch_bounds__(kThr, 1)
+score_prefill_kernel(const uint16_t *__restrict__ q_tilde, const float *__restrict__ w,
+                     const float *__restrict__ beta, int n_q, const int32_t *__restrict__ q_seq,
+                     const int32_t *__restrict__ q_len, int max_len, CacheView cv, float *__restrict__ out,
+                     int64_t ld, int n_groups, int range_pages) {
+  constexpr int kInstPerWave = (kPage * kRowB / 1024) / kQ;  // 1 KB per wave-instruction: 4
+  __shared__ PrefillShared<NSTAGE> sh;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, g4 = lane >> 4;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int rng = xcd + 8 * (slot / n_groups), qg = slot % n_groups;
+  const int q = qg * kQ + wave;  // this wavefront's query
+  const bool has_q = q < n_q;
+
+  // operands of the wavefront's query: A[rt][kb] = q~[q][16 rt + lane%16][kb*32 + g4*8 .. +8]
+  Frag A[4][8];
+  float wv[4][4], bv[4][4];
+  {
+    const int qq = has_q ? q : 0;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const uint16_t *src = q_tilde + ((int64_t)qq * 64 + 16 * rt + (lane & 15)) * 256 + g4 * 8;
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const uint4 x = *(const uint4 *)(src + kb * 32);
+        A[rt][kb].u[0] = x.x;
+        A[rt][kb].u[1] = x.y;
+        A[rt][kb].u[2] = x.z;
+        A[rt][kb].u[3] = x.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 16 * rt + 4 * g4 + i;
+        wv[rt][i] = w[(int64_t)qq * 64 + h];
+        bv[rt][i] = beta ? beta[(int64_t)qq * 64 + h] : 0.f;
+      }
+    }
+  }
+  if (tid < kQ) {
+    const int qi = qg * kQ + tid;
+    const int sq = qi < n_q ? q_seq[qi] : -1;
+    const bool ok = sq >= 0 && sq < cv.n_seq;  // others are skipped
+    sh.qseq[tid] = ok ? sq : -1;
+    sh.qlen[tid] = ok ? min(q_len[qi], max_len) : 0;
+  }
+  bar();
+  const int myseq = sh.qseq[wave];
+  const int mylen = has_q ? sh.qlen[wave] : 0;
+  float *orow = out + (int64_t)(has_q ? q : 0) * ld;
+  uint32_t done = 0;  // bit w: query of wavefront w served
+  for (int w2 = 0; w2 < kQ; ++w2)
+    if (sh.qseq[w2] < 0) done |= 1u << w2;
+
+  const char *gdata = (const char *)cv.data;
+  while (true) {
+    // next round: the first unserved query's sequence, and the longest
+    // length among the queries on it
+    if (tid == 0) {
+      int s = -1, L = 0;
+      for (int w2 = 0; w2 < kQ; ++w2)
+        if (!((done >> w2) & 1u) && s < 0) s = sh.qseq[w2];
+      for (int w2 = 0; w2 < kQ; ++w2)
+        if (!((done >> w2) & 1u) && sh.qseq[w2] == s) L = max(L, sh.qlen[w2]);
+      sh.round_seq = s;
+      sh.round_len = L;
+    }
+    bar();
+    const int s = sh.round_seq, L = sh.round_len;
+    if (s < 0) break;
+    const bool active = has_q && myseq == s;
+    for (int w2 = 0; w2 < kQ; ++w2)
+      if (sh.qseq[w2] == s) done |= 1u << w2;
+    // this range's pages of sequence s that some query of the round needs
+    const int pg0 = rng * range_pages;
+    const int npg =
+        max(0, min(min(range_pages, cv.max_blocks - pg0), (L + kPage - 1) / kPage - pg0));
+    for (int p = tid; p < npg; p += kThr) {
+      const int b = cv.block_table[(int64_t)s * cv.max_blocks + pg0 + p];
+      sh.blk[p] = (b >= 0 && b < cv.n_blocks) ? b : 0;
+    }
+    bar();
+    auto issue = [&](int p, int st) INL {
+      LDS3 char *dst = (LDS3 char *)sh.stage[st];
+      const char *base = gdata + (int64_t)sh.blk[p] * kPage * kRowB;
+#pragma unroll
+      for (int m = 0; m < kInstPerWave; ++m) {
+        const int gi = wave * kInstPerWave + m;
+        const int row = gi * 2 + lane / kChunks;  // 2 rows per 1 KB instruction
+        const int chunk = (lane % kChunks) ^ (row & kSwz);
+        __builtin_amdgcn_global_load_lds((const void *)(base + row * kRowB + chunk * 16),
+                                         (LDS3 void *)(dst + gi * 1024), 16, 0, 0);
+      }
+    };
+    for (int p = 0; p < NSTAGE - 1; ++p)
+      if (p < npg) issue(p, p);
+    for (int p = 0; p < npg; ++p) {
+      const int after = min(NSTAGE - 2, npg - 1 - p);
+      if (after >= 2) wait_vm<2 * kInstPerWave>();
+      else if (after == 1) wait_vm<kInstPerWave>();
+      else wait_vm<0>();
+      bar();
+      if (p + NSTAGE - 1 < npg) issue(p + NSTAGE - 1, (p + NSTAGE - 1) % NSTAGE);
+      const int t_page = (pg0 + p) * kPage;
+      if (active && t_page < mylen) {
+        const char *sp = sh.stage[p % NSTAGE];
+        float outv = 0.f;
+#pragma unroll 1
+        for (int tt = 0; tt < 4; ++tt) {
+          const int row = tt * 16 + (lane & 15);
+          const char *rp = sp + row * kRowB;
+          bf16x8 b[8];
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) {
+            const int chunk = kb * 4 + g4;
+            b[kb] = *(const bf16x8 *)(rp + ((chunk ^ (row & kSwz)) * 16));
+          }
+          f32x4 acc[4];
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{bv[rt][0], bv[rt][1], bv[rt][2], bv[rt][3]};
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+              acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rt][kb].v, b[kb], acc[rt], 0, 0, 0);
+          float v = 0.f;
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v = fmaf(wv[rt][i], fmaxf(acc[rt][i], 0.f), v);
+          v += __shfl_xor(v, 16, kWave);
+          v += __shfl_xor(v, 32, kWave);
+          if (g4 == tt) outv = v;
+        }
+        const int t = t_page + lane;
+        if (t < mylen) orow[t] = outv;
+      }
+    }
+    bar();  // all reads of the stages done before the next round reuses them
+  }
+}
+
+}  // namespace
+
+bool score_prefill_supported(int qt_dt, int H, int n_q, const CacheView &cv) {
+  // worth it when queries share sequences: at least kQ per sequence on average
+  return qt_dt == LI_BF16 && H == 64 && cv.r == 256 && cv.dtype == LI_BF16 && n_q >= 64 &&
+         n_q >= kQ * cv.n_seq;
+}
+
+hipError_t launch_score_prefill(const void *q_tilde, const float *w, const float *beta, int n_q,
+                                const int32_t *q_seq, const int32_t *q_len, int max_len,
+                                const CacheView &cv, float *out, int64_t ld, hipStream_t st) {
+  // token ranges in multiples of 8 (one per XCD), at most kMaxRangePages
+  // pages each (the page table a workgroup keeps in LDS)
+  const int pages = (max_len + kPage - 1) / kPage;
+  int n_ranges = 8;
+  while ((pages + n_ranges - 1) / n_ranges > kMaxRangePages) n_ranges += 8;
+  const int range_pages = (pages + n_ranges - 1) / n_ranges;
+  const int n_groups = (n_q + kQ - 1) / kQ;
+  const int64_t grid = (int64_t)n_groups * n_ranges;
+  if (pages <= 0 || n_groups <= 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  score_prefill_kernel<4><<<(unsigned)grid, kThr, 0, st>>>(
+      (const uint16_t *)q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, out, ld, n_groups,
+      range_pages);
+  return hipGetLastError();
+}
+
+}  // namespace li
