@@ -14,6 +14,11 @@ Printed: one JSON line with the throughput in scored tokens per second
 dominant kernel's roofline fraction (the anchor's latent scan, timed with HIP
 events on its stream), the same workload's full-scan step for the HS speedup,
 and the CPU oracle timed on a bounded sample of the same step.
+
+A second leg measures the prefill chunk on the matrix cores: 2,048 causal
+query positions (62K-64K) against a 64K-token bf16 latent, four layers of
+li_score (bf16 absorbed queries, H = 64, r = 256) each followed by li_topk
+(k = 2048 per row), reported as MFMA utilisation against the bf16 dense peak.
 """
 
 from __future__ import annotations
@@ -27,6 +32,7 @@ import time
 import numpy as np
 
 HBM_PEAK = 8.0e12  # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15  # flop/s, MI355X dense bf16 matrix cores
 
 
 def parse():
@@ -43,6 +49,10 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --profile-steps: also run a plain device copy of this many MiB "
                          "three times (calibrates hardware byte counters)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk leg")
+    ap.add_argument("--prefill-iters", type=int, default=10)
+    ap.add_argument("--path", choices=["hs", "prefill"], default="hs",
+                    help="with --profile-steps: which path to run")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host instead of replaying HIP graphs")
     return ap.parse_args()
@@ -126,6 +136,67 @@ def cpu_baseline(wl, seconds: float):
                       f"{cores} cores, BLAS threads {blas_threads}"}
 
 
+def prefill_setup(torch, W, DeviceWorkload):
+    """Device operands of the prefill chunk: the 64K-token latent, every
+    layer's bf16 absorbed queries and head weights, score and index buffers."""
+    wl = W.config(4)
+    dw = DeviceWorkload(wl, hold_last=False)
+    qts, ws = [], []
+    for layer in range(wl.G):
+        bits, w = wl.prefill_queries(layer)
+        qts.append(torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16))
+        ws.append(torch.from_numpy(w).cuda())
+    L = int(wl.lens[0])
+    u = torch.empty((wl.n_q, L), dtype=torch.float32, device="cuda")
+    idx = torch.empty((wl.G, wl.n_q, wl.k), dtype=torch.int32, device="cuda")
+    return wl, dw, qts, ws, u, idx
+
+
+def prefill_chunk(ops, wl, dw, qts, ws, u, idx, ev=None):
+    """One prefill chunk: per layer, score every causal (query, token) pair,
+    then select each row's top-k.  ev (optional): per layer, a pair of events
+    bracketing li_score."""
+    L = int(wl.lens[0])
+    for layer in range(wl.G):
+        if ev is not None:
+            ev[layer][0].record()
+        ops.score(qts[layer], ws[layer], None, dw.q_seq, dw.q_len, L, dw.cache, scores=u)
+        if ev is not None:
+            ev[layer][1].record()
+        ops.topk(u, dw.q_len, L, wl.k, out_idx=idx[layer])
+
+
+def prefill_leg(torch, ops, W, DeviceWorkload, iters: int) -> dict:
+    wl, dw, qts, ws, u, idx = prefill_setup(torch, W, DeviceWorkload)
+    for _ in range(2):
+        prefill_chunk(ops, wl, dw, qts, ws, u, idx)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(wl.G)] for _ in range(iters)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(iters):
+        prefill_chunk(ops, wl, dw, qts, ws, u, idx, ev[i])
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / iters
+    score_s = float(np.mean([a.elapsed_time(b) for it in ev for a, b in it])) * 1e-3
+    pairs = int(wl.q_len.astype(np.int64).sum())       # valid (query, token) pairs per layer
+    flop = 2 * wl.H * wl.r * pairs                        # one MAC per head and latent dim
+    return {"workload": f"{wl.name}: {wl.G} layers x (li_score of {wl.n_q} causal bf16 queries "
+                        f"(positions {int(wl.q_len[0]) - 1}..{int(wl.q_len[-1]) - 1}) over "
+                        f"{int(wl.lens[0])} bf16 latents, H={wl.H}, r={wl.r}; li_topk k={wl.k} "
+                        f"per row)",
+            "ms_per_chunk": el * 1e3,
+            "score_ms_per_layer": score_s * 1e3,
+            "topk_ms_per_layer": (el - wl.G * score_s) / wl.G * 1e3,
+            "valid_pairs_per_layer": pairs,
+            "flop_per_layer": flop,
+            "roofline": {"bound": "mfma", "kernel": "score_prefill_kernel",
+                         "achieved": flop / score_s / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
+                         "unit": "TFLOP/s", "frac": flop / score_s / MFMA_BF16_PEAK,
+                         "avg_kernel_us": score_s * 1e6},
+            "tokens_scored_per_s": wl.G * pairs / el}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -143,6 +214,12 @@ def main():
     torch.cuda.set_device(0)
     if ops.lib().li_check_device() != ops.LI_OK:
         raise SystemExit(ops.lib().li_last_error().decode())
+    if args.profile_steps and args.path == "prefill":
+        pf = prefill_setup(torch, W, DeviceWorkload)
+        for _ in range(args.warmup + args.profile_steps):
+            prefill_chunk(ops, *pf)
+        torch.cuda.synchronize()
+        return
     wl = W.config(args.config)
     hs = wl.B is not None
     dw = DeviceWorkload(wl, hold_last=True)
@@ -249,6 +326,9 @@ def main():
             cold.append(a.elapsed_time(b))
         out["cold_mall_us_per_group_step"] = float(np.median(cold)) * 1e3
         del flush
+
+    if not args.no_prefill:
+        out["prefill"] = prefill_leg(torch, ops, W, DeviceWorkload, args.prefill_iters)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -10,9 +10,14 @@
 //  * A workgroup holds 8 queries (one per wavefront, all 64 heads of its
 //    query's q~ in registers: 4 head tiles x 8 k-steps of
 //    v_mfma_f32_16x16x32_bf16 operands) and one token range.
-//  * Pages (64 tokens, 32 KB) stream HBM/L2 -> LDS with direct-to-LDS loads
-//    (XOR-swizzled 16-byte chunks, NSTAGE stages); every wavefront reads each
-//    page once from LDS and computes 64 heads x 64 tokens (128 MFMAs).
+//  * Pages (64 tokens, 32 KB) stream HBM/L2 -> LDS with direct-to-LDS buffer
+//    loads (NSTAGE stages), stored k-block-major: [8 k-blocks of 32 latent
+//    dims][64 tokens][64 B], the four 16-byte chunks of token n XOR-swizzled
+//    by f(n) = (n1 ^ n3) | n2 << 1 (n_i: bit i of n), so that the 8 lanes of
+//    any aligned group reading one chunk of 8 tokens cover 128 distinct bytes
+//    modulo 128, and the 16 lanes of a quarter-wave 256 distinct bytes modulo
+//    256.  Every operand address is then one register plus an immediate.  Each wavefront reads every page once from LDS and
+//    computes 64 heads x 64 tokens (128 MFMAs).
 //  * beta enters as the accumulator's initial value; the epilogue (ReLU, x w,
 //    the 64-head sum: 16 heads per lane, then two cross-lane adds) stays in
 //    registers and each wavefront writes one 64-token row segment per page.
@@ -36,14 +41,17 @@ namespace {
 constexpr int kQ = 8;             // queries (wavefronts) per workgroup
 constexpr int kThr = kQ * kWave;  // 512
 constexpr int kRowB = 512;        // bf16 latent row bytes (r = 256)
-constexpr int kChunks = kRowB / 16;
-constexpr int kSwz = 15;
+constexpr int kKb = 8;             // k-blocks of 32 dims (64 B) per token
 constexpr int kMaxRangePages = 256;  // pages per token range
+
+static_assert(kKb == kQ, "wavefront w stages k-block w of every page");
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// chunk swizzle of token n (only bits 1-3 of n matter)
+__device__ __forceinline__ int swz(int n) { return (((n >> 1) ^ (n >> 3)) & 1) | (n & 4) >> 1; }
 __device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int NSTAGE>
@@ -140,17 +148,53 @@ score_prefill_kernel(const uint16_t *__restrict__ q_tilde, const float *__restri
       sh.blk[p] = (b >= 0 && b < cv.n_blocks) ? b : 0;
     }
     bar();
+    // wavefront w stages k-block w of a page: 4 loads of 16 tokens x 64 B;
+    // lane -> token m*16 + lane/4, LDS slot lane%4 holding chunk
+    // (lane%4) ^ f(lane/4)
+    const int voff = (lane >> 2) * kRowB + wave * 64 + (((lane & 3) ^ swz(lane >> 2)) << 4);
     auto issue = [&](int p, int st) INL {
-      LDS3 char *dst = (LDS3 char *)sh.stage[st];
-      const char *base = gdata + (int64_t)sh.blk[p] * kPage * kRowB;
+      LDS3 char *dst = (LDS3 char *)sh.stage[st] + wave * (kPage * 64);
+      const int blk = __builtin_amdgcn_readfirstlane(sh.blk[p]);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(gdata + (int64_t)blk * kPage * kRowB), 0, kPage * kRowB, 0x00020000);
 #pragma unroll
-      for (int m = 0; m < kInstPerWave; ++m) {
-        const int gi = wave * kInstPerWave + m;
-        const int row = gi * 2 + lane / kChunks;  // 2 rows per 1 KB instruction
-        const int chunk = (lane % kChunks) ^ (row & kSwz);
-        __builtin_amdgcn_global_load_lds((const void *)(base + row * kRowB + chunk * 16),
-                                         (LDS3 void *)(dst + gi * 1024), 16, 0, 0);
-      }
+      for (int m = 0; m < kInstPerWave; ++m)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS3 void *)(dst + m * 1024), 16, voff,
+                                                 m * 16 * kRowB, 0, 0);
+    };
+    // operand read of lane (g4, n): token tt*16 + n, k-block kb, chunk g4
+    const int roff = (lane & 15) * 64 + ((g4 ^ swz(lane & 15)) << 4);
+    // Software pipeline: the epilogue of tile tt runs between the MFMAs of
+    // tile tt+1, whose operands are read one k-block behind the MFMAs of tile
+    // tt; a page's last tile is finished after the next page's barrier,
+    // while that page's first operands are in flight.
+    f32x4 accP[4];   // pending tile (epilogue not yet applied)
+    float part[4];   // this lane's 16-head partial sum for each 16-token tile
+    int pend_t = -1; // first token of the page whose last tile is pending
+    auto relu_w = [&](const f32x4 (&acc)[4], int e, float v) INL {
+      // ReLU as an integer max on the bit pattern (negative floats, -0.0
+      // included, are negative integers), weighted by the head's w
+      const float r = __int_as_float(max(__float_as_int(acc[e >> 2][e & 3]), 0));
+      return fmaf(wv[e >> 2][e & 3], r, v);
+    };
+    auto flush = [&]() INL {
+      float v = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v = relu_w(accP, e, v);
+      part[3] = v;
+      // reduce-scatter over the four 16-lane groups: tile j's head sum lands
+      // in lane group j (token pend_t + lane)
+      const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
+                                                        __float_as_uint(part[2]), false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]),
+                                                        __float_as_uint(part[3]), false, false);
+      const float q02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+      const float q13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+      const auto s4 = __builtin_amdgcn_permlane16_swap(__float_as_uint(q02), __float_as_uint(q13),
+                                                       false, false);
+      const float outv = __uint_as_float(s4[0]) + __uint_as_float(s4[1]);
+      const int t = pend_t + lane;
+      if (t < mylen) orow[t] = outv;
     };
     for (int p = 0; p < NSTAGE - 1; ++p)
       if (p < npg) issue(p, p);
@@ -162,40 +206,44 @@ score_prefill_kernel(const uint16_t *__restrict__ q_tilde, const float *__restri
       bar();
       if (p + NSTAGE - 1 < npg) issue(p + NSTAGE - 1, (p + NSTAGE - 1) % NSTAGE);
       const int t_page = (pg0 + p) * kPage;
-      if (active && t_page < mylen) {
-        const char *sp = sh.stage[p % NSTAGE];
-        float outv = 0.f;
-#pragma unroll 1
-        for (int tt = 0; tt < 4; ++tt) {
-          const int row = tt * 16 + (lane & 15);
-          const char *rp = sp + row * kRowB;
-          bf16x8 b[8];
+      const bool act = active && t_page < mylen;
+      const char *sp = sh.stage[p % NSTAGE] + roff;
+      bf16x8 b[kKb];
+      if (act) {
 #pragma unroll
-          for (int kb = 0; kb < 8; ++kb) {
-            const int chunk = kb * 4 + g4;
-            b[kb] = *(const bf16x8 *)(rp + ((chunk ^ (row & kSwz)) * 16));
-          }
+        for (int kb = 0; kb < kKb; ++kb) b[kb] = *(const bf16x8 *)(sp + kb * (kPage * 64));
+      }
+      if (pend_t >= 0) {
+        flush();
+        pend_t = -1;
+      }
+      if (act) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
           f32x4 acc[4];
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{bv[rt][0], bv[rt][1], bv[rt][2], bv[rt][3]};
+          float v = 0.f;
 #pragma unroll
-          for (int kb = 0; kb < 8; ++kb)
+          for (int kb = 0; kb < kKb; ++kb) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
               acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rt][kb].v, b[kb], acc[rt], 0, 0, 0);
-          float v = 0.f;
+            if (tt < 3)
+              b[kb] = *(const bf16x8 *)(sp + kb * (kPage * 64) + (tt + 1) * 16 * 64);
+            if (tt > 0) {
+              v = relu_w(accP, 2 * kb, v);
+              v = relu_w(accP, 2 * kb + 1, v);
+            }
+          }
+          if (tt > 0) part[tt - 1] = v;
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v = fmaf(wv[rt][i], fmaxf(acc[rt][i], 0.f), v);
-          v += __shfl_xor(v, 16, kWave);
-          v += __shfl_xor(v, 32, kWave);
-          if (g4 == tt) outv = v;
+          for (int rt = 0; rt < 4; ++rt) accP[rt] = acc[rt];
         }
-        const int t = t_page + lane;
-        if (t < mylen) orow[t] = outv;
+        pend_t = t_page;
       }
     }
+    if (pend_t >= 0) flush();
     bar();  // all reads of the stages done before the next round reuses them
   }
 }

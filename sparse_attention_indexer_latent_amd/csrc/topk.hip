@@ -840,6 +840,243 @@ topk_lds_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
   emit(sh, (uint32_t)n, theta, need_eq, all_eq, false, get, idm, u, oi, ov, m);
 }
 
+// ---------------------------------------------------------------------------
+// Many rows of up to 64K scores (a prefill chunk: one row per query): one
+// workgroup of 1024 threads per row holds the whole row's keys in registers
+// (64 per thread), so the row is read from memory once.  Thread t holds
+// positions it*4096 + 4t + j (it < NIT, j < 4): 16-byte coalesced loads, and
+// every thread's positions ascend with (it, j).
+//   A. histogram of key bits 31..21, the bin of the k-th largest key.  Score
+//      rows crowd into few bins, so the histogram has 8 interleaved copies
+//      (lane % 8 picks one): lanes of one atomic that hit the same bin mostly
+//      hit different words;
+//   the keys at or above that bin (the selection plus the bin's rest) are
+//      gathered with their positions into an LDS list;
+//   B. among keys in that bin, histogram of bits 20..10;
+//   C. among keys matching both, histogram of bits 9..0: theta and how many
+//      keys equal to theta are taken (lowest positions first);
+//   D. two bitmaps over positions (key > theta, key == theta), then one
+//      ordered pass over them: thread t owns positions 64t..64t+63, block
+//      scans give the equal keys taken before it and its output offset.
+//   B-D read the LDS list, or the row again from memory when more keys than
+//   the list holds reach bin b1 (heavy ties).
+// ---------------------------------------------------------------------------
+constexpr int kRegMax = 65536;
+constexpr int kRegBins = 2048;
+constexpr int kRegCopies = 8;
+constexpr int kRegCand = 6144;  // gathered (key, position) pairs, in pass A's space
+static_assert(kRegBins + 1024 + 2 * (kRegCand + kWave) <= kRegBins * kRegCopies,
+              "candidate list fits");
+
+struct RegShared {
+  uint32_t hA[kRegBins * kRegCopies];  // pass A copies [bin][copy]; then B (2048) and C (1024)
+  uint32_t hM[kRegBins];               // pass A merged
+  uint32_t gt[kRegMax / 32];
+  uint32_t eq[kRegMax / 32];
+  uint32_t wtot[kWaves];
+  uint32_t sel_bin, sel_above, sel_count;
+};
+
+// Bin holding the need-th largest key of an nb-bin histogram h (nb a
+// multiple of kThreads): sum_{b' > b} h[b'] < need <= sum_{b' >= b} h[b'].
+__device__ void reg_find(RegShared &sh, const uint32_t *h, int nb, uint32_t need) {
+  const int per = nb / kThreads;
+  const int top = nb - 1 - threadIdx.x * per;
+  uint32_t s = 0;
+  for (int e = 0; e < per; ++e) s += h[top - e];
+  uint32_t total;
+  uint32_t run = block_exclusive_scan(s, sh.wtot, &total);
+  for (int e = 0; e < per; ++e) {
+    const uint32_t c = h[top - e];
+    if (run < need && need <= run + c) {
+      sh.sel_bin = top - e;
+      sh.sel_above = run;
+      sh.sel_count = c;
+    }
+    run += c;
+  }
+  lds_sync();
+}
+
+template <int NIT>
+__global__ void __launch_bounds__(kThreads)
+topk_reg_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ valid_len,
+                const int32_t *__restrict__ ids, int64_t ids_ld, int ids_rows, int k,
+                int32_t *__restrict__ out_idx, float *__restrict__ out_val) {
+  __shared__ RegShared sh;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int n = min(valid_len[row], NIT * 4 * kThreads);
+  const float *u = scores + (int64_t)row * ld;
+  const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
+  int32_t *oi = out_idx + (int64_t)row * k;
+  float *ov = out_val ? out_val + (int64_t)row * k : nullptr;
+  const int m = min(k, n);
+  for (int j = m + tid; j < k; j += kThreads) {
+    oi[j] = -1;
+    if (ov) ov[j] = -INFINITY;
+  }
+  if (n <= k) {
+    for (int p = tid; p < n; p += kThreads) {
+      oi[p] = idm ? idm[p] : p;
+      if (ov) ov[p] = u[p];
+    }
+    return;
+  }
+  for (int b = tid; b < kRegCopies * kRegBins; b += kThreads) sh.hA[b] = 0;
+  // this thread's valid elements form a prefix of its (it, j) order
+  int nv = 0;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) nv += min(4, max(0, n - 4 * tid - it * 4096));
+  // Buffer loads bounded by the row's valid length never read past the row.
+  // Positions >= n get key 0: they land in bin 0 of pass A, whose count is
+  // corrected below; a selection that reaches bin 0 takes the re-reading
+  // path.
+  uint32_t key[NIT * 4];
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(u), 0, n * 4, 0x00020000);
+  if ((reinterpret_cast<uintptr_t>(u) & 15) == 0) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, (it * 4096 + 4 * tid) * 4, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) key[it * 4 + j] = score_key(__uint_as_float(x[j]));
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        key[it * 4 + j] = score_key(__uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rs, (it * 4096 + 4 * tid + j) * 4, 0, 0)));
+  }
+#pragma unroll
+  for (int e = 0; e < NIT * 4; ++e) key[e] = e < nv ? key[e] : 0u;
+  lds_sync();  // histogram cleared
+  // A (consumes keys as their loads land)
+  {
+    uint32_t *h = sh.hA + (lane & (kRegCopies - 1));
+#pragma unroll
+    for (int e = 0; e < NIT * 4; ++e) atomicAdd(&h[(key[e] >> 21) * kRegCopies], 1u);
+  }
+  lds_sync();
+  for (int b = tid; b < kRegBins; b += kThreads) {
+    const uint4 *c = reinterpret_cast<const uint4 *>(sh.hA + b * kRegCopies);
+    const uint4 x = c[0], y = c[1];
+    sh.hM[b] = x.x + x.y + x.z + x.w + y.x + y.y + y.z + y.w -
+               (b == 0 ? (uint32_t)(NIT * 4 * kThreads - n) : 0u);
+  }
+  lds_sync();
+  uint32_t *hB = sh.hA, *hC = sh.hA + kRegBins;
+  for (int b = tid; b < kRegBins + 1024; b += kThreads) sh.hA[b] = 0;
+  reg_find(sh, sh.hM, kRegBins, (uint32_t)k);
+  const uint32_t b1 = sh.sel_bin;
+  uint32_t need = (uint32_t)k - sh.sel_above;
+  // Gather every key at or above bin b1 (the selection plus bin b1's rest)
+  // with its position into an LDS list: per-thread counts, one block scan
+  // for the offsets, then branch-free writes (lanes with nothing to write
+  // hit a slot of their own past the list).
+  uint32_t *ckey = sh.hA + kRegBins + 1024, *cpos = ckey + kRegCand + kWave;
+  const uint32_t lo = b1 << 21;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int e = 0; e < NIT * 4; ++e) cnt += key[e] >= lo ? 1u : 0u;
+  uint32_t n_cand;
+  uint32_t slot = block_exclusive_scan(cnt, sh.wtot, &n_cand);
+  const bool listed = b1 > 0 && n_cand <= (uint32_t)kRegCand;  // else B-D re-read the row
+  if (listed) {
+#pragma unroll
+    for (int e = 0; e < NIT * 4; ++e) {
+      const bool pr = key[e] >= lo;
+      const uint32_t at = pr ? slot : (uint32_t)(kRegCand + lane);
+      ckey[at] = key[e];
+      cpos[at] = (e >> 2) * 4096 + 4 * tid + (e & 3);
+      slot += pr ? 1u : 0u;
+    }
+  }
+  lds_sync();
+  // B
+  if (listed) {
+    for (uint32_t c = tid; c < n_cand; c += kThreads)
+      if ((ckey[c] >> 21) == b1) atomicAdd(&hB[(ckey[c] >> 10) & 2047u], 1u);
+  } else {
+    for (int p = tid; p < n; p += kThreads) {
+      const uint32_t kp = score_key(u[p]);
+      if ((kp >> 21) == b1) atomicAdd(&hB[(kp >> 10) & 2047u], 1u);
+    }
+  }
+  lds_sync();
+  reg_find(sh, hB, kRegBins, need);
+  const uint32_t p22 = (b1 << 11) | sh.sel_bin;
+  need -= sh.sel_above;
+  // C
+  if (listed) {
+    for (uint32_t c = tid; c < n_cand; c += kThreads)
+      if ((ckey[c] >> 10) == p22) atomicAdd(&hC[ckey[c] & 1023u], 1u);
+  } else {
+    for (int p = tid; p < n; p += kThreads) {
+      const uint32_t kp = score_key(u[p]);
+      if ((kp >> 10) == p22) atomicAdd(&hC[kp & 1023u], 1u);
+    }
+  }
+  lds_sync();
+  reg_find(sh, hC, 1024, need);
+  const uint32_t theta = (p22 << 10) | sh.sel_bin;
+  need -= sh.sel_above;  // keys equal to theta to take, 1 <= need <= n_eq
+  const bool take_all_eq = need == sh.sel_count;
+  // D: bitmaps of the positions with key > theta and key == theta
+  if (listed) {
+    for (int wd = tid; wd < kRegMax / 32; wd += kThreads) sh.gt[wd] = sh.eq[wd] = 0;
+    lds_sync();
+    for (uint32_t c = tid; c < n_cand; c += kThreads) {
+      const uint32_t kc = ckey[c], pc = cpos[c];
+      if (kc > theta) atomicOr(&sh.gt[pc >> 5], 1u << (pc & 31));
+      else if (kc == theta) atomicOr(&sh.eq[pc >> 5], 1u << (pc & 31));
+    }
+  } else {
+    // thread t builds the words of positions 64t..64t+63 from the row itself
+    for (int h = 0; h < 2; ++h) {
+      uint32_t g = 0, q = 0;
+      for (int b = 0; b < 32; ++b) {
+        const int p = 64 * tid + 32 * h + b;
+        if (p < n) {
+          const uint32_t kp = score_key(u[p]);
+          g |= (kp > theta ? 1u : 0u) << b;
+          q |= (kp == theta ? 1u : 0u) << b;
+        }
+      }
+      sh.gt[2 * tid + h] = g;
+      sh.eq[2 * tid + h] = q;
+    }
+  }
+  lds_sync();
+  uint64_t sel = (uint64_t)sh.gt[2 * tid] | (uint64_t)sh.gt[2 * tid + 1] << 32;
+  uint64_t eqm = (uint64_t)sh.eq[2 * tid] | (uint64_t)sh.eq[2 * tid + 1] << 32;
+  if (take_all_eq) {
+    sel |= eqm;
+  } else {
+    uint32_t tot;
+    const uint32_t before = block_exclusive_scan((uint32_t)__popcll(eqm), sh.wtot, &tot);
+    const uint32_t take = need > before ? need - before : 0u;  // lowest `take` equal keys
+    for (uint32_t c = 0; c < take && eqm; ++c) {
+      const uint64_t low = eqm & (~eqm + 1);
+      sel |= low;
+      eqm ^= low;
+    }
+  }
+  uint32_t tot;
+  uint32_t pos = block_exclusive_scan((uint32_t)__popcll(sel), sh.wtot, &tot);
+  while (sel) {
+    const int b = __builtin_ctzll(sel);
+    sel &= sel - 1;
+    const int p = 64 * tid + b;
+    if (pos < (uint32_t)m) {
+      oi[pos] = idm ? idm[p] : p;
+      if (ov) ov[pos] = u[p];
+    }
+    ++pos;
+  }
+}
+
 hipError_t launch_multi(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
                         const int32_t *ids, int64_t ids_ld, int ids_rows, int max_len, FinOut o0,
                         FinOut o1, int n_out, void *ws, hipStream_t st) {
@@ -879,6 +1116,15 @@ hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_
   if (use_multi(n_rows, max_len))
     return launch_multi(scores, ld, n_rows, valid_len, ids, ids_ld, ids_rows, max_len,
                         FinOut{k, out_idx, out_val}, FinOut{0, nullptr, nullptr}, 1, ws, st);
+  if (max_len <= kRegMax) {
+    if (max_len <= kRegMax / 2)
+      topk_reg_kernel<8><<<n_rows, kThreads, 0, st>>>(scores, ld, valid_len, ids, ids_ld, ids_rows,
+                                                      k, out_idx, out_val);
+    else
+      topk_reg_kernel<16><<<n_rows, kThreads, 0, st>>>(scores, ld, valid_len, ids, ids_ld, ids_rows,
+                                                       k, out_idx, out_val);
+    return hipGetLastError();
+  }
   const size_t lds = sizeof(TopkShared);
   static bool attr_set = false;
   if (!attr_set) {

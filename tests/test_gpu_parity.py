@@ -339,6 +339,51 @@ def test_topk_exact_ties_and_signed_zero():
         _check_topk_exact(u, [n] * len(rows), k)
 
 
+def _check_topk_exact_sample(u, lens, k, rows):
+    """As _check_topk_exact, with every row selected on the GPU and the
+    listed rows compared."""
+    idx, val = _topk_gpu(u, lens, k)
+    for i in rows:
+        n = int(lens[i])
+        ref = O.pad(O.topk(u[i, :n].astype(np.float64), k), k)
+        assert np.array_equal(idx[i], ref), f"row {i}: n={n} k={k}"
+        m = min(k, n)
+        assert np.array_equal(val[i, :m].view(np.uint32), u[i, ref[:m]].astype(np.float32).view(np.uint32))
+        assert np.all(np.isneginf(val[i, m:]))
+
+
+@pytest.mark.parametrize("k", [1, 2048, 8192])
+def test_topk_many_long_rows_exact(k):
+    """More than 64 rows longer than 16K (one workgroup per row, the row held
+    in registers), an odd row stride (unaligned rows), ragged lengths around
+    the 4,096-position load blocks and k."""
+    say(f"topk many long rows k={k}")
+    rng = np.random.default_rng(100 + k)
+    n_rows, ld = 80, 65537
+    u = rng.standard_normal((n_rows, ld)).astype(np.float32)
+    edge = [0, 1, k - 1, k, k + 1, 4095, 4096, 4097, 16385, 32767, 32768, 32769, 65535, 65536]
+    lens = np.array(edge + list(rng.integers(16385, 65537, n_rows - len(edge))), dtype=np.int32)
+    lens = np.clip(lens, 0, 65536)
+    rows = list(range(len(edge))) + list(rng.choice(np.arange(len(edge), n_rows), 6, replace=False))
+    _check_topk_exact_sample(u, lens, k, rows)
+
+
+def test_topk_many_rows_ties_and_signed_zero():
+    say("topk many long rows: heavy ties, signed zeros, all-equal rows")
+    rng = np.random.default_rng(4)
+    n = 40000
+    base = [np.round(rng.standard_normal(n), 1),
+            np.zeros(n),
+            np.where(rng.random(n) < 0.5, -0.0, 0.0),
+            np.full(n, 3.25),
+            np.concatenate([np.full(n // 2, 1.0), np.full(n - n // 2, 2.0)]),
+            rng.choice([-np.inf, 0.0, 1.0], n),
+            rng.integers(0, 4, n) * 0.5]
+    u = np.stack([base[i % len(base)] for i in range(70)]).astype(np.float32)
+    for k in [1, 100, 2048, 9999, 39999]:
+        _check_topk_exact_sample(u, [n] * len(u), k, range(len(base)))
+
+
 @pytest.mark.parametrize("B,k", [(8192, 2048), (300, 300), (5000, 1)])
 def test_hs_anchor_select_nested_exact(B, k):
     say(f"hs_anchor_select B={B} k={k}")
