@@ -70,33 +70,51 @@ def latent_bytes_per_token(wl) -> int:
     return {"bf16": 2, "fp8": 1, "fp32": 4}[wl.cache_dtype] * wl.r + (4 if wl.cache_dtype == "fp8" else 0)
 
 
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "anchor_scan_128k_b4_hbm_traffic.md")
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "anchor_scan_128k_b4_hbm_traffic.md")
 SCAN_SOURCES = ["sparse_attention_indexer_latent_amd/csrc/score_mfma.hip",
                 "sparse_attention_indexer_latent_amd/csrc/li_device.h"]
+MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_score_2048x64k_mfma_counters.md")
+PREFILL_SOURCES = ["sparse_attention_indexer_latent_amd/csrc/score_prefill.hip",
+                   "sparse_attention_indexer_latent_amd/csrc/li_device.h"]
+
+
+def profile_fields(path, sources):
+    """The machine-read `key: value` lines of a committed counter summary, or
+    None when it is missing or the kernel sources changed since it was taken
+    (the summary records their SHA-256)."""
+    import hashlib
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", "-", " ")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return fields if fields.get("kernel_source_sha256") == h.hexdigest() else None
 
 
 def measured_traffic(wl):
     """HBM bytes per anchor-scan launch from the committed counter summary
     (calibrated FETCH_SIZE + WRITE_SIZE), or None when that summary covers
     another workload or the scan kernel's source changed since it was taken."""
-    import hashlib
-    if wl.name != "hs-128k-b4" or not os.path.exists(TRAFFIC_FILE):
-        return None
-    fields = {}
-    for line in open(TRAFFIC_FILE):
-        if ":" in line and not line.startswith(("#", "|", "-", " ")):
-            k, v = line.split(":", 1)
-            fields[k.strip()] = v.strip()
-    h = hashlib.sha256()
-    root = os.path.dirname(os.path.abspath(__file__))
-    for f in SCAN_SOURCES:
-        with open(os.path.join(root, f), "rb") as fh:
-            h.update(fh.read())
-    if fields.get("kernel_source_sha256") != h.hexdigest():
-        return None
+    f = profile_fields(TRAFFIC_FILE, SCAN_SOURCES) if wl.name == "hs-128k-b4" else None
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        return int(f["traffic_bytes_per_launch"]) if f else None
+    except (KeyError, ValueError):
+        return None
+
+
+def measured_mfma_busy():
+    """Fraction of cycles the matrix pipes were busy in the prefill scorer,
+    from the committed counter summary (None when stale)."""
+    f = profile_fields(MFMA_FILE, PREFILL_SOURCES)
+    try:
+        return float(f["mfma_busy_frac"]) if f else None
     except (KeyError, ValueError):
         return None
 
@@ -193,7 +211,9 @@ def prefill_leg(torch, ops, W, DeviceWorkload, iters: int) -> dict:
             "roofline": {"bound": "mfma", "kernel": "score_prefill_kernel",
                          "achieved": flop / score_s / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
                          "unit": "TFLOP/s", "frac": flop / score_s / MFMA_BF16_PEAK,
-                         "avg_kernel_us": score_s * 1e6},
+                         "traffic": None, "avg_kernel_us": score_s * 1e6,
+                         "flop_per_launch": flop,
+                         "mfma_busy_frac_counters": measured_mfma_busy()},
             "tokens_scored_per_s": wl.G * pairs / el}
 
 

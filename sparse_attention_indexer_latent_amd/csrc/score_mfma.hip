@@ -14,26 +14,28 @@
 // MFMA accumulates in fp32, so the only rounding left is ~2^-16 relative in
 // q~ plus fp32 accumulation.  A bf16 q~ input takes a single pass.
 //
-// Structure (one workgroup = 8 wavefronts, two per SIMD, one per CU):
-//  * The flattened list of 64-token pages of all queries is split into
-//    contiguous ranges, one per workgroup (balances ragged batches).  The
-//    exact plan and the block ids of the range cost two global round trips;
-//    the common decode shape (every query max_len long, query q on
-//    sequence q) is guessed at entry, so its first pages stream after one.
-//  * Pages stream HBM -> LDS with direct-to-LDS loads
-//    (global_load_lds_dwordx4), NSTAGE pages in flight, completion tracked
+// Structure (one workgroup = 4 wavefronts over units of TOK = 32 tokens, two
+// workgroups per CU, so one computes while the other waits at a barrier):
+//  * The flattened list of units of all queries is split into contiguous
+//    ranges, one per workgroup (balances ragged batches).  The exact plan
+//    and the block ids of the range cost two global round trips; the common
+//    decode shape (every query max_len long, query q on sequence q) is
+//    guessed at entry, so its first units stream after one.
+//  * Units stream HBM -> LDS with direct-to-LDS loads
+//    (global_load_lds_dwordx4), NSTAGE units in flight, completion tracked
 //    with explicit vmcnt waits and a bare s_barrier.  A token row of 512 B
 //    sits in LDS with its 16-byte chunks XOR-swizzled by (row & 15), so the
 //    MFMA operand reads (16 rows x 16 B per pass) are bank-conflict free.
-//  * Wavefront w holds the A operand of heads 16*(w%4) .. +15 (all of r, hi
-//    and lo: 64 VGPRs) for the whole range and computes heads x tokens
-//    32*(w/4) .. +31 of each page as two 16x16 tiles.
+//  * Wavefront w holds the A operand of heads 16w .. 16w+15 (all of r, hi
+//    and lo for an fp32 q~) for the whole range and computes the unit's
+//    heads x tokens as two 16x16 tiles.
 //  * Epilogue per tile: + beta, ReLU, * w, sum over the lane's 4 heads, two
 //    cross-lane adds (the 16 heads of the group), then the four head groups
-//    meet through LDS one page later (no extra barrier).
-//  * Candidate mode (hierarchical selection): "pages" are 64 candidate slots
+//    meet through LDS one unit later (no extra barrier); the epilogue of
+//    unit p-1 runs while the matrix core works on unit p.
+//  * Candidate mode (hierarchical selection): units are candidate slots
 //    whose physical rows were resolved beforehand; each query owns exactly
-//    ceil(B/64) such pages, so the range plan needs no loads.
+//    ceil(B/TOK) of them, so the range plan needs no loads.
 #include <algorithm>
 
 #include "li_device.h"
@@ -135,10 +137,11 @@ __device__ void plan_range(SH &sh, int n_q, const int32_t *q_len, const int32_t 
 }
 
 // ---------------------------------------------------------------------------
-// Eight wavefronts: wavefront w owns heads 16*(w%4) .. +15 and tokens
-// 32*(w/4) .. +31 of every page (two 16-token tiles).  Two wavefronts per SIMD
-// hide the LDS, MFMA-result and barrier latencies that a single wavefront per
-// SIMD exposes.  The four head groups meet through LDS one page later.
+// Four wavefronts per workgroup: wavefront w owns heads 16w .. 16w+15 of
+// every 32-token unit (two 16-token tiles).  Two workgroups per CU (two
+// wavefronts per SIMD) hide the LDS, MFMA-result and barrier latencies that
+// a single wavefront per SIMD exposes.  The four head groups meet through
+// LDS one unit later.
 //
 // bf16 cache: v_mfma_f32_16x16x32_bf16; an fp32 q~ is carried as bf16 hi + lo.
 // fp8 cache (E4M3FN + per-token fp32 scale): v_mfma_f32_16x16x128_f8f6f4 with
