@@ -29,8 +29,9 @@
 //  * Wavefront w holds the A operand of heads 16w .. 16w+15 (all of r, hi
 //    and lo for an fp32 q~) for the whole range and computes the unit's
 //    heads x tokens as two 16x16 tiles.
-//  * Epilogue per tile: + beta, ReLU, * w, sum over the lane's 4 heads, two
-//    cross-lane adds (the 16 heads of the group), then the four head groups
+//  * Epilogue per tile: + beta (bf16: the MFMAs' start value), ReLU, * w,
+//    sum over the lane's 4 heads, two lane swaps (v_permlane32/16_swap) for
+//    the 16 heads of the group, then the four head groups
 //    meet through LDS one unit later (no extra barrier); the epilogue of
 //    unit p-1 runs while the matrix core works on unit p.
 //  * Candidate mode (hierarchical selection): units are candidate slots
@@ -573,20 +574,27 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
     float p0 = 0.f, p1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float x0 = accO0[i], x1 = accO1[i];
+      float x0 = accO0[i], x1 = accO1[i];  // bf16: beta is already in (the MFMAs' start value)
       if constexpr (C8) {
-        x0 = (x0 * hO[i]) * s0O;
-        x1 = (x1 * hO[i]) * s1O;
+        x0 = (x0 * hO[i]) * s0O + bO[i];
+        x1 = (x1 * hO[i]) * s1O + bO[i];
       }
-      p0 = fmaf(wO[i], fmaxf(x0 + bO[i], 0.f), p0);
-      p1 = fmaf(wO[i], fmaxf(x1 + bO[i], 0.f), p1);
+      // ReLU as an integer max on the bit pattern (negative floats, -0.0
+      // included, are negative integers)
+      p0 = fmaf(wO[i], __int_as_float(max(__float_as_int(x0), 0)), p0);
+      p1 = fmaf(wO[i], __int_as_float(max(__float_as_int(x1), 0)), p1);
     }
-    p0 += __shfl_xor(p0, 16, kWave);
-    p1 += __shfl_xor(p1, 16, kWave);
-    p0 += __shfl_xor(p0, 32, kWave);
-    p1 += __shfl_xor(p1, 32, kWave);
-    const float mine = lane < 16 ? p0 : p1;  // lanes 0..31: token nh*32 + lane
-    if (lane < 32) sh.red[pp & 1][hg][nh * 32 + lane] = mine;
+    // sum over the four 16-lane groups (the group's 16 heads): after the
+    // 32-lane swap, lanes 0-31 hold tile 0 and lanes 32-63 tile 1, each as
+    // two half sums that the 16-lane swap adds up
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false,
+                                                    false);
+    const float q = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    const auto g = __builtin_amdgcn_permlane16_swap(__float_as_uint(q), __float_as_uint(q), false,
+                                                    false);
+    const float v = __uint_as_float(g[0]) + __uint_as_float(g[1]);
+    // lanes 0-15: token nh*32 + lane of tile 0; lanes 32-47: of tile 1
+    if ((lane & 16) == 0) sh.red[pp & 1][hg][nh * 32 + (lane & 15) + ((lane >> 5) << 4)] = v;
   };
   const int row0 = nh * 32 + (lane & 15), row1 = row0 + 16;
   for (int p = 0; p < np; ++p) {
@@ -606,6 +614,7 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
     const char *sp = sh.stage[p % NSTAGE];
     const char *rp0 = sp + row0 * kRowBytes, *rp1 = sp + row1 * kRowBytes;
     f32x4 acc0 = {}, acc1 = {};
+    if constexpr (!C8) acc0 = acc1 = f32x4{bv[0], bv[1], bv[2], bv[3]};
     if constexpr (!C8) {
       // all of the page's B fragments first (16 LDS reads in flight), so the
       // MFMAs wait on them in order instead of once per k-step
