@@ -289,12 +289,14 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if constexpr (QF32) {
+            // v_cvt_pk_bf16_f32 rounds a pair to nearest even in one step
             const float x0 = elem(kb, 2 * e), x1 = elem(kb, 2 * e + 1);
-            const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
-            const uint32_t l0 = f32_to_bf16_bits(x0 - bf16_bits_to_f32(h0));
-            const uint32_t l1 = f32_to_bf16_bits(x1 - bf16_bits_to_f32(h1));
-            abf[0][kb].u[e] = h0 | (h1 << 16);
-            abf[NT - 1][kb].u[e] = l0 | (l1 << 16);
+            const bf16x2 h = {(__bf16)x0, (__bf16)x1};
+            const uint32_t hu = __builtin_bit_cast(uint32_t, h);
+            const bf16x2 l = {(__bf16)(x0 - __uint_as_float(hu << 16)),
+                              (__bf16)(x1 - __uint_as_float(hu & 0xFFFF0000u))};
+            abf[0][kb].u[e] = hu;
+            abf[NT - 1][kb].u[e] = __builtin_bit_cast(uint32_t, l);
           } else {
             abf[0][kb].u[e] = qraw[4 * kb + e];
           }
@@ -406,12 +408,17 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
   int issued = 0;  // local pages whose loads are in flight
   if constexpr (!gather) {
     // Speculative plan for the common decode case, every query with
-    // ceil(max_len / 64) pages and query q reading sequence q: its block ids
-    // and first query operands load together with the real lengths, and the
-    // first pages stream one round trip after entry.  Block ids are clamped
-    // into the pool, so a wrong guess costs bandwidth only; the exact plan
-    // then reissues every stage (loads of a wavefront land in issue order,
-    // so the exact data overwrites the guessed data).
+    // ceil(max_len / TOK) units and query q reading sequence q: its block ids
+    // load together with the real lengths, the first unit streams one round
+    // trip after entry, and the query operands load behind it.  Block ids
+    // are clamped into the pool, so a wrong guess costs bandwidth only; the
+    // exact plan then reissues every stage (loads of a wavefront land in
+    // issue order, so the exact data overwrites the guessed data).
+    //
+    // The loads are unconditional (clamped indices, results dropped where
+    // unused) and the guessed units are issued on one straight path: the
+    // compiler then counts outstanding loads exactly, and converting the
+    // operands waits for them and the first unit only.
     const int PPQ = (max_len + TOK - 1) / TOK;  // units per query
     const bool try_spec = n_q <= kWave && n_q <= cv.n_seq && PPQ > 0 && PPQ <= cv.max_blocks;
     int cnt_s = 0;
@@ -422,37 +429,34 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
       cnt_s = (int)min<int64_t>((g + 1) * T / G - f0s, kMaxPagesPerWG);
       if (cnt_s > kThreads) cnt_s = 0;  // one block id per thread: no guess for longer ranges
     }
-    int len0 = 0, seq0 = 0;
-    if (wave == 0) {  // real lengths and sequence ids of the first 64 queries
-      len0 = lane < n_q ? q_len[lane] : 0;
-      seq0 = lane < n_q ? q_seq[lane] : 0;
-    }
-    int sq = 0, spg = 0, sblk = 0;
-    if (tid < cnt_s) {
-      sq = (int)((f0s + tid) / PPQ);
-      spg = (int)((f0s + tid) % PPQ);
-      sblk = cv.block_table[(int64_t)sq * cv.max_blocks + ((spg * TOK) >> 6)];
-    }
-    if (cnt_s > 0) fetch_query((int)(f0s / PPQ));  // issued after the block ids: not waited for here
+    const int ti = min(tid, max(cnt_s - 1, 0));
+    const int sq = (int)((f0s + ti) / PPQ), spg = (int)((f0s + ti) % PPQ);
+    const int sblk = cv.block_table[(int64_t)sq * cv.max_blocks + ((spg * TOK) >> 6)];
+    const int li = min(lane, n_q - 1);
+    int len0 = q_len[li], seq0 = q_seq[li];  // real lengths and sequences of the first 64 queries
+    if (lane >= n_q) len0 = seq0 = 0;
+    const int slen = q_len[sq];
+    const int q0 = cnt_s > 0 ? (int)(f0s / PPQ) : 0;
     if (tid < cnt_s) {
       sh.prow[tid] = ((sblk >= 0 && sblk < cv.n_blocks) ? sblk : 0) * kPage + ((spg * TOK) & 63);
       sh.pq[tid] = sq;
       sh.ppg[tid] = spg;
+      sh.pvalid[tid] = min(TOK, slen - spg * TOK);
     }
-    lds_barrier();
-    for (; issued < NSTAGE - 1 && issued < cnt_s; ++issued) issue_page(issued, issued);
-    if (cnt_s > 0) finish_query((int)(f0s / PPQ));
     if (wave == 0) {
-      // the guess is the exact plan iff every query has PPQ pages and reads
+      // the guess is the exact plan iff every query has PPQ units and reads
       // its own sequence
       const bool bad = lane < n_q && (((len0 + TOK - 1) / TOK) != PPQ || seq0 != lane);
       const bool ok = try_spec && cnt_s > 0 && __ballot(bad) == 0ull;
-      if (lane == 0) sh.spec_ok = ok ? 1 : 0;
+      if (lane == 0) {
+        sh.spec_ok = ok ? 1 : 0;
+        if (ok) sh.np = cnt_s;
+      }
       sh.qlen[lane] = len0;
       if (!ok) {
         if (n_q <= kWave) {
-          // per-query page counts -> inclusive prefix (lane = query), then
-          // this workgroup's range; the page -> (query, page) map is built
+          // per-query unit counts -> inclusive prefix (lane = query), then
+          // this workgroup's range; the unit -> (query, unit) map is built
           // by all threads below
           const int npq = lane < n_q ? (len0 + TOK - 1) / TOK : 0;
           const int incl = (int)wave_incl_scan((uint32_t)npq);
@@ -468,19 +472,26 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
         } else {
           plan_range<TOK>(sh, n_q, q_len, q_seq, kMaxPagesPerWG, len0, seq0);
         }
-      } else if (lane == 0) {
-        sh.np = cnt_s;
       }
     }
     lds_barrier();
-    if (!sh.spec_ok) {
-      issued = 0;  // every stage is reissued from the exact plan
+    if (sh.spec_ok) {
+      // unit 0, the operands, then the next units (any past the range
+      // re-read the range's last unit and are never consumed)
+      issue_page(0, 0);
+      fetch_query(q0);
+#pragma unroll
+      for (int i = 1; i < NSTAGE - 1; ++i) issue_page(min(i, cnt_s - 1), i);
+      issued = NSTAGE - 1;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NSTAGE - 2) * kVm));
+      finish_query(q0);
+    } else {
       const int npl = sh.np;
       if (n_q <= kWave) {
         const int64_t f0 = sh.f0;
         for (int p = tid; p < npl; p += kThreads) {
           const int f = (int)(f0 + p);
-          int lo = 0, hi = n_q - 1;  // first query whose inclusive page count exceeds f
+          int lo = 0, hi = n_q - 1;  // first query whose inclusive unit count exceeds f
           while (lo < hi) {
             const int mid = (lo + hi) >> 1;
             if (sh.qcum[mid] > f) hi = mid;
@@ -498,12 +509,12 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
                            kPage + ((sh.ppg[p] * TOK) & 63);
       }
       __syncthreads();
-    }
-    // valid tokens per unit (read by the stores, after the loop's barriers)
-    for (int p = tid; p < sh.np; p += kThreads) {
-      const int q = sh.pq[p];
-      const int len = n_q <= kWave ? sh.qlen[q] : q_len[q];
-      sh.pvalid[p] = min(TOK, len - sh.ppg[p] * TOK);
+      // valid tokens per unit (read by the stores, after the loop's barriers)
+      for (int p = tid; p < npl; p += kThreads) {
+        const int q = sh.pq[p];
+        const int len = n_q <= kWave ? sh.qlen[q] : q_len[q];
+        sh.pvalid[p] = min(TOK, len - sh.ppg[p] * TOK);
+      }
     }
   } else {
     // Every query owns exactly ceil(B / 64) candidate slot pages: the range
