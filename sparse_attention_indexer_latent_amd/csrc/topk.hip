@@ -869,7 +869,7 @@ static_assert(kRegBins + 1024 + 2 * (kRegCand + kWave) <= kRegBins * kRegCopies,
               "candidate list fits");
 
 struct RegShared {
-  uint32_t hA[kRegBins * kRegCopies];  // pass A copies [bin][copy]; then B (2048) and C (1024)
+  __align__(16) uint32_t hA[kRegBins * kRegCopies];  // pass A copies [bin][copy]; then B and C
   uint32_t hM[kRegBins];               // pass A merged
   uint32_t gt[kRegMax / 32];
   uint32_t eq[kRegMax / 32];
@@ -904,7 +904,7 @@ topk_reg_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
                 const int32_t *__restrict__ ids, int64_t ids_ld, int ids_rows, int k,
                 int32_t *__restrict__ out_idx, float *__restrict__ out_val) {
   __shared__ RegShared sh;
-  const int row = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid % kWave;
   const int n = min(valid_len[row], NIT * 4 * kThreads);
   const float *u = scores + (int64_t)row * ld;
   const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
