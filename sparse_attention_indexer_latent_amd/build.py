@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "liblatentindex.so")
 ARCH = "gfx950"
 
 SOURCES = ["latentindex_api.cpp", "append.hip", "absorb.hip", "score_valu.hip",
-           "score_mfma.hip", "score_prefill.hip", "topk.hip"]
+           "score_mfma.hip", "score_scan.hip", "score_prefill.hip", "topk.hip"]
 
 # Packed fp32 VALU ops are disabled for all device code.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror", "-Wno-unused-function",

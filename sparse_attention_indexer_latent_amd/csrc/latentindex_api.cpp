@@ -153,6 +153,9 @@ li_status li_score(const void *q_tilde, li_dtype qt_dt, const float *w, const fl
   if (li::score_prefill_supported(qt_dt, H, n_q, cv))
     e = li::launch_score_prefill(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv, scores, ld,
                                  (hipStream_t)stream);
+  else if (li::score_scan_supported(qt_dt, H, n_q, max_len, cv))
+    e = li::launch_score_scan(q_tilde, qt_dt, w, beta, n_q, q_seq, q_len, max_len, cv, scores, ld,
+                              (hipStream_t)stream);
   else if (li::score_mfma_supported(qt_dt, H, cv))
     e = li::launch_score_mfma(q_tilde, qt_dt, w, beta, n_q, H, q_seq, q_len, max_len, cv, nullptr,
                               0, 1, scores, ld, (hipStream_t)stream);

@@ -80,6 +80,22 @@ __device__ __forceinline__ void lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Direct HBM -> LDS load of 16 bytes per lane: lane i's 16 bytes at `g` land
+// at lds + 16 i (the LDS address is taken from the first active lane).
+// Written as inline assembly on purpose: the compiler then does not track the
+// load, so it adds none of its own waits for it (with the builtin form it
+// drains every load in flight before any LDS read that might alias the
+// target, which serialises a multi-stage pipeline).  The caller owns all
+// synchronisation: s_waitcnt vmcnt(n) for the data, then a barrier before
+// other wavefronts read it, and no overwrite before all reads of the old
+// contents are done.  The s_nop is the one wait state required between the
+// M0 write (made by the compiler for the "{m0}" operand) and the load.
+__device__ __forceinline__ void dma16_to_lds(const void *g,
+                                             __attribute__((address_space(3))) void *lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+}
+
 // Inclusive prefix sum across a wavefront with DPP moves (row shifts within
 // 16-lane rows, then row broadcasts 15 and 31 across rows).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {

@@ -59,6 +59,13 @@ hipError_t launch_score_mfma(const void *q_tilde, int qt_dt, const float *w, con
                              int max_len, const CacheView &cv, const int32_t *cand, int B,
                              int cand_rows, float *out, int64_t ld, hipStream_t st);
 
+// score_scan.hip: full-scan decode scorer for a bf16 cache, H == 64,
+// r == 256 and at most 64 queries (page mode), one workgroup per CU.
+bool score_scan_supported(int qt_dt, int H, int n_q, int max_len, const CacheView &cv);
+hipError_t launch_score_scan(const void *q_tilde, int qt_dt, const float *w, const float *beta,
+                             int n_q, const int32_t *q_seq, const int32_t *q_len, int max_len,
+                             const CacheView &cv, float *out, int64_t ld, hipStream_t st);
+
 // score_prefill.hip: matrix-core scorer for many bf16 queries per sequence
 // (a prefill chunk), page mode only.
 bool score_prefill_supported(int qt_dt, int H, int n_q, const CacheView &cv);
