@@ -72,7 +72,7 @@ def latent_bytes_per_token(wl) -> int:
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "anchor_scan_128k_b4_hbm_traffic.md")
-SCAN_SOURCES = ["sparse_attention_indexer_latent_amd/csrc/score_mfma.hip",
+SCAN_SOURCES = ["sparse_attention_indexer_latent_amd/csrc/score_scan.hip",
                 "sparse_attention_indexer_latent_amd/csrc/li_device.h"]
 MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_score_2048x64k_mfma_counters.md")
 PREFILL_SOURCES = ["sparse_attention_indexer_latent_amd/csrc/score_prefill.hip",
@@ -304,7 +304,7 @@ def main():
         "us_per_group_step": us_step,
         "scored_positions_per_step": pos,
         "hbm_frac_step": step_bytes / (el / K) / HBM_PEAK,
-        "roofline": {"bound": "hbm", "kernel": "score_mfma_kernel (anchor full scan)",
+        "roofline": {"bound": "hbm", "kernel": "score_scan_kernel (anchor full scan)",
                      "achieved": scan_bytes / (scan_ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": scan_bytes / (scan_ms * 1e-3) / HBM_PEAK,
                      "traffic": measured_traffic(wl), "avg_kernel_us": scan_ms * 1e3,
