@@ -255,7 +255,10 @@ li_status li_hs_select(const int32_t *cand, int32_t B, int32_t n_f, const void *
   //    candidate and maps to id -1, so the output is the top-min(k, |C|)
   //    then -1 padding.
   hipError_t e;
-  if (li::score_mfma_supported(qt_dt, H, cv))
+  if (li::score_scan_cand_supported(qt_dt, H, rows, B, n_q, cv))
+    e = li::launch_score_scan_cand(q_tilde, qt_dt, w, beta, rows, q_seq, cv, cand, B, n_q, dst, B,
+                                   st);
+  else if (li::score_mfma_supported(qt_dt, H, cv))
     e = li::launch_score_mfma(q_tilde, qt_dt, w, beta, rows, H, q_seq, nullptr, B, cv, cand, B,
                               n_q, dst, B, st);
   else

@@ -65,6 +65,14 @@ bool score_scan_supported(int qt_dt, int H, int n_q, int max_len, const CacheVie
 hipError_t launch_score_scan(const void *q_tilde, int qt_dt, const float *w, const float *beta,
                              int n_q, const int32_t *q_seq, const int32_t *q_len, int max_len,
                              const CacheView &cv, float *out, int64_t ld, hipStream_t st);
+// The same kernel in candidate mode (HS followers): query i scores the B
+// slots of candidate list i % cand_rows into out[i*ld + j], -inf on padding.
+bool score_scan_cand_supported(int qt_dt, int H, int n_q, int B, int cand_rows,
+                               const CacheView &cv);
+hipError_t launch_score_scan_cand(const void *q_tilde, int qt_dt, const float *w,
+                                  const float *beta, int n_q, const int32_t *q_seq,
+                                  const CacheView &cv, const int32_t *cand, int B, int cand_rows,
+                                  float *out, int64_t ld, hipStream_t st);
 
 // score_prefill.hip: matrix-core scorer for many bf16 queries per sequence
 // (a prefill chunk), page mode only.

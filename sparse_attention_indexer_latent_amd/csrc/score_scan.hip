@@ -48,13 +48,17 @@ constexpr int kThr = (kCW + kIW) * kWave;
 constexpr int kPieces = kUnitB / 1024;  // 1 KB loads per unit
 constexpr int kPerIssuer = kPieces / kIW;
 constexpr int kMaxPages = 1024;       // page table of one workgroup's range
+constexpr int kMaxCandUnits = 64;     // candidate mode: units of one workgroup's range
+constexpr int kTab = kMaxCandUnits * kTok;  // table entries (pages, or candidate rows)
+constexpr int kTabPer = (kTab + kThr - 1) / kThr;
+static_assert(kTab >= kMaxPages, "the table holds a page range");
 constexpr int kSwz = 15;
 static_assert(kQst + 2 <= kNst, "q~ staging fits in the stages");
 static_assert(kPerIssuer * kAhead <= 24, "issuer wait counts stay in range");
 
 struct ScanShared {
   __align__(16) char stage[kNst][kUnitB];
-  int32_t page[kMaxPages];  // block id of page u0 + i
+  int32_t page[kTab];  // block id of page u0 + i; candidate mode: cache row of slot 64 u0 + i (-1: none)
   float red[2][4][kTok];    // per head group partial scores, two units
   int32_t ok, myq, mylen, myseq, u0, nu;
 };
@@ -92,11 +96,16 @@ __device__ __forceinline__ int64_t wg_start(int q, int64_t cum, int64_t T, int G
   return q + ((int64_t)(G - n) * cum) / T;
 }
 
-template <bool QF32>
+// CAND: candidate mode (HS followers).  Query i scores the B slots of
+// candidate list c = i % cand_rows (token ids of sequence q_seq[c], -1 for
+// padding) into out[i*ld + j]; units are 64 consecutive slots; q_len and
+// max_len are unused.
+template <bool QF32, bool CAND>
 __global__ void __launch_bounds__(kThr, 1)
 score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
                   const float *__restrict__ beta, int n_q, const int32_t *__restrict__ q_seq,
                   const int32_t *__restrict__ q_len, int max_len, CacheView cv,
+                  const int32_t *__restrict__ cand, int B, int cand_rows, int xw,
                   float *__restrict__ out, int64_t ld) {
   constexpr int NT = QF32 ? 2 : 1;               // A operand terms (bf16 hi + lo, or the bf16 q~)
   constexpr int KB = kR / 32;                    // MFMA k-steps
@@ -137,13 +146,34 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
   };
 
   // ---- plan: guess (every query max_len long, query q on sequence q) ------
-  const int PPQ = (max_len + kTok - 1) / kTok;
+  // (exact in candidate mode: every query has B slots)
+  const int PPQ = ((CAND ? B : max_len) + kTok - 1) / kTok;
   const int64_t T0 = (int64_t)n_q * PPQ;
   int gq = 0;  // guessed query: the last q with start(q) <= g
-  for (int q = 1; q < n_q; ++q)
-    if (wg_start(q, (int64_t)q * PPQ, T0, G, n_q) <= g) gq = q;
   int gu0, gnu;
-  {
+  if (CAND && xw > 0) {
+    // Candidate lists shared by NL layers' queries (i = l * cand_rows + c),
+    // xw ranges per query: the NL workgroups of one (list, range) pair sit
+    // 8 apart in g, i.e. on one XCD (g mod 8) side by side, so the rows they
+    // all read come from that XCD's L2 after the first.
+    const int NL = n_q / cand_rows, NP = cand_rows * xw, full = NP - NP % 8;
+    int j, l;
+    if (g < NL * full) {
+      const int within = g % (8 * NL);
+      l = within / 8;
+      j = (g / (8 * NL)) * 8 + within % 8;
+    } else {
+      const int g2 = g - NL * full, m = NP - full;
+      l = g2 / m;
+      j = full + g2 % m;
+    }
+    const int r = j % xw;
+    gq = l * cand_rows + j / xw;
+    gu0 = (int)((int64_t)r * PPQ / xw);
+    gnu = (int)((int64_t)(r + 1) * PPQ / xw) - gu0;
+  } else {
+    for (int q = 1; q < n_q; ++q)
+      if (wg_start(q, (int64_t)q * PPQ, T0, G, n_q) <= g) gq = q;
     const int s = (int)wg_start(gq, (int64_t)gq * PPQ, T0, G, n_q);
     const int W = (int)wg_start(gq + 1, (int64_t)(gq + 1) * PPQ, T0, G, n_q) - s;
     const int j = g - s;
@@ -155,51 +185,84 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
   // 0), the guessed range's page table, w and beta; one wait covers
   // them all, the q~ loads included, before the barrier that ends the plan.
   fetch_q(gq);
-  const int li = min(lane, n_q - 1);
-  int len0 = q_len[li], seq0 = q_seq[li];
-  if (lane >= n_q) len0 = seq0 = 0;
-  int pg[2];
+  if constexpr (CAND) {
+    // the range's candidate token ids, then their cache rows (a second,
+    // dependent load through the block table)
+    const int c = gq % cand_rows;
+    const int seq = q_seq[c];
+    const int s0 = gu0 * kTok, ns = min(gnu * kTok, B - s0);  // slots of the range
+    int tk[kTabPer], bk[kTabPer];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = min(tid + k * kThr, max(gnu - 1, 0));
-    pg[k] = cv.block_table[(int64_t)gq * cv.max_blocks + min(gu0 + i, cv.max_blocks - 1)];
-  }
-  load_wb(gq);
+    for (int k = 0; k < kTabPer; ++k) {
+      const int i = tid + k * kThr;
+      tk[k] = cand[(int64_t)c * B + min(s0 + min(i, max(ns - 1, 0)), B - 1)];
+      if (i >= ns) tk[k] = -1;
+    }
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
-    if (tid + k * kThr < gnu) sh.page[tid + k * kThr] = pg[k];
-  if (wave == 0) {
-    const bool bad = lane < n_q && (((len0 + kTok - 1) / kTok) != PPQ || seq0 != lane);
-    const bool ok = __ballot(bad) == 0ull;
-    const int glen = min(__shfl(len0, gq, kWave), max_len);
-    if (lane == 0) {
-      sh.ok = ok ? 1 : 0;
+    for (int k = 0; k < kTabPer; ++k)
+      bk[k] = cv.block_table[(int64_t)seq * cv.max_blocks + min(max(tk[k], 0) >> 6, cv.max_blocks - 1)];
+    load_wb(gq);
+#pragma unroll
+    for (int k = 0; k < kTabPer; ++k) {
+      const int i = tid + k * kThr;
+      const int b = (bk[k] >= 0 && bk[k] < cv.n_blocks) ? bk[k] : 0;
+      if (i < gnu * kTok) sh.page[i] = tk[k] < 0 ? -1 : b * kPage + (tk[k] & 63);
+    }
+    if (tid == 0) {
+      sh.ok = 1;
       sh.myq = gq;
-      sh.mylen = glen;
-      sh.myseq = gq;
+      sh.mylen = B;
+      sh.myseq = seq;
       sh.u0 = gu0;
       sh.nu = gnu;
     }
-    if (!ok) {
-      // exact partition from the real lengths
-      const int len = min(len0, max_len);
-      const int units = lane < n_q ? (len + kTok - 1) / kTok : 0;
-      const int incl = (int)wave_incl_scan((uint32_t)units);
-      const int64_t T = max(__shfl(incl, kWave - 1, kWave), 1);
-      const int64_t st = lane < n_q ? wg_start(lane, incl - units, T, G, n_q) : (int64_t)G;
-      const int q = __popcll(__ballot(lane < n_q && st <= g)) - 1;
-      const int s = __shfl((int)st, q, kWave);
-      const int W = (q + 1 < n_q ? __shfl((int)st, q + 1, kWave) : G) - s;
-      const int uq = __shfl(units, q, kWave);
-      const int j = g - s;
-      const int qlen = __shfl(len, q, kWave), qseq = __shfl(seq0, q, kWave);  // all lanes active
+  } else {
+    const int li = min(lane, n_q - 1);
+    int len0 = q_len[li], seq0 = q_seq[li];
+    if (lane >= n_q) len0 = seq0 = 0;
+    int pg[2];
+  #pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = min(tid + k * kThr, max(gnu - 1, 0));
+      pg[k] = cv.block_table[(int64_t)gq * cv.max_blocks + min(gu0 + i, cv.max_blocks - 1)];
+    }
+    load_wb(gq);
+  #pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (tid + k * kThr < gnu) sh.page[tid + k * kThr] = pg[k];
+    if (wave == 0) {
+      const bool bad = lane < n_q && (((len0 + kTok - 1) / kTok) != PPQ || seq0 != lane);
+      const bool ok = __ballot(bad) == 0ull;
+      const int glen = min(__shfl(len0, gq, kWave), max_len);
       if (lane == 0) {
-        const int a = (int)((int64_t)j * uq / W), b = (int)((int64_t)(j + 1) * uq / W);
-        sh.myq = q;
-        sh.mylen = qlen;
-        sh.myseq = qseq;
-        sh.u0 = a;
-        sh.nu = b - a;
+        sh.ok = ok ? 1 : 0;
+        sh.myq = gq;
+        sh.mylen = glen;
+        sh.myseq = gq;
+        sh.u0 = gu0;
+        sh.nu = gnu;
+      }
+      if (!ok) {
+        // exact partition from the real lengths
+        const int len = min(len0, max_len);
+        const int units = lane < n_q ? (len + kTok - 1) / kTok : 0;
+        const int incl = (int)wave_incl_scan((uint32_t)units);
+        const int64_t T = max(__shfl(incl, kWave - 1, kWave), 1);
+        const int64_t st = lane < n_q ? wg_start(lane, incl - units, T, G, n_q) : (int64_t)G;
+        const int q = __popcll(__ballot(lane < n_q && st <= g)) - 1;
+        const int s = __shfl((int)st, q, kWave);
+        const int W = (q + 1 < n_q ? __shfl((int)st, q + 1, kWave) : G) - s;
+        const int uq = __shfl(units, q, kWave);
+        const int j = g - s;
+        const int qlen = __shfl(len, q, kWave), qseq = __shfl(seq0, q, kWave);  // all lanes active
+        if (lane == 0) {
+          const int a = (int)((int64_t)j * uq / W), b = (int)((int64_t)(j + 1) * uq / W);
+          sh.myq = q;
+          sh.mylen = qlen;
+          sh.myseq = qseq;
+          sh.u0 = a;
+          sh.nu = b - a;
+        }
       }
     }
   }
@@ -228,16 +291,28 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
   // each), issuer i loads pieces 8i .. 8i+7 ------------------------------------
   const int gi0 = (wave - kCW) * kPerIssuer;
   auto issue_unit = [&](int u) INL {
-    int b = sh.page[u];
-    b = (b >= 0 && b < cv.n_blocks) ? b : 0;
-    const char *src = gdata + (int64_t)b * kUnitB;
     LDS3 char *st = (LDS3 char *)sh.stage[u % kNst];
+    if constexpr (CAND) {
+      // every half-wavefront gathers one candidate row (a padding slot reads row 0)
 #pragma unroll
-    for (int m = 0; m < kPerIssuer; ++m) {
-      const int gi = gi0 + m;
-      const int r = gi * 2 + lane / 32;
-      const int chunk = (lane % 32) ^ (r & kSwz);
-      dma16_to_lds(src + r * kRowB + chunk * 16, (LDS3 void *)(st + gi * 1024));
+      for (int m = 0; m < kPerIssuer; ++m) {
+        const int gi = gi0 + m;
+        const int r = gi * 2 + lane / 32;
+        const int chunk = (lane % 32) ^ (r & kSwz);
+        const int64_t row = max(sh.page[u * kTok + r], 0);
+        dma16_to_lds(gdata + row * kRowB + chunk * 16, (LDS3 void *)(st + gi * 1024));
+      }
+    } else {
+      int b = sh.page[u];
+      b = (b >= 0 && b < cv.n_blocks) ? b : 0;
+      const char *src = gdata + (int64_t)b * kUnitB;
+#pragma unroll
+      for (int m = 0; m < kPerIssuer; ++m) {
+        const int gi = gi0 + m;
+        const int r = gi * 2 + lane / 32;
+        const int chunk = (lane % 32) ^ (r & kSwz);
+        dma16_to_lds(src + r * kRowB + chunk * 16, (LDS3 void *)(st + gi * 1024));
+      }
     }
   };
   int issued = min(nu, kQst);  // prologue: units clear of the q~ copy
@@ -305,7 +380,11 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
       const float *rd = &sh.red[pp & 1][0][0];
       const float v = ((rd[lane] + rd[kTok + lane]) + rd[2 * kTok + lane]) + rd[3 * kTok + lane];
       const int t = (u0 + pp) * kTok + lane;
-      if (t < mylen) out[(int64_t)myq * ld + t] = v;
+      if (CAND) {
+        if (t < mylen) out[(int64_t)myq * ld + t] = sh.page[pp * kTok + lane] < 0 ? -INFINITY : v;
+      } else if (t < mylen) {
+        out[(int64_t)myq * ld + t] = v;
+      }
     }
   };
 
@@ -363,16 +442,38 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
 
 int g_scan_cu = 0;
 
-int scan_grid(int n_q, int max_len) {
+// One workgroup per CU, two units each at least, one per query at least.
+int scan_grid(int n_q, int64_t units_per_query) {
   if (g_scan_cu == 0) {
     int dev = 0;
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&g_scan_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (g_scan_cu <= 0) g_scan_cu = 256;
   }
-  // one workgroup per CU, two pages each at least, one per query at least
-  const int64_t T = (int64_t)n_q * ((max_len + kTok - 1) / kTok);
+  const int64_t T = (int64_t)n_q * units_per_query;
   return (int)std::max<int64_t>(std::min<int64_t>(g_scan_cu, (T + 1) / 2), n_q);
+}
+
+// Most units one workgroup gets: a query with U units gets W > (G - n) U / T
+// workgroups, so fewer than T / (G - n) + 1 units each; with G == n, U.
+int64_t max_units_per_wg(int n_q, int64_t units_per_query) {
+  const int G = scan_grid(n_q, units_per_query);
+  const int64_t T = (int64_t)n_q * units_per_query;
+  return G > n_q ? T / (G - n_q) + 1 : units_per_query;
+}
+
+// Candidate mode: with n_q a multiple of cand_rows, xw ranges per query and
+// G = n_q * xw (the XCD-grouped plan); else the proportional plan (xw = 0).
+void cand_plan(int n_q, int B, int cand_rows, int *G, int *xw) {
+  const int64_t U = (B + kTok - 1) / kTok;
+  if (n_q % cand_rows == 0) {
+    (void)scan_grid(n_q, U);  // reads the CU count
+    *xw = (int)std::max<int64_t>(1, std::min<int64_t>(g_scan_cu / n_q, U));
+    *G = n_q * *xw;
+  } else {
+    *xw = 0;
+    *G = scan_grid(n_q, U);
+  }
 }
 
 }  // namespace
@@ -381,25 +482,46 @@ bool score_scan_supported(int qt_dt, int H, int n_q, int max_len, const CacheVie
   if (!((qt_dt == LI_FP32 || qt_dt == LI_BF16) && H == 64 && cv.r == kR && cv.dtype == LI_BF16 &&
         n_q >= 1 && n_q <= kWave && n_q <= cv.n_seq && max_len >= 1))
     return false;
-  // Every workgroup's pages must fit its table.  A query with U pages gets W >
-  // (G - n) U / T workgroups, so fewer than T / (G - n) + 1 pages each; with
-  // G == n, a query's pages.
-  const int G = scan_grid(n_q, max_len);
-  const int64_t T = (int64_t)n_q * ((max_len + kTok - 1) / kTok);
-  const int64_t pages = G > n_q ? T / (G - n_q) + 1 : T / n_q;
-  return pages <= kMaxPages;
+  return max_units_per_wg(n_q, (max_len + kTok - 1) / kTok) <= kMaxPages;  // pages fit the table
+}
+
+bool score_scan_cand_supported(int qt_dt, int H, int n_q, int B, int cand_rows,
+                               const CacheView &cv) {
+  if (!((qt_dt == LI_FP32 || qt_dt == LI_BF16) && H == 64 && cv.r == kR && cv.dtype == LI_BF16 &&
+        n_q >= 1 && B >= 1 && cand_rows >= 1))
+    return false;
+  int G, xw;
+  cand_plan(n_q, B, cand_rows, &G, &xw);
+  const int64_t U = (B + kTok - 1) / kTok;
+  const int64_t units = xw > 0 ? (U + xw - 1) / xw : max_units_per_wg(n_q, U);
+  return units <= kMaxCandUnits;  // slots fit the table
 }
 
 hipError_t launch_score_scan(const void *q_tilde, int qt_dt, const float *w, const float *beta,
                              int n_q, const int32_t *q_seq, const int32_t *q_len, int max_len,
                              const CacheView &cv, float *out, int64_t ld, hipStream_t st) {
-  const int G = scan_grid(n_q, max_len);
+  const int G = scan_grid(n_q, (max_len + kTok - 1) / kTok);
   if (qt_dt == LI_FP32)
-    score_scan_kernel<true><<<G, kThr, 0, st>>>(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv,
-                                                out, ld);
+    score_scan_kernel<true, false><<<G, kThr, 0, st>>>(q_tilde, w, beta, n_q, q_seq, q_len, max_len,
+                                                       cv, nullptr, 0, 1, 0, out, ld);
   else
-    score_scan_kernel<false><<<G, kThr, 0, st>>>(q_tilde, w, beta, n_q, q_seq, q_len, max_len, cv,
-                                                 out, ld);
+    score_scan_kernel<false, false><<<G, kThr, 0, st>>>(q_tilde, w, beta, n_q, q_seq, q_len, max_len,
+                                                        cv, nullptr, 0, 1, 0, out, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_scan_cand(const void *q_tilde, int qt_dt, const float *w,
+                                  const float *beta, int n_q, const int32_t *q_seq,
+                                  const CacheView &cv, const int32_t *cand, int B, int cand_rows,
+                                  float *out, int64_t ld, hipStream_t st) {
+  int G, xw;
+  cand_plan(n_q, B, cand_rows, &G, &xw);
+  if (qt_dt == LI_FP32)
+    score_scan_kernel<true, true><<<G, kThr, 0, st>>>(q_tilde, w, beta, n_q, q_seq, nullptr, 0, cv,
+                                                      cand, B, cand_rows, xw, out, ld);
+  else
+    score_scan_kernel<false, true><<<G, kThr, 0, st>>>(q_tilde, w, beta, n_q, q_seq, nullptr, 0, cv,
+                                                       cand, B, cand_rows, xw, out, ld);
   return hipGetLastError();
 }
 
