@@ -348,6 +348,7 @@ topk_extract_kernel(const float *__restrict__ scores, int64_t ld, const int32_t 
                     int k0, int k1, MultiWs m) {
   __shared__ uint32_t wt[kSegThreads / kWave];
   __shared__ uint32_t res[4];
+  __shared__ uint32_t h12[kBins];
   const int row = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
   const int n = valid_len[row];
   const int p0 = seg * kSeg;
@@ -355,21 +356,34 @@ topk_extract_kernel(const float *__restrict__ scores, int64_t ld, const int32_t 
     if (tid == 0) m.seg_cnt[(int64_t)row * m.S + seg] = 0;
     return;
   }
-  const uint32_t *g = m.hist + (int64_t)row * kBins;
-  // threshold buckets of both outputs (all ones: the output takes every key)
-  uint32_t bk[2] = {0xFFFFFFFFu, 0xFFFFFFFFu}, above, c;
-  if (k0 < n) bk[0] = nt_find<kSegThreads>(g, kBins, (uint32_t)k0, wt, res, &above, &c);
-  if (k1 > 0 && k1 < n) bk[1] = nt_find<kSegThreads>(g, kBins, (uint32_t)k1, wt, res, &above, &c);
-  const int kmax = max(k0, k1);
-  const uint32_t b1 = kmax < n ? (k1 > k0 ? bk[1] : bk[0]) : 0u;  // extraction bucket
+  // one round trip: this segment's scores and the row histogram (into LDS)
   const float *u = scores + (int64_t)row * ld;
   const int pb = p0 + tid * kSegPer;
   uint32_t key[kSegPer];
-  uint32_t cnt = 0;
 #pragma unroll
   for (int e = 0; e < kSegPer; ++e) {
     const int p = pb + e;
     key[e] = p < n ? score_key(u[p]) : 0u;
+  }
+  {
+    const uint32_t *g = m.hist + (int64_t)row * kBins;
+    uint32_t a[kBins / kSegThreads];
+#pragma unroll
+    for (int e = 0; e < kBins / kSegThreads; ++e) a[e] = g[e * kSegThreads + tid];
+#pragma unroll
+    for (int e = 0; e < kBins / kSegThreads; ++e) h12[e * kSegThreads + tid] = a[e];
+  }
+  lds_sync();
+  // threshold buckets of both outputs (all ones: the output takes every key)
+  uint32_t bk[2] = {0xFFFFFFFFu, 0xFFFFFFFFu}, above, c;
+  if (k0 < n) bk[0] = nt_find<kSegThreads>(h12, kBins, (uint32_t)k0, wt, res, &above, &c);
+  if (k1 > 0 && k1 < n) bk[1] = nt_find<kSegThreads>(h12, kBins, (uint32_t)k1, wt, res, &above, &c);
+  const int kmax = max(k0, k1);
+  const uint32_t b1 = kmax < n ? (k1 > k0 ? bk[1] : bk[0]) : 0u;  // extraction bucket
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int e = 0; e < kSegPer; ++e) {
+    const int p = pb + e;
     cnt += (p < n && (key[e] >> 20) >= b1) ? 1u : 0u;
   }
   uint32_t tot;
@@ -583,6 +597,8 @@ constexpr int kSelBatch = 16;       // extracted keys per thread in flight
 constexpr int kMaxChunks = 4096;    // chunk (16 keys) -> segment table
 
 struct SelShared {
+  uint32_t h12[kBins];     // the row's histograms, copied in one round trip
+  uint32_t h10[2][1024];
   uint32_t seg_off[kMaxSegs + 1];
   uint16_t cseg[kMaxChunks];
   uint32_t hlow[2][1024];  // low 10 bits of the keys sharing the 22-bit prefix: whole row
@@ -613,6 +629,20 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
   if (n <= 0 || seg >= S) return;  // uniform per workgroup
   const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
   const float *u = scores + (int64_t)row * ld;
+  {
+    // the row histograms into LDS, all loads issued before any is used
+    const uint32_t *g12 = m.hist + (int64_t)row * kBins;
+    const uint32_t *g10 = m.h10 + (int64_t)row * 2 * 1024;
+    uint32_t a[kBins / kSelThreads], b[2 * 1024 / kSelThreads];
+#pragma unroll
+    for (int e = 0; e < kBins / kSelThreads; ++e) a[e] = g12[e * kSelThreads + tid];
+#pragma unroll
+    for (int e = 0; e < 2 * 1024 / kSelThreads; ++e) b[e] = g10[e * kSelThreads + tid];
+#pragma unroll
+    for (int e = 0; e < kBins / kSelThreads; ++e) sh.h12[e * kSelThreads + tid] = a[e];
+#pragma unroll
+    for (int e = 0; e < 2 * 1024 / kSelThreads; ++e) (&sh.h10[0][0])[e * kSelThreads + tid] = b[e];
+  }
   // offsets of the segments' lists in the row's flattened extracted keys
   const uint32_t *cnt = m.seg_cnt + (int64_t)row * m.S;
   uint32_t carry = 0;
@@ -641,15 +671,13 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
   uint32_t pre22[2] = {0, 0}, need[2] = {0, 0};
 #pragma unroll
   for (int j = 0; j < 2; ++j) act[j] = j < n_out && out[j].k < n;  // else every key is taken
-  const uint32_t *g12 = m.hist + (int64_t)row * kBins;
-  const uint32_t *g10 = m.h10 + (int64_t)row * 2 * 1024;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (!act[j]) continue;
     uint32_t above, c;
-    const uint32_t b12 = nt_find<kSelThreads>(g12, kBins, (uint32_t)out[j].k, sh.wt, sh.res, &above, &c);
+    const uint32_t b12 = nt_find<kSelThreads>(sh.h12, kBins, (uint32_t)out[j].k, sh.wt, sh.res, &above, &c);
     const uint32_t nd = (uint32_t)out[j].k - above;
-    const uint32_t d10 = nt_find<kSelThreads>(g10 + j * 1024, 1024, nd, sh.wt, sh.res, &above, &c);
+    const uint32_t d10 = nt_find<kSelThreads>(sh.h10[j], 1024, nd, sh.wt, sh.res, &above, &c);
     need[j] = nd - above;
     pre22[j] = (b12 << 10) | d10;
   }
