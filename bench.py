@@ -53,8 +53,10 @@ def parse():
     ap.add_argument("--prefill-iters", type=int, default=10)
     ap.add_argument("--path", choices=["hs", "prefill"], default="hs",
                     help="with --profile-steps: which path to run")
-    ap.add_argument("--eager", action="store_true",
-                    help="launch every kernel from the host instead of replaying HIP graphs")
+    ap.add_argument("--graphs", action="store_true",
+                    help="replay the step as two HIP graphs around a direct scan launch instead of "
+                         "launching every kernel from the host (on this stack a graph's end costs "
+                         "~8 us before the next launch starts, more than the host needs per launch)")
     return ap.parse_args()
 
 
@@ -71,6 +73,45 @@ def latent_bytes_per_token(wl) -> int:
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+EV_EVERY = 5  # timed steps per event-timed anchor scan
+
+
+class ScanEvent:
+    """A HIP timing event without the system-scope fence a default event
+    performs when it completes (hipEventDisableSystemFence): that fence's
+    cache writeback and invalidation would otherwise sit inside the timed
+    interval (+2 us on the scan here) and slow the following kernels.
+    Recorded on torch's current stream, read like torch.cuda.Event."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        import torch
+        self._torch = torch
+        if ScanEvent._hip is None:
+            ScanEvent._hip = ctypes.CDLL("libamdhip64.so")
+        self._c = ctypes
+        self.e = ctypes.c_void_p()
+        r = self._hip.hipEventCreateWithFlags(ctypes.byref(self.e), ctypes.c_uint(0x20000000))
+        if r != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({r})")
+
+    def record(self):
+        r = self._hip.hipEventRecord(self.e,
+                                     self._c.c_void_p(self._torch.cuda.current_stream().cuda_stream))
+        if r != 0:
+            raise RuntimeError(f"hipEventRecord failed ({r})")
+
+    def elapsed_time(self, end) -> float:
+        ms = self._c.c_float()
+        r = self._hip.hipEventElapsedTime(self._c.byref(ms), self.e, end.e)
+        if r != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({r})")
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "e", None) and ScanEvent._hip is not None:
+            ScanEvent._hip.hipEventDestroy(self.e)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "anchor_scan_128k_b4_hbm_traffic.md")
 SCAN_SOURCES = ["sparse_attention_indexer_latent_amd/csrc/score_scan.hip",
                 "sparse_attention_indexer_latent_amd/csrc/li_device.h"]
@@ -243,11 +284,11 @@ def main():
     wl = W.config(args.config)
     hs = wl.B is not None
     dw = DeviceWorkload(wl, hold_last=True)
-    if args.eager:
-        step = dw.hs_step if hs else dw.full_step
-    else:
+    if args.graphs:
         graphs = dw.capture(hs)
         step = graphs.replay
+    else:
+        step = dw.hs_step if hs else dw.full_step
 
     for _ in range(args.warmup):
         step()
@@ -264,16 +305,18 @@ def main():
         return
 
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+    # Events bracket the anchor scan on every EV_EVERY-th timed step: even a
+    # fence-free pair of event records costs ~3 us of a ~115 us step, so
+    # timing every step would slow the very loop whose throughput is reported.
+    evs = {i: (ScanEvent(), ScanEvent()) for i in range(0, K, EV_EVERY)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(events=evs[i])
+        step(events=evs.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     el = t1 - t0
-    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs.values()]))
 
     pos = scored_positions(wl, hs)
     bpt = latent_bytes_per_token(wl)
@@ -300,7 +343,8 @@ def main():
                                f"L={wl.max_len}, H={wl.H}, r={wl.r}, {wl.cache_dtype} latent, "
                                f"B={wl.B}, k={wl.k}, 64-token pages, random block table",
                    "global_batch": wl.n_q, "seq_len": wl.max_len, "parallelism": "none (1 GPU)",
-                   "launch": "eager" if args.eager else "hipGraph pre | direct anchor scan | hipGraph post"},
+                   "launch": "hipGraph pre | direct anchor scan | hipGraph post" if args.graphs
+                   else "direct launches from the host on one stream"},
         "us_per_group_step": us_step,
         "scored_positions_per_step": pos,
         "hbm_frac_step": step_bytes / (el / K) / HBM_PEAK,
@@ -314,18 +358,17 @@ def main():
     if not args.no_extra:
         # Full scan of the same group (every layer scans everything).
         Kf = max(5, K // 2)
-        fstep = dw.full_step if args.eager else dw.capture(False).replay
+        fstep = dw.capture(False).replay if args.graphs else dw.full_step
         for _ in range(2):
             fstep()
-        fevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(Kf)]
+        fevs = {i: (ScanEvent(), ScanEvent()) for i in range(0, Kf, EV_EVERY)}
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(Kf):
-            fstep(events=fevs[i])
+            fstep(events=fevs.get(i))
         torch.cuda.synchronize()
         elf = time.perf_counter() - t0
-        fscan = float(np.mean([a.elapsed_time(b) for a, b in fevs]))
+        fscan = float(np.mean([a.elapsed_time(b) for a, b in fevs.values()]))
         fpos = scored_positions(wl, False)
         out["full_scan"] = {"us_per_group_step": elf / Kf * 1e6,
                             "scored_tokens_per_s": fpos * Kf / elf,
