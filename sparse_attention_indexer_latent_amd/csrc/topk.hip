@@ -343,6 +343,40 @@ __device__ uint32_t nt_find(const uint32_t *hist, int nb, uint32_t nd, uint32_t 
   return b;
 }
 
+// The same search by one wavefront, without barriers (nb a multiple of 64,
+// at most 4096): lane l owns bins top - l*per ... top - l*per - per + 1
+// (highest bins to lane 0) and sums them, reading them rotated by l so the
+// wavefront's reads spread over the LDS banks; a wavefront prefix sum picks
+// the lane holding the nd-th largest key, then every lane takes one of that
+// lane's bins and a second prefix sum picks the bin.  nd must be at least 1
+// and at most the histogram total.
+__device__ uint32_t wave_find(const uint32_t *hist, int nb, uint32_t nd, uint32_t *above,
+                              uint32_t *count) {
+  const int lane = threadIdx.x % kWave;
+  const int per = nb / kWave;
+  const int top = nb - 1 - lane * per;
+  uint32_t sum = 0;
+  for (int e = 0; e < per; ++e) sum += hist[top - ((e + lane) & (per - 1))];
+  const uint32_t incl = wave_incl_scan(sum), excl = incl - sum;
+  const uint64_t hit = __ballot(excl < nd && nd <= incl);
+  const int L = hit ? __ffsll((unsigned long long)hit) - 1 : kWave - 1;
+  const uint32_t base = __shfl(excl, L, kWave);
+  const int topL = nb - 1 - L * per;
+  const uint32_t v = lane < per ? hist[topL - lane] : 0u;
+  const uint32_t inc2 = base + wave_incl_scan(v), ex2 = inc2 - v;
+  const uint64_t hit2 = __ballot(lane < per && ex2 < nd && nd <= inc2);
+  const int t = hit2 ? __ffsll((unsigned long long)hit2) - 1 : 0;
+  *above = __shfl(ex2, t, kWave);
+  *count = __shfl(v, t, kWave);
+  return (uint32_t)(topL - t);
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
 __global__ void __launch_bounds__(kSegThreads)
 topk_extract_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ valid_len,
                     int k0, int k1, MultiWs m) {
@@ -584,8 +618,9 @@ struct FinOut {
 // Select step of the multi-workgroup path, one workgroup per (row, segment).
 // Every workgroup derives the exact thresholds itself: the 12-bit bucket from
 // the row histogram, the next 10 bits from the bucket's histogram built by the
-// extract step, the last 10 bits from the row's extracted keys that share
-// those 22 bits.  The same pass over the extracted keys counts, in the
+// extract step (one wavefront per output, single-wavefront searches), the last
+// 10 bits from the row's extracted keys that share those 22 bits.  The same
+// pass over the extracted keys (one wavefront per segment) counts, in the
 // segments before its own, the keys above each threshold and those equal to
 // it, which fixes the output offset of the segment's first selected key; the
 // segment then emits its own selected keys in ascending positions.  Two
@@ -593,18 +628,15 @@ struct FinOut {
 // of a 32-bit word where they are bounded by 2048).
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 512;
-constexpr int kSelBatch = 16;       // extracted keys per thread in flight
-constexpr int kMaxChunks = 4096;    // chunk (16 keys) -> segment table
 
 struct SelShared {
   uint32_t h12[kBins];     // the row's histograms, copied in one round trip
   uint32_t h10[2][1024];
   uint32_t seg_off[kMaxSegs + 1];
-  uint16_t cseg[kMaxChunks];
   uint32_t hlow[2][1024];  // low 10 bits of the keys sharing the 22-bit prefix: whole row
   uint32_t hbef[2][1024];  // ... in segments before this one
   uint32_t wt[kSelThreads / kWave];
-  uint32_t res[4];
+  uint32_t pre22[2], need[2], gtb[2], theta[2], need_eq[2], all_eq[2], sel_before[2], eq_before[2];
 };
 
 __global__ void __launch_bounds__(kSelThreads)
@@ -659,73 +691,106 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
     (&sh.hbef[0][0])[b] = 0;
   }
   lds_sync();
-  const uint32_t M = carry;
-  // chunk -> segment table (segment of flat index 16c)
-  const uint32_t n_chunks = min((M + 15) / 16, (uint32_t)kMaxChunks);
-  for (int s = tid; s < S; s += kSelThreads) {
-    const uint32_t c0 = (sh.seg_off[s] + 15) / 16, c1 = min((sh.seg_off[s + 1] + 15) / 16, n_chunks);
-    for (uint32_t c = c0; c < c1; ++c) sh.cseg[c] = (uint16_t)s;
-  }
-  // thresholds: top 12 bits, then the next 10
+  if (tid < 2) sh.gtb[tid] = 0;
+  // thresholds: top 12 bits, then the next 10; output j's by wavefront j
+  const int lane = tid % kWave, wave = tid / kWave;
+  constexpr int NW = kSelThreads / kWave;
   bool act[2];
-  uint32_t pre22[2] = {0, 0}, need[2] = {0, 0};
 #pragma unroll
   for (int j = 0; j < 2; ++j) act[j] = j < n_out && out[j].k < n;  // else every key is taken
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (!act[j]) continue;
+  // (selects instead of indexing by the wavefront: a runtime index would put
+  // the arrays in scratch memory)
+  const bool act_w = wave == 0 ? act[0] : act[1];
+  const uint32_t k_w = (uint32_t)(wave == 0 ? o0.k : o1.k);
+  if (wave < 2 && act_w) {
+    const int j = wave;
     uint32_t above, c;
-    const uint32_t b12 = nt_find<kSelThreads>(sh.h12, kBins, (uint32_t)out[j].k, sh.wt, sh.res, &above, &c);
-    const uint32_t nd = (uint32_t)out[j].k - above;
-    const uint32_t d10 = nt_find<kSelThreads>(sh.h10[j], 1024, nd, sh.wt, sh.res, &above, &c);
-    need[j] = nd - above;
-    pre22[j] = (b12 << 10) | d10;
+    const uint32_t b12 = wave_find(sh.h12, kBins, k_w, &above, &c);
+    const uint32_t nd = k_w - above;
+    const uint32_t d10 = wave_find(sh.h10[j], 1024, nd, &above, &c);
+    if (lane == 0) {
+      sh.pre22[j] = (b12 << 10) | d10;
+      sh.need[j] = nd - above;
+    }
   }
-  lds_sync();  // cseg complete
-  // one pass over the row's extracted keys
+  lds_sync();
+  uint32_t pre22[2] = {0, 0}, need[2] = {0, 0};
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (act[j]) {
+      pre22[j] = sh.pre22[j];
+      need[j] = sh.need[j];
+    }
+  // One pass over the row's extracted keys, one wavefront per segment, four
+  // segments at a time with their first 256 keys loaded before any is used:
+  // the low 10 bits of the keys sharing each 22-bit prefix, over the row and
+  // over the segments before this one, and the keys above it before this one.
   const uint32_t *lkey = m.lkey + (int64_t)row * m.S * kSeg;
   const uint32_t my0 = sh.seg_off[seg];
-  uint32_t gt_bef[2] = {0, 0};
+  uint32_t gt_bef[2] = {0, 0};  // per wavefront, the same in every lane
   if (act[0] || act[1]) {
-    for (uint32_t base = 0; base < M; base += kSelThreads * kSelBatch) {
-      uint32_t key[kSelBatch];
+    for (int t0 = wave; t0 < S; t0 += NW * 4) {
+      int sgs[4];
+      uint32_t cn[4], key[4][4];
 #pragma unroll
-      for (int e = 0; e < kSelBatch; ++e) {
-        const uint32_t i = base + e * kSelThreads + tid;
-        key[e] = 0;
-        if (i < M) {
-          int s;
-          if ((i >> 4) < n_chunks) {
-            s = sh.cseg[i >> 4];
-          } else {  // beyond the table: binary search
-            int lo = 0, hi = S - 1;
-            while (lo < hi) {
-              const int mid = (lo + hi + 1) >> 1;
-              if (sh.seg_off[mid] <= i) lo = mid; else hi = mid - 1;
+      for (int u = 0; u < 4; ++u) {
+        sgs[u] = t0 + NW * u;
+        cn[u] = sgs[u] < S ? sh.seg_off[sgs[u] + 1] - sh.seg_off[sgs[u]] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t e = c * kWave + lane;
+          key[u][c] = e < cn[u] ? lkey[(int64_t)sgs[u] * kSeg + e] : 0u;
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool before = sgs[u] < seg;  // wave-uniform, as is sgs[u] < S
+        auto visit = [&](uint32_t k, bool valid) __attribute__((always_inline)) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint32_t hi22 = k >> 10;
+            if (act[j] && valid && hi22 == pre22[j]) {
+              atomicAdd(&sh.hlow[j][k & 1023u], 1u);
+              if (before) atomicAdd(&sh.hbef[j][k & 1023u], 1u);
             }
-            s = lo;
+            const uint32_t g = (uint32_t)__popcll(__ballot(act[j] && before && valid && hi22 > pre22[j]));
+            gt_bef[j] += g;  // the same in every lane
           }
-          while (sh.seg_off[s + 1] <= i) ++s;
-          key[e] = lkey[(int64_t)s * kSeg + (i - sh.seg_off[s])];
-        }
-      }
+        };
+        if (sgs[u] < S) {
 #pragma unroll
-      for (int e = 0; e < kSelBatch; ++e) {
-        const uint32_t i = base + e * kSelThreads + tid;
-        if (i >= M) continue;
-        const bool before = i < my0;
-        const uint32_t hi22 = key[e] >> 10;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (!act[j]) continue;
-          if (hi22 == pre22[j]) {
-            atomicAdd(&sh.hlow[j][key[e] & 1023u], 1u);
-            if (before) atomicAdd(&sh.hbef[j][key[e] & 1023u], 1u);
-          } else if (before && hi22 > pre22[j]) {
-            ++gt_bef[j];
+          for (int c = 0; c < 4; ++c) visit(key[u][c], (uint32_t)(c * kWave + lane) < cn[u]);
+          for (uint32_t e0 = 4 * kWave; e0 < cn[u]; e0 += kWave) {  // segments with more keys
+            const uint32_t e = e0 + lane;
+            visit(e < cn[u] ? lkey[(int64_t)sgs[u] * kSeg + e] : 0u, e < cn[u]);
           }
         }
       }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (act[j] && lane == 0 && gt_bef[j]) atomicAdd(&sh.gtb[j], gt_bef[j]);
+  lds_sync();
+  // exact thresholds and this segment's offsets, output j's by wavefront j
+  if (wave < 2 && act_w) {
+    const int j = wave;
+    const uint32_t need_w = j == 0 ? need[0] : need[1], pre_w = j == 0 ? pre22[0] : pre22[1];
+    uint32_t above, c;
+    const uint32_t d = wave_find(sh.hlow[j], 1024, need_w, &above, &c);
+    uint32_t gl = 0;  // keys of the 22-bit prefix above theta, before this segment
+    for (int b = lane; b < 1024; b += kWave)
+      if ((uint32_t)b > d) gl += sh.hbef[j][b];
+    gl = wave_sum_u32(gl);
+    if (lane == 0) {
+      const uint32_t ne = need_w - above, eb = sh.hbef[j][d];
+      sh.theta[j] = (pre_w << 10) | d;
+      sh.need_eq[j] = ne;
+      sh.all_eq[j] = ne == c ? 1u : 0u;
+      sh.eq_before[j] = eb;
+      sh.sel_before[j] = sh.gtb[j] + gl + min(eb, ne);
     }
   }
   lds_sync();
@@ -735,17 +800,11 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (!act[j]) continue;  // every key is taken: offset = extracted keys before
-    uint32_t gtb, above, c, gt_low = 0, t2;
-    (void)nt_scan<kSelThreads>(gt_bef[j], sh.wt, &gtb);
-    const uint32_t d = nt_find<kSelThreads>(sh.hlow[j], 1024, need[j], sh.wt, sh.res, &above, &c);
-    theta[j] = (pre22[j] << 10) | d;
-    need_eq[j] = need[j] - above;
-    all_eq[j] = need_eq[j] == c;
-    for (int b = tid; b < 1024; b += kSelThreads)
-      if ((uint32_t)b > d) gt_low += sh.hbef[j][b];
-    (void)nt_scan<kSelThreads>(gt_low, sh.wt, &t2);
-    eq_before[j] = sh.hbef[j][d];
-    sel_before[j] = gtb + t2 + min(eq_before[j], need_eq[j]);
+    theta[j] = sh.theta[j];
+    need_eq[j] = sh.need_eq[j];
+    all_eq[j] = sh.all_eq[j] != 0;
+    eq_before[j] = sh.eq_before[j];
+    sel_before[j] = sh.sel_before[j];
   }
   // emit this segment's selected keys in ascending positions
   constexpr int kOwn = kSeg / kSelThreads;  // own entries per thread
