@@ -408,10 +408,20 @@ topk_extract_kernel(const float *__restrict__ scores, int64_t ld, const int32_t 
     for (int e = 0; e < kBins / kSegThreads; ++e) h12[e * kSegThreads + tid] = a[e];
   }
   lds_sync();
-  // threshold buckets of both outputs (all ones: the output takes every key)
-  uint32_t bk[2] = {0xFFFFFFFFu, 0xFFFFFFFFu}, above, c;
-  if (k0 < n) bk[0] = nt_find<kSegThreads>(h12, kBins, (uint32_t)k0, wt, res, &above, &c);
-  if (k1 > 0 && k1 < n) bk[1] = nt_find<kSegThreads>(h12, kBins, (uint32_t)k1, wt, res, &above, &c);
+  // threshold buckets of both outputs (all ones: the output takes every key),
+  // output j's by wavefront j
+  {
+    const int wave = tid / kWave;
+    if (wave < 2) {
+      const int kj = wave ? k1 : k0;
+      const bool on = wave ? (k1 > 0 && k1 < n) : (k0 < n);
+      uint32_t b = 0xFFFFFFFFu, above, c;
+      if (on) b = wave_find(h12, kBins, (uint32_t)kj, &above, &c);
+      if (tid % kWave == 0) res[wave] = b;
+    }
+    lds_sync();
+  }
+  const uint32_t bk[2] = {res[0], res[1]};
   const int kmax = max(k0, k1);
   const uint32_t b1 = kmax < n ? (k1 > k0 ? bk[1] : bk[0]) : 0u;  // extraction bucket
   uint32_t cnt = 0;
@@ -458,21 +468,15 @@ template <typename SHT, typename Get>
 __device__ uint32_t refine(SHT &sh, uint32_t M, uint32_t need, Get get, uint32_t *need_eq,
                            bool *all_eq, bool have_hist) {
   const int tid = threadIdx.x;
-  auto find = [&](int nb, uint32_t nd) {  // bin of the nd-th largest (highest bins to thread 0)
-    const int per = nb / kThreads;
-    const int top = nb - 1 - tid * per;
-    uint32_t sum = 0;
-    for (int e = 0; e < per; ++e) sum += sh.hist[top - e];
-    uint32_t total;
-    uint32_t run = block_exclusive_scan(sum, sh.wtot, &total);
-    for (int e = 0; e < per; ++e) {
-      const uint32_t c = sh.hist[top - e];
-      if (run < nd && nd <= run + c) {
-        sh.sel_bin = top - e;
-        sh.sel_above = run;
+  auto find = [&](int nb, uint32_t nd) {  // bin of the nd-th largest, by wavefront 0
+    if (tid < kWave) {
+      uint32_t above, c;
+      const uint32_t b = wave_find(sh.hist, nb, nd, &above, &c);
+      if (tid == 0) {
+        sh.sel_bin = b;
+        sh.sel_above = above;
         sh.sel_count = c;
       }
-      run += c;
     }
     lds_sync();
   };
