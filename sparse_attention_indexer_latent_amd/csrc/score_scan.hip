@@ -145,6 +145,22 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
     bv[2] = has_beta ? b4.z : 0.f; bv[3] = has_beta ? b4.w : 0.f;
   };
 
+  // issuers: page b (64 token rows) into stage u % kNst, 32 loads of 1 KB
+  // (two token rows each), issuer i loading pieces 8i .. 8i+7
+  const char *gdata = (const char *)cv.data;
+  const int gi0 = (wave - kCW) * kPerIssuer;
+  auto issue_page = [&](int u, int b) INL {
+    LDS3 char *st = (LDS3 char *)sh.stage[u % kNst];
+    const char *src = gdata + (int64_t)((b >= 0 && b < cv.n_blocks) ? b : 0) * kUnitB;
+#pragma unroll
+    for (int m = 0; m < kPerIssuer; ++m) {
+      const int gi = gi0 + m;
+      const int r = gi * 2 + lane / 32;
+      const int chunk = (lane % 32) ^ (r & kSwz);
+      dma16_to_lds(src + r * kRowB + chunk * 16, (LDS3 void *)(st + gi * 1024));
+    }
+  };
+
   // ---- plan: guess (every query max_len long, query q on sequence q) ------
   // (exact in candidate mode: every query has B slots)
   const int PPQ = ((CAND ? B : max_len) + kTok - 1) / kTok;
@@ -216,20 +232,38 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
       sh.u0 = gu0;
       sh.nu = gnu;
     }
+  } else if (issuer) {
+    // The guessed range's first pages stream while the plan is checked (a
+    // wrong guess waits for them and loads those stages again).  The issuers
+    // make no other loads here, so no wait for the plan's loads holds these.
+    // All block ids first (a wait for one must not wait for pages), and all
+    // kQst pages unconditionally so the loads issue together: past a short
+    // range they fetch a clamped page into a stage nothing reads, and the
+    // waits below, which count only the range's pages, stay conservative.
+    int bid[kQst];
+#pragma unroll
+    for (int u = 0; u < kQst; ++u)
+      bid[u] = cv.block_table[(int64_t)gq * cv.max_blocks + min(gu0 + min(u, max(gnu - 1, 0)), cv.max_blocks - 1)];
+#pragma unroll
+    for (int u = 0; u < kQst; ++u) asm volatile("" : "+v"(bid[u]));  // both loads land here
+#pragma unroll
+    for (int u = 0; u < kQst; ++u) issue_page(u, bid[u]);
   } else {
+    constexpr int kCT = kCW * kWave;  // compute threads
+    static_assert(2 * kCT >= kMaxPages, "two page-table entries per compute thread");
     const int li = min(lane, n_q - 1);
     int len0 = q_len[li], seq0 = q_seq[li];
     if (lane >= n_q) len0 = seq0 = 0;
     int pg[2];
   #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int i = min(tid + k * kThr, max(gnu - 1, 0));
+      const int i = min(tid + k * kCT, max(gnu - 1, 0));
       pg[k] = cv.block_table[(int64_t)gq * cv.max_blocks + min(gu0 + i, cv.max_blocks - 1)];
     }
     load_wb(gq);
   #pragma unroll
     for (int k = 0; k < 2; ++k)
-      if (tid + k * kThr < gnu) sh.page[tid + k * kThr] = pg[k];
+      if (tid + k * kCT < gnu) sh.page[tid + k * kCT] = pg[k];
     if (wave == 0) {
       const bool bad = lane < n_q && (((len0 + kTok - 1) / kTok) != PPQ || seq0 != lane);
       const bool ok = __ballot(bad) == 0ull;
@@ -266,9 +300,11 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
       }
     }
   }
-  // Every wavefront's loads are in, the q~ copy included: the compiler may
-  // sink its own waits for w and beta past the first reads of that copy.
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  // Every loading wavefront's loads are in, the q~ copy included: the
+  // compiler may sink its own waits for w and beta past the first reads of
+  // that copy.  (Issuers of a page scan have only their early pages in
+  // flight and go on.)
+  if (CAND || !issuer) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   lds_barrier();
   if (!sh.ok) {
     // second round trip: this range's page table and, if the query changed,
@@ -285,14 +321,11 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
     lds_barrier();
   }
   const int myq = sh.myq, mylen = sh.mylen, u0 = sh.u0, nu = sh.nu;
-  const char *gdata = (const char *)cv.data;
 
-  // ---- issuers: unit u (page u0 + u) is 32 loads of 1 KB (two token rows
-  // each), issuer i loads pieces 8i .. 8i+7 ------------------------------------
-  const int gi0 = (wave - kCW) * kPerIssuer;
+  // ---- issuers: unit u of the range (page u0 + u, or 64 candidate rows) ----
   auto issue_unit = [&](int u) INL {
-    LDS3 char *st = (LDS3 char *)sh.stage[u % kNst];
     if constexpr (CAND) {
+      LDS3 char *st = (LDS3 char *)sh.stage[u % kNst];
       // every half-wavefront gathers one candidate row (a padding slot reads row 0)
 #pragma unroll
       for (int m = 0; m < kPerIssuer; ++m) {
@@ -303,21 +336,15 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
         dma16_to_lds(gdata + row * kRowB + chunk * 16, (LDS3 void *)(st + gi * 1024));
       }
     } else {
-      int b = sh.page[u];
-      b = (b >= 0 && b < cv.n_blocks) ? b : 0;
-      const char *src = gdata + (int64_t)b * kUnitB;
-#pragma unroll
-      for (int m = 0; m < kPerIssuer; ++m) {
-        const int gi = gi0 + m;
-        const int r = gi * 2 + lane / 32;
-        const int chunk = (lane % 32) ^ (r & kSwz);
-        dma16_to_lds(src + r * kRowB + chunk * 16, (LDS3 void *)(st + gi * 1024));
-      }
+      issue_page(u, sh.page[u]);
     }
   };
-  int issued = min(nu, kQst);  // prologue: units clear of the q~ copy
+  // prologue: units clear of the q~ copy (a page scan whose guess held has
+  // issued them already; after the slow path every load has landed)
+  int issued = (!CAND && sh.ok) ? min(nu, kQst) : 0;
   if (issuer)
-    for (int u = 0; u < issued; ++u) issue_unit(u);
+    for (int u = issued; u < min(nu, kQst); ++u) issue_unit(u);
+  issued = min(nu, kQst);
 
   // ---- compute: A fragments of heads 16 hg .. +15 from the q~ copy ---------
   Frag abf[NT][KB];
