@@ -26,7 +26,7 @@ constexpr int kCap = 6144;
 constexpr int kPer = 8;  // consecutive positions per thread in the emit pass
 
 struct TopkShared {
-  uint32_t hist[kBins];
+  __align__(16) uint32_t hist[kBins];
   uint32_t ckey[kCap];
   int32_t cpos[kCap];
   uint32_t wtot[kWaves];
@@ -343,8 +343,9 @@ __device__ uint32_t nt_find(const uint32_t *hist, int nb, uint32_t nd, uint32_t 
   return b;
 }
 
-// The same search by one wavefront, without barriers (nb a multiple of 64,
-// at most 4096): lane l owns bins top - l*per ... top - l*per - per + 1
+// The same search by one wavefront, without barriers (nb a multiple of 256,
+// at most 4096, hist 16-byte aligned): lane l owns bins top - l*per ...
+// top - l*per - per + 1
 // (highest bins to lane 0) and sums them, reading them rotated by l so the
 // wavefront's reads spread over the LDS banks; a wavefront prefix sum picks
 // the lane holding the nd-th largest key, then every lane takes one of that
@@ -356,7 +357,15 @@ __device__ uint32_t wave_find(const uint32_t *hist, int nb, uint32_t nd, uint32_
   const int per = nb / kWave;
   const int top = nb - 1 - lane * per;
   uint32_t sum = 0;
-  for (int e = 0; e < per; ++e) sum += hist[top - ((e + lane) & (per - 1))];
+  {
+    // 16 bytes at a time, chunk order rotated by lane (bank spread)
+    const uint4 *h4 = (const uint4 *)(hist + top - per + 1);
+    const int nc = per / 4;
+    for (int e = 0; e < nc; ++e) {
+      const uint4 v = h4[(e + lane) & (nc - 1)];
+      sum += (v.x + v.y) + (v.z + v.w);
+    }
+  }
   const uint32_t incl = wave_incl_scan(sum), excl = incl - sum;
   const uint64_t hit = __ballot(excl < nd && nd <= incl);
   const int L = hit ? __ffsll((unsigned long long)hit) - 1 : kWave - 1;
@@ -382,7 +391,7 @@ topk_extract_kernel(const float *__restrict__ scores, int64_t ld, const int32_t 
                     int k0, int k1, MultiWs m) {
   __shared__ uint32_t wt[kSegThreads / kWave];
   __shared__ uint32_t res[4];
-  __shared__ uint32_t h12[kBins];
+  __shared__ __align__(16) uint32_t h12[kBins];
   const int row = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
   const int n = valid_len[row];
   const int p0 = seg * kSeg;
@@ -634,11 +643,11 @@ struct FinOut {
 constexpr int kSelThreads = 512;
 
 struct SelShared {
-  uint32_t h12[kBins];     // the row's histograms, copied in one round trip
-  uint32_t h10[2][1024];
+  __align__(16) uint32_t h12[kBins];  // the row's histograms, copied in one round trip
+  __align__(16) uint32_t h10[2][1024];
   uint32_t seg_off[kMaxSegs + 1];
-  uint32_t hlow[2][1024];  // low 10 bits of the keys sharing the 22-bit prefix: whole row
-  uint32_t hbef[2][1024];  // ... in segments before this one
+  __align__(16) uint32_t hlow[2][1024];  // low 10 bits of the keys sharing the 22-bit prefix: whole row
+  __align__(16) uint32_t hbef[2][1024];  // ... in segments before this one
   uint32_t wt[kSelThreads / kWave];
   uint32_t pre22[2], need[2], gtb[2], theta[2], need_eq[2], all_eq[2], sel_before[2], eq_before[2];
 };
@@ -878,8 +887,8 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
 constexpr int kLdsRow = 16384;
 
 struct LdsRowShared {
-  uint32_t key[kLdsRow];
-  uint32_t hist[kBins];
+  __align__(16) uint32_t key[kLdsRow];
+  __align__(16) uint32_t hist[kBins];
   uint32_t small[4096];
   uint32_t wtot[kWaves];
   uint32_t sel_bin, sel_above, sel_count, n_small;
