@@ -880,7 +880,7 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
 }
 
 // ---------------------------------------------------------------------------
-// Rows of at most kLdsRow elements (e.g. a follower's candidate scores): one
+// Rows of 8193 .. kLdsRow elements (longer candidate lists): one
 // workgroup per row keeps the whole row's keys in LDS, so the three radix
 // passes and the ordered emit touch global memory once.
 // ---------------------------------------------------------------------------
@@ -938,6 +938,189 @@ topk_lds_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
   bool all_eq = true;
   const uint32_t theta = refine(sh, (uint32_t)n, (uint32_t)k, get, &need_eq, &all_eq, false);
   emit(sh, (uint32_t)n, theta, need_eq, all_eq, false, get, idm, u, oi, ov, m);
+}
+
+// ---------------------------------------------------------------------------
+// Rows of at most 8192 scores (a follower layer's rescored candidates): one
+// workgroup of 1024 threads per row, eight consecutive positions per thread
+// held in registers together with their ids (both loaded up front), so LDS
+// holds only histograms and every pass re-reads registers:
+//   A. histogram of key bits 31..21 in 8 interleaved copies (lane % 8 picks
+//      one: a candidate set's scores crowd into few bins, and lanes of one
+//      atomic that hit the same bin then mostly hit different words), merged,
+//      and the bin b1 of the k-th largest key found by one wavefront;
+//   B. among keys in b1, histogram of bits 20..10; C. among keys matching
+//      both, of bits 9..0: theta, and how many keys equal to it are taken;
+//   D. the equal keys taken are the lowest positions, so one block scan of
+//      the per-thread counts of keys above theta and equal to it (two 16-bit
+//      halves of one word) gives every thread its output offset.
+// ---------------------------------------------------------------------------
+constexpr int kR8Per = 8;
+constexpr int kR8Max = kThreads * kR8Per;  // 8192
+constexpr int kR8Bins = 2048;
+constexpr int kR8Copies = 8;
+
+struct R8Shared {
+  __align__(16) uint32_t hA[kR8Bins * kR8Copies];  // [bin][copy]
+  __align__(16) uint32_t hM[kR8Bins];
+  __align__(16) uint32_t hB[kR8Bins];
+  __align__(16) uint32_t hC[1024];
+  uint32_t wtot[kWaves];
+  uint32_t sel_bin, sel_above, sel_count;
+};
+
+__global__ void __launch_bounds__(kThreads)
+topk_r8_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ valid_len,
+               int const_len, const int32_t *__restrict__ ids, int64_t ids_ld, int ids_rows, int k,
+               int32_t *__restrict__ out_idx, float *__restrict__ out_val) {
+  __shared__ R8Shared sh;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int n = min(valid_len ? valid_len[row] : const_len, kR8Max);
+  const float *u = scores + (int64_t)row * ld;
+  const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
+  int32_t *oi = out_idx + (int64_t)row * k;
+  float *ov = out_val ? out_val + (int64_t)row * k : nullptr;
+  const int m = min(k, n);
+  for (int j = m + tid; j < k; j += kThreads) {
+    oi[j] = -1;
+    if (ov) ov[j] = -INFINITY;
+  }
+  if (n <= k) {
+    for (int p = tid; p < n; p += kThreads) {
+      oi[p] = idm ? idm[p] : p;
+      if (ov) ov[p] = u[p];
+    }
+    return;
+  }
+  // Buffer loads bounded by the row's valid length never read past it.
+  const int p0 = kR8Per * tid;
+  const int nv = min(kR8Per, max(0, n - p0));  // this thread's valid entries (a prefix)
+  float v[kR8Per];
+  int32_t id[kR8Per];
+  {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(u), 0, n * 4, 0x00020000);
+    if ((reinterpret_cast<uintptr_t>(u) & 15) == 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, (p0 + 4 * h) * 4, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * h + j] = __uint_as_float(x[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kR8Per; ++j)
+        v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (p0 + j) * 4, 0, 0));
+    }
+    if (idm) {
+      const __amdgpu_buffer_rsrc_t ri =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(idm), 0, n * 4, 0x00020000);
+      if ((reinterpret_cast<uintptr_t>(idm) & 15) == 0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const auto x = __builtin_amdgcn_raw_buffer_load_b128(ri, (p0 + 4 * h) * 4, 0, 0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) id[4 * h + j] = (int32_t)x[j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kR8Per; ++j)
+          id[j] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (p0 + j) * 4, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kR8Per; ++j) id[j] = p0 + j;
+    }
+  }
+  // clear the histograms while the loads are in flight
+  {
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < kR8Bins * kR8Copies / 4 / kThreads; ++i)
+      reinterpret_cast<uint4 *>(sh.hA)[tid + i * kThreads] = z;
+    if (tid < kR8Bins / 4) reinterpret_cast<uint4 *>(sh.hB)[tid] = z;
+    if (tid < 1024 / 4) reinterpret_cast<uint4 *>(sh.hC)[tid] = z;
+  }
+  uint32_t key[kR8Per];
+#pragma unroll
+  for (int j = 0; j < kR8Per; ++j) key[j] = score_key(v[j]);
+  auto find = [&](const uint32_t *h, int nb, uint32_t nd) {
+    if (tid < kWave) {
+      uint32_t above, c;
+      const uint32_t b = wave_find(h, nb, nd, &above, &c);
+      if (tid == 0) {
+        sh.sel_bin = b;
+        sh.sel_above = above;
+        sh.sel_count = c;
+      }
+    }
+    lds_sync();
+  };
+  lds_sync();
+  // A
+  {
+    uint32_t *h = sh.hA + (lane & (kR8Copies - 1));
+#pragma unroll
+    for (int j = 0; j < kR8Per; ++j)
+      if (j < nv) atomicAdd(&h[(key[j] >> 21) * kR8Copies], 1u);
+  }
+  lds_sync();
+  {
+    const uint4 *c = reinterpret_cast<const uint4 *>(sh.hA) + 4 * tid;  // bins 2 tid, 2 tid + 1
+    const uint4 a = c[0], b = c[1], d = c[2], e = c[3];
+    reinterpret_cast<uint2 *>(sh.hM)[tid] =
+        make_uint2((a.x + a.y) + (a.z + a.w) + (b.x + b.y) + (b.z + b.w),
+                   (d.x + d.y) + (d.z + d.w) + (e.x + e.y) + (e.z + e.w));
+  }
+  lds_sync();
+  find(sh.hM, kR8Bins, (uint32_t)k);
+  const uint32_t b1 = sh.sel_bin;
+  uint32_t need = (uint32_t)k - sh.sel_above;
+  // B
+#pragma unroll
+  for (int j = 0; j < kR8Per; ++j)
+    if (j < nv && (key[j] >> 21) == b1) atomicAdd(&sh.hB[(key[j] >> 10) & 2047u], 1u);
+  lds_sync();
+  find(sh.hB, kR8Bins, need);
+  const uint32_t p22 = (b1 << 11) | sh.sel_bin;
+  need -= sh.sel_above;
+  // C
+#pragma unroll
+  for (int j = 0; j < kR8Per; ++j)
+    if (j < nv && (key[j] >> 10) == p22) atomicAdd(&sh.hC[key[j] & 1023u], 1u);
+  lds_sync();
+  find(sh.hC, 1024, need);
+  const uint32_t theta = (p22 << 10) | sh.sel_bin;
+  need -= sh.sel_above;  // keys equal to theta to take (lowest positions), >= 1
+  // D
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < kR8Per; ++j) {
+    gt += (j < nv && key[j] > theta) ? 1u : 0u;
+    eq += (j < nv && key[j] == theta) ? 1u : 0u;
+  }
+  const uint32_t packed = gt | (eq << 16);  // each half bounded by 8192
+  const uint32_t incl = wave_incl_scan(packed);
+  if (lane == kWave - 1) sh.wtot[wave] = incl;
+  lds_sync();
+  uint32_t before = incl - packed;
+#pragma unroll
+  for (int w2 = 0; w2 < kWaves; ++w2) before += w2 < wave ? sh.wtot[w2] : 0u;
+  uint32_t eq_b = before >> 16;
+  uint32_t pos = (before & 0xFFFFu) + min(eq_b, need);
+#pragma unroll
+  for (int j = 0; j < kR8Per; ++j) {
+    const bool is_eq = j < nv && key[j] == theta;
+    const bool s = j < nv && (key[j] > theta || (is_eq && eq_b < need));
+    if (s) {
+      if (pos < (uint32_t)m) {
+        oi[pos] = id[j];
+        if (ov) ov[pos] = v[j];
+      }
+      ++pos;
+    }
+    eq_b += is_eq ? 1u : 0u;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1201,6 +1384,11 @@ size_t topk_ws_bytes(int n_rows, int max_len, int) {
 hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
                        const int32_t *ids, int64_t ids_ld, int ids_rows, int max_len, int k, int32_t *out_idx,
                        float *out_val, void *ws, hipStream_t st) {
+  if (max_len <= kR8Max) {
+    topk_r8_kernel<<<n_rows, kThreads, 0, st>>>(scores, ld, valid_len, max_len, ids, ids_ld, ids_rows, k,
+                                                out_idx, out_val);
+    return hipGetLastError();
+  }
   if (max_len <= kLdsRow) {
     const size_t lds = sizeof(LdsRowShared);
     static bool attr_lds = false;

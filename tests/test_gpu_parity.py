@@ -401,9 +401,11 @@ def test_hs_anchor_select_nested_exact(B, k):
         assert np.array_equal(sel[i], O.pad(O.topk(row, k), k)), i
 
 
-@pytest.mark.parametrize("n", [16384, 9000])
+@pytest.mark.parametrize("n", [16384, 9000, 8192, 5001])
 def test_topk_exact_short_rows_in_lds(n):
-    """Rows of at most 16K elements take the LDS-resident path."""
+    """Rows of at most 16K elements take the LDS-resident path, rows of at
+    most 8,192 the register-resident one (5,001: an odd row stride, so rows
+    are not 16-byte aligned)."""
     say(f"topk exact, LDS-resident rows n={n}")
     rng = np.random.default_rng(n)
     rows = [rng.standard_normal(n), np.round(rng.standard_normal(n), 1), np.zeros(n),
@@ -428,11 +430,13 @@ def test_topk_bucket_overflow_path():
 
 # --------------------------------------------------------------------- HS ---
 
-@pytest.mark.parametrize("dtype,H,r", [("bf16", 64, 256), ("fp32", 8, 32), ("fp8", 64, 256)])
-def test_hs_select_matches_oracle(dtype, H, r):
-    say(f"hs_select dtype={dtype} H={H} r={r}")
+@pytest.mark.parametrize("dtype,H,r,B", [("bf16", 64, 256, 512), ("fp32", 8, 32, 301),
+                                         ("fp8", 64, 256, 512)])
+def test_hs_select_matches_oracle(dtype, H, r, B):
+    """B = 301: candidate lists at an odd stride (unaligned id rows)."""
+    say(f"hs_select dtype={dtype} H={H} r={r} B={B}")
     wl = W.small_decode(6, n_seq=3, lens=[50, 1500, 4000], H=H, r=r, d_I=128 if H == 64 else 16,
-                        G=4, k=64, B=512, cache_dtype=dtype, plant=20, factor=3.0)
+                        G=4, k=64, B=B, cache_dtype=dtype, plant=20, factor=3.0)
     dw = DeviceWorkload(wl, hold_last=False)
     dw.hs_step(append=False, keep_scores=True)
     torch.cuda.synchronize()
