@@ -947,8 +947,9 @@ topk_lds_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
 // holds only histograms and every pass re-reads registers:
 //   A. histogram of key bits 31..21 in 8 interleaved copies (lane % 8 picks
 //      one: a candidate set's scores crowd into few bins, and lanes of one
-//      atomic that hit the same bin then mostly hit different words), merged,
-//      and the bin b1 of the k-th largest key found by one wavefront;
+//      atomic that hit the same bin then mostly hit different words); each
+//      thread merges two bins and a block scan finds the bin b1 of the k-th
+//      largest key (likewise in B and C);
 //   B. among keys in b1, histogram of bits 20..10; C. among keys matching
 //      both, of bits 9..0: theta, and how many keys equal to it are taken;
 //   D. the equal keys taken are the lowest positions, so one block scan of
@@ -962,12 +963,42 @@ constexpr int kR8Copies = 8;
 
 struct R8Shared {
   __align__(16) uint32_t hA[kR8Bins * kR8Copies];  // [bin][copy]
-  __align__(16) uint32_t hM[kR8Bins];
   __align__(16) uint32_t hB[kR8Bins];
   __align__(16) uint32_t hC[1024];
   uint32_t wtot[kWaves];
-  uint32_t sel_bin, sel_above, sel_count;
+  uint32_t sel[3];  // bin, count above it, its own count
 };
+
+// Block-wide search for the bin of the nd-th largest key: thread t holds the
+// counts c[e] of bins top - e, top = nb - 1 - PER t (highest bins to thread
+// 0); one block scan of the per-thread sums, then the thread whose bins hold
+// the nd-th key publishes (bin, count above it, its count) in sel.  nd must
+// be at least 1 and at most the histogram total.
+template <int PER>
+__device__ __forceinline__ void r8_find(const uint32_t (&c)[PER], int nb, uint32_t nd, uint32_t *wtot,
+                                        uint32_t *sel) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  uint32_t s = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) s += c[e];
+  const uint32_t incl = wave_incl_scan(s);
+  if (lane == kWave - 1) wtot[wave] = incl;
+  lds_sync();
+  uint32_t run = incl - s;
+#pragma unroll
+  for (int w2 = 0; w2 < kWaves; ++w2) run += w2 < wave ? wtot[w2] : 0u;
+  const int top = nb - 1 - PER * tid;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    if (run < nd && nd <= run + c[e]) {
+      sel[0] = (uint32_t)(top - e);
+      sel[1] = run;
+      sel[2] = c[e];
+    }
+    run += c[e];
+  }
+  lds_sync();
+}
 
 __global__ void __launch_bounds__(kThreads)
 topk_r8_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ valid_len,
@@ -975,31 +1006,17 @@ topk_r8_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__re
                int32_t *__restrict__ out_idx, float *__restrict__ out_val) {
   __shared__ R8Shared sh;
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int n = min(valid_len ? valid_len[row] : const_len, kR8Max);
   const float *u = scores + (int64_t)row * ld;
   const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
-  int32_t *oi = out_idx + (int64_t)row * k;
-  float *ov = out_val ? out_val + (int64_t)row * k : nullptr;
-  const int m = min(k, n);
-  for (int j = m + tid; j < k; j += kThreads) {
-    oi[j] = -1;
-    if (ov) ov[j] = -INFINITY;
-  }
-  if (n <= k) {
-    for (int p = tid; p < n; p += kThreads) {
-      oi[p] = idm ? idm[p] : p;
-      if (ov) ov[p] = u[p];
-    }
-    return;
-  }
-  // Buffer loads bounded by the row's valid length never read past it.
+  const int cap = min(const_len, kR8Max);  // the row's allocated length bounds the loads
+  // Scores and ids are loaded before the row's valid length is known (buffer
+  // loads bounded by the allocated length), so their latency overlaps its.
   const int p0 = kR8Per * tid;
-  const int nv = min(kR8Per, max(0, n - p0));  // this thread's valid entries (a prefix)
   float v[kR8Per];
   int32_t id[kR8Per];
   {
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(u), 0, n * 4, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(u), 0, cap * 4, 0x00020000);
     if ((reinterpret_cast<uintptr_t>(u) & 15) == 0) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -1014,7 +1031,7 @@ topk_r8_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__re
     }
     if (idm) {
       const __amdgpu_buffer_rsrc_t ri =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(idm), 0, n * 4, 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(idm), 0, cap * 4, 0x00020000);
       if ((reinterpret_cast<uintptr_t>(idm) & 15) == 0) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -1032,6 +1049,22 @@ topk_r8_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__re
       for (int j = 0; j < kR8Per; ++j) id[j] = p0 + j;
     }
   }
+  const int n = valid_len ? min(valid_len[row], cap) : cap;
+  int32_t *oi = out_idx + (int64_t)row * k;
+  float *ov = out_val ? out_val + (int64_t)row * k : nullptr;
+  const int m = min(k, n);
+  for (int j = m + tid; j < k; j += kThreads) {
+    oi[j] = -1;
+    if (ov) ov[j] = -INFINITY;
+  }
+  if (n <= k) {
+    for (int p = tid; p < n; p += kThreads) {
+      oi[p] = idm ? idm[p] : p;
+      if (ov) ov[p] = u[p];
+    }
+    return;
+  }
+  const int nv = min(kR8Per, max(0, n - p0));  // this thread's valid entries (a prefix)
   // clear the histograms while the loads are in flight
   {
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
@@ -1044,20 +1077,8 @@ topk_r8_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__re
   uint32_t key[kR8Per];
 #pragma unroll
   for (int j = 0; j < kR8Per; ++j) key[j] = score_key(v[j]);
-  auto find = [&](const uint32_t *h, int nb, uint32_t nd) {
-    if (tid < kWave) {
-      uint32_t above, c;
-      const uint32_t b = wave_find(h, nb, nd, &above, &c);
-      if (tid == 0) {
-        sh.sel_bin = b;
-        sh.sel_above = above;
-        sh.sel_count = c;
-      }
-    }
-    lds_sync();
-  };
   lds_sync();
-  // A
+  // A: thread t then merges the copies of bins 2047 - 2t and 2046 - 2t
   {
     uint32_t *h = sh.hA + (lane & (kR8Copies - 1));
 #pragma unroll
@@ -1065,33 +1086,39 @@ topk_r8_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__re
       if (j < nv) atomicAdd(&h[(key[j] >> 21) * kR8Copies], 1u);
   }
   lds_sync();
+  uint32_t cA[2];
   {
-    const uint4 *c = reinterpret_cast<const uint4 *>(sh.hA) + 4 * tid;  // bins 2 tid, 2 tid + 1
-    const uint4 a = c[0], b = c[1], d = c[2], e = c[3];
-    reinterpret_cast<uint2 *>(sh.hM)[tid] =
-        make_uint2((a.x + a.y) + (a.z + a.w) + (b.x + b.y) + (b.z + b.w),
-                   (d.x + d.y) + (d.z + d.w) + (e.x + e.y) + (e.z + e.w));
+    const uint4 *c = reinterpret_cast<const uint4 *>(sh.hA) + 4 * (kR8Bins / 2 - 1 - tid);
+    const uint4 a = c[0], b = c[1], d = c[2], e = c[3];  // bin 2046 - 2t, then 2047 - 2t
+    cA[1] = (a.x + a.y) + (a.z + a.w) + (b.x + b.y) + (b.z + b.w);
+    cA[0] = (d.x + d.y) + (d.z + d.w) + (e.x + e.y) + (e.z + e.w);
   }
-  lds_sync();
-  find(sh.hM, kR8Bins, (uint32_t)k);
-  const uint32_t b1 = sh.sel_bin;
-  uint32_t need = (uint32_t)k - sh.sel_above;
+  r8_find<2>(cA, kR8Bins, (uint32_t)k, sh.wtot, sh.sel);
+  const uint32_t b1 = sh.sel[0];
+  uint32_t need = (uint32_t)k - sh.sel[1];
   // B
 #pragma unroll
   for (int j = 0; j < kR8Per; ++j)
     if (j < nv && (key[j] >> 21) == b1) atomicAdd(&sh.hB[(key[j] >> 10) & 2047u], 1u);
   lds_sync();
-  find(sh.hB, kR8Bins, need);
-  const uint32_t p22 = (b1 << 11) | sh.sel_bin;
-  need -= sh.sel_above;
+  uint32_t cB[2];
+  {
+    const uint2 x = reinterpret_cast<const uint2 *>(sh.hB)[kR8Bins / 2 - 1 - tid];
+    cB[0] = x.y;
+    cB[1] = x.x;
+  }
+  r8_find<2>(cB, kR8Bins, need, sh.wtot, sh.sel);
+  const uint32_t p22 = (b1 << 11) | sh.sel[0];
+  need -= sh.sel[1];
   // C
 #pragma unroll
   for (int j = 0; j < kR8Per; ++j)
     if (j < nv && (key[j] >> 10) == p22) atomicAdd(&sh.hC[key[j] & 1023u], 1u);
   lds_sync();
-  find(sh.hC, 1024, need);
-  const uint32_t theta = (p22 << 10) | sh.sel_bin;
-  need -= sh.sel_above;  // keys equal to theta to take (lowest positions), >= 1
+  uint32_t cC[1] = {sh.hC[1023 - tid]};
+  r8_find<1>(cC, 1024, need, sh.wtot, sh.sel);
+  const uint32_t theta = (p22 << 10) | sh.sel[0];
+  need -= sh.sel[1];  // keys equal to theta to take (lowest positions), >= 1
   // D
   uint32_t gt = 0, eq = 0;
 #pragma unroll
