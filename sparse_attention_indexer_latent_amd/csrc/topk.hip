@@ -380,10 +380,9 @@ __device__ uint32_t wave_find(const uint32_t *hist, int nb, uint32_t nd, uint32_
   return (uint32_t)(topL - t);
 }
 
+// Sum over the wavefront, in every lane (DPP scan, then lane 63's total).
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(v), kWave - 1);
 }
 
 __global__ void __launch_bounds__(kSegThreads)
@@ -455,6 +454,9 @@ topk_extract_kernel(const float *__restrict__ scores, int64_t ld, const int32_t 
     for (int j = 0; j < 2; ++j)
       if (p < n && (key[e] >> 20) == bk[j]) atomicAdd(&h10[j * 1024 + ((key[e] >> 10) & 1023u)], 1u);
   }
+  // zeros up to the next multiple of 256 slots, so the select step reads the
+  // list in whole 16-byte-per-lane rows without masks (key 0 is no score's)
+  for (uint32_t e = tot + tid; e < ((tot + 255u) & ~255u); e += kSegThreads) m.lkey[off + e] = 0u;
   if (tid == 0) m.seg_cnt[(int64_t)row * m.S + seg] = tot;
 }
 
@@ -658,7 +660,40 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
                    int64_t ids_ld, int ids_rows, FinOut o0, FinOut o1, int n_out, MultiWs m) {
   __shared__ SelShared sh;
   const int row = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave;
+  constexpr int NW = kSelThreads / kWave;
+  constexpr int kOwn = kSeg / kSelThreads;  // own entries per thread
+  // Every load whose address depends on no other load is issued here, before
+  // any result is used: the row's valid length and histograms, the segments'
+  // key counts, this segment's extracted keys and positions, and the first
+  // 256 extracted keys of the 8 segments this wavefront scans first.  Each
+  // segment owns kSeg slots, so these are in bounds whatever the counts.
   const int n = valid_len[row];
+  uint32_t a[kBins / kSelThreads], b[2 * 1024 / kSelThreads];
+  {
+    const uint32_t *g12 = m.hist + (int64_t)row * kBins;
+    const uint32_t *g10 = m.h10 + (int64_t)row * 2 * 1024;
+#pragma unroll
+    for (int e = 0; e < kBins / kSelThreads; ++e) a[e] = g12[e * kSelThreads + tid];
+#pragma unroll
+    for (int e = 0; e < 2 * 1024 / kSelThreads; ++e) b[e] = g10[e * kSelThreads + tid];
+  }
+  const uint32_t *cnt = m.seg_cnt + (int64_t)row * m.S;
+  const uint32_t c_first = tid < m.S ? cnt[tid] : 0u;
+  const int64_t own = ((int64_t)row * m.S + seg) * kSeg;
+  const uint32_t i0 = tid * kOwn;
+  static_assert(kOwn == 4, "own entries load as one 16-byte vector");
+  const uint4 ek4 = *reinterpret_cast<const uint4 *>(m.lkey + own + i0);
+  const int4 ep4 = *reinterpret_cast<const int4 *>(m.lpos + own + i0);
+  const uint32_t *lkey = m.lkey + (int64_t)row * m.S * kSeg;
+  constexpr int kPF = 8;  // segments wave + NW u, u < kPF: their first 256 keys, 4 per lane
+  uint4 pk[kPF];
+#pragma unroll
+  for (int v = 0; v < kPF; ++v) {
+    const int sg = wave + NW * v;
+    pk[v] = sg < m.S ? *reinterpret_cast<const uint4 *>(lkey + (int64_t)sg * kSeg + 4 * lane)
+                     : make_uint4(0u, 0u, 0u, 0u);
+  }
   const FinOut out[2] = {o0, o1};
   if (seg == 0) {  // padding of the outputs
 #pragma unroll
@@ -674,40 +709,27 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
   if (n <= 0 || seg >= S) return;  // uniform per workgroup
   const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
   const float *u = scores + (int64_t)row * ld;
-  {
-    // the row histograms into LDS, all loads issued before any is used
-    const uint32_t *g12 = m.hist + (int64_t)row * kBins;
-    const uint32_t *g10 = m.h10 + (int64_t)row * 2 * 1024;
-    uint32_t a[kBins / kSelThreads], b[2 * 1024 / kSelThreads];
 #pragma unroll
-    for (int e = 0; e < kBins / kSelThreads; ++e) a[e] = g12[e * kSelThreads + tid];
+  for (int e = 0; e < kBins / kSelThreads; ++e) sh.h12[e * kSelThreads + tid] = a[e];
 #pragma unroll
-    for (int e = 0; e < 2 * 1024 / kSelThreads; ++e) b[e] = g10[e * kSelThreads + tid];
-#pragma unroll
-    for (int e = 0; e < kBins / kSelThreads; ++e) sh.h12[e * kSelThreads + tid] = a[e];
-#pragma unroll
-    for (int e = 0; e < 2 * 1024 / kSelThreads; ++e) (&sh.h10[0][0])[e * kSelThreads + tid] = b[e];
-  }
+  for (int e = 0; e < 2 * 1024 / kSelThreads; ++e) (&sh.h10[0][0])[e * kSelThreads + tid] = b[e];
   // offsets of the segments' lists in the row's flattened extracted keys
-  const uint32_t *cnt = m.seg_cnt + (int64_t)row * m.S;
   uint32_t carry = 0;
-  for (int b = 0; b < S; b += kSelThreads) {
-    const uint32_t c = (b + tid < S) ? cnt[b + tid] : 0u;
+  for (int b0 = 0; b0 < S; b0 += kSelThreads) {
+    const uint32_t c = (b0 + tid < S) ? (b0 == 0 ? c_first : cnt[b0 + tid]) : 0u;
     uint32_t tot;
     const uint32_t ex = nt_scan<kSelThreads>(c, sh.wt, &tot);
-    if (b + tid < S) sh.seg_off[b + tid] = carry + ex;
+    if (b0 + tid < S) sh.seg_off[b0 + tid] = carry + ex;
     carry += tot;
   }
   if (tid == 0) sh.seg_off[S] = carry;
-  for (int b = tid; b < 2 * 1024; b += kSelThreads) {
-    (&sh.hlow[0][0])[b] = 0;
-    (&sh.hbef[0][0])[b] = 0;
+  for (int b0 = tid; b0 < 2 * 1024; b0 += kSelThreads) {
+    (&sh.hlow[0][0])[b0] = 0;
+    (&sh.hbef[0][0])[b0] = 0;
   }
   lds_sync();
   if (tid < 2) sh.gtb[tid] = 0;
   // thresholds: top 12 bits, then the next 10; output j's by wavefront j
-  const int lane = tid % kWave, wave = tid / kWave;
-  constexpr int NW = kSelThreads / kWave;
   bool act[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) act[j] = j < n_out && out[j].k < n;  // else every key is taken
@@ -735,57 +757,58 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
       need[j] = sh.need[j];
     }
   // One pass over the row's extracted keys, one wavefront per segment, four
-  // segments at a time with their first 256 keys loaded before any is used:
-  // the low 10 bits of the keys sharing each 22-bit prefix, over the row and
-  // over the segments before this one, and the keys above it before this one.
-  const uint32_t *lkey = m.lkey + (int64_t)row * m.S * kSeg;
+  // keys per lane per 16-byte load (the lists are zero-padded to whole
+  // 256-key rows; key 0 matches no prefix): the low 10 bits of the keys
+  // sharing each 22-bit prefix, over the row and over the segments before
+  // this one, and the keys above it before this one (per-lane counts, summed
+  // once at the end).
   const uint32_t my0 = sh.seg_off[seg];
-  uint32_t gt_bef[2] = {0, 0};  // per wavefront, the same in every lane
-  if (act[0] || act[1]) {
-    for (int t0 = wave; t0 < S; t0 += NW * 4) {
-      int sgs[4];
-      uint32_t cn[4], key[4][4];
+  uint32_t gtc[2] = {0, 0};
+  auto visit4 = [&](const uint4 kv, bool before) __attribute__((always_inline)) {
+    const uint32_t ks[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        sgs[u] = t0 + NW * u;
-        cn[u] = sgs[u] < S ? sh.seg_off[sgs[u] + 1] - sh.seg_off[sgs[u]] : 0u;
+    for (int j = 0; j < 2; ++j) {
+      if (!act[j]) continue;  // uniform
+      const uint32_t P = pre22[j];
+      uint32_t g = 0;
+      bool hit = false;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t h = ks[t] >> 10;
+        g += h > P ? 1u : 0u;
+        hit |= h == P;
       }
+      if (before) gtc[j] += g;
+      if (hit) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t e = c * kWave + lane;
-          key[u][c] = e < cn[u] ? lkey[(int64_t)sgs[u] * kSeg + e] : 0u;
-        }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bool before = sgs[u] < seg;  // wave-uniform, as is sgs[u] < S
-        auto visit = [&](uint32_t k, bool valid) __attribute__((always_inline)) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const uint32_t hi22 = k >> 10;
-            if (act[j] && valid && hi22 == pre22[j]) {
-              atomicAdd(&sh.hlow[j][k & 1023u], 1u);
-              if (before) atomicAdd(&sh.hbef[j][k & 1023u], 1u);
-            }
-            const uint32_t g = (uint32_t)__popcll(__ballot(act[j] && before && valid && hi22 > pre22[j]));
-            gt_bef[j] += g;  // the same in every lane
+        for (int t = 0; t < 4; ++t)
+          if ((ks[t] >> 10) == P) {
+            atomicAdd(&sh.hlow[j][ks[t] & 1023u], 1u);
+            if (before) atomicAdd(&sh.hbef[j][ks[t] & 1023u], 1u);
           }
-        };
-        if (sgs[u] < S) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) visit(key[u][c], (uint32_t)(c * kWave + lane) < cn[u]);
-          for (uint32_t e0 = 4 * kWave; e0 < cn[u]; e0 += kWave) {  // segments with more keys
-            const uint32_t e = e0 + lane;
-            visit(e < cn[u] ? lkey[(int64_t)sgs[u] * kSeg + e] : 0u, e < cn[u]);
-          }
-        }
       }
     }
+  };
+  auto seg_pass = [&](int sg, const uint4 first) __attribute__((always_inline)) {
+    if (sg >= S) return;  // uniform
+    const bool before = sg < seg;
+    const uint32_t cn = sh.seg_off[sg + 1] - sh.seg_off[sg];
+    if (cn == 0) return;
+    visit4(first, before);
+    for (uint32_t e0 = 256; e0 < cn; e0 += 256)  // lists longer than 256 keys
+      visit4(*reinterpret_cast<const uint4 *>(lkey + (int64_t)sg * kSeg + e0 + 4 * lane), before);
+  };
+  if (act[0] || act[1]) {
+#pragma unroll
+    for (int v = 0; v < kPF; ++v) seg_pass(wave + NW * v, pk[v]);
+    for (int sg = wave + NW * kPF; sg < S; sg += NW)
+      seg_pass(sg, *reinterpret_cast<const uint4 *>(lkey + (int64_t)sg * kSeg + 4 * lane));
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    if (act[j] && lane == 0 && gt_bef[j]) atomicAdd(&sh.gtb[j], gt_bef[j]);
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t g = act[j] ? wave_sum_u32(gtc[j]) : 0u;
+    if (lane == 0 && g) atomicAdd(&sh.gtb[j], g);
+  }
   lds_sync();
   // exact thresholds and this segment's offsets, output j's by wavefront j
   if (wave < 2 && act_w) {
@@ -794,8 +817,8 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
     uint32_t above, c;
     const uint32_t d = wave_find(sh.hlow[j], 1024, need_w, &above, &c);
     uint32_t gl = 0;  // keys of the 22-bit prefix above theta, before this segment
-    for (int b = lane; b < 1024; b += kWave)
-      if ((uint32_t)b > d) gl += sh.hbef[j][b];
+    for (int b0 = lane; b0 < 1024; b0 += kWave)
+      if ((uint32_t)b0 > d) gl += sh.hbef[j][b0];
     gl = wave_sum_u32(gl);
     if (lane == 0) {
       const uint32_t ne = need_w - above, eb = sh.hbef[j][d];
@@ -820,17 +843,9 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
     sel_before[j] = sh.sel_before[j];
   }
   // emit this segment's selected keys in ascending positions
-  constexpr int kOwn = kSeg / kSelThreads;  // own entries per thread
   const uint32_t mc = sh.seg_off[seg + 1] - my0;
-  const int64_t own = ((int64_t)row * m.S + seg) * kSeg;
-  const uint32_t i0 = tid * kOwn;
-  uint32_t ek[kOwn];
-  int32_t ep[kOwn];
-#pragma unroll
-  for (int t = 0; t < kOwn; ++t) {
-    ek[t] = i0 + t < mc ? m.lkey[own + i0 + t] : 0u;
-    ep[t] = i0 + t < mc ? m.lpos[own + i0 + t] : 0;
-  }
+  const uint32_t ek[kOwn] = {ek4.x, ek4.y, ek4.z, ek4.w};
+  const int32_t ep[kOwn] = {ep4.x, ep4.y, ep4.z, ep4.w};
   uint32_t eqb[2] = {eq_before[0], eq_before[1]};
   if ((act[0] && !all_eq[0]) || (act[1] && !all_eq[1])) {
     uint32_t c = 0;
