@@ -5,19 +5,24 @@
 // For a decoder shared by the heads this is one small GEMM,
 // [n_q*H x d_I] x [d_I x r]; with per-head decoders it is one GEMM per head
 // over that head's queries.  Several layers (each with its own decoder) go
-// in one launch: blockIdx.z enumerates (layer, head).  Each workgroup computes a 32 x 32 output tile in
-// fp32 from LDS-staged 32 x 128 slices of q and Dt (each thread 2 x 2
-// outputs); a decode layer (4 x 64 heads, r = 256) spreads over 64 workgroups,
-// so the call costs about one load round trip.  The work is applied once per
-// new query instead of once per cached token.
+// in one launch: blockIdx.z enumerates (layer, head).  Both operands are
+// contiguous along d, and the GEMM runs on the fp32 matrix cores
+// (v_mfma_f32_16x16x4f32) with no LDS: a workgroup computes a 32 x 32
+// output block, one wavefront per 16 x 16 tile.  The instruction takes, for
+// each of its 4 k slots g, A[i][g] from lane i + 16 g and B[g][j] from lane
+// j + 16 g; slot g is given the contiguous quarter d in [32 g, 32 g + 32) of
+// each 128-wide slice of d, so every lane streams its own row of q and of Dt
+// with 16-byte loads straight into registers, and step t of the chain pairs
+// d = 32 g + t across the slots.  The work is applied once per new query
+// instead of once per cached token.
 #include "li_device.h"
 #include "li_internal.h"
 
 namespace li {
 namespace {
 
-constexpr int kT = 32;   // tile rows and columns
-constexpr int kKC = 128;  // d slice per LDS stage (d_I <= 128 takes one round trip)
+constexpr int kT = 32;    // output block rows and columns per workgroup
+constexpr int kKC = 128;  // d per slice: 32 per k slot
 
 // Rows of the output are "row slots": with a shared decoder, slot = s*H + h
 // (all rows); with per-head decoders, blockIdx.z selects the head and
@@ -54,85 +59,66 @@ absorb_kernel(const void *__restrict__ q, int n_q, int H, int d_I, const float *
   if (b) b += (int64_t)layer * (d_I - nope_off);
   q_tilde += (int64_t)layer * n_q * H * r;
   if (beta) beta += (int64_t)layer * n_q * H;
-  __shared__ float As[kKC][kT + 4];  // As[d][row]
-  __shared__ float Bs[kKC][kT + 4];  // Bs[d][j]
-  constexpr int kPer4 = kT * kKC / 4 / 256;  // float4 loads of each operand per thread
   const int h_fixed = blockIdx.z % zH;
   const int n_rows = per_head ? n_q : n_q * H;
-  const int row0 = blockIdx.y * kT, j0 = blockIdx.x * kT;
   const float *D = Dt + (per_head ? (int64_t)h_fixed * head_stride : 0);
-  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   auto qrow = [&](int slot) -> int64_t {  // element offset of q row `slot`
     return q_layer + (per_head ? ((int64_t)slot * H + h_fixed) * d_I : (int64_t)slot * d_I);
   };
-  float acc[2][2] = {};
+  // this wavefront's 16 x 16 tile; lane supplies row i of A and of B, slot g
+  const int ti = wave >> 1, tj = wave & 1;
+  const int i = lane % 16, g = lane / 16;
+  const int slot = blockIdx.y * kT + 16 * ti + i, j = blockIdx.x * kT + 16 * tj + i;
+  const bool a_ok = slot < n_rows, b_ok = j < r;
+  // out-of-range rows read a valid row and are zeroed, so loads need no branches
+  const int64_t qo = qrow(a_ok ? slot : 0);
+  const float *dr = D + (int64_t)(b_ok ? j : 0) * d_I;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int d0 = 0; d0 < d_I; d0 += kKC) {
-    // Out-of-range elements load from a clamped, valid address and are
-    // zeroed afterwards, so all loads issue back to back without branches.
-    float4 av[kPer4], bv[kPer4];
+    float4 av[8], bv[8];
 #pragma unroll
-    for (int m = 0; m < kPer4; ++m) {
-      const int e = tid + 256 * m, rr = e / (kKC / 4), d = d0 + 4 * (e % (kKC / 4));
-      const int slot = row0 + rr, j = j0 + rr;
+    for (int c = 0; c < 8; ++c) {
+      const int d = d0 + 32 * g + 4 * c;
       const int dc = d < d_I ? d : 0;
-      av[m] = ldq4<BF16Q>(q, qrow(slot < n_rows ? slot : 0) + dc);
-      bv[m] = *(const float4 *)(D + (int64_t)(j < r ? j : 0) * d_I + dc);
-      if (!(d < d_I && slot < n_rows)) av[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (!(d < d_I && j < r)) bv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+      av[c] = ldq4<BF16Q>(q, qo + dc);
+      bv[c] = *(const float4 *)(dr + dc);
+      if (!(a_ok && d < d_I)) av[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (!(b_ok && d < d_I)) bv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int m = 0; m < kPer4; ++m) {
-      const int e = tid + 256 * m, rr = e / (kKC / 4), dd = 4 * (e % (kKC / 4));
-      As[dd][rr] = av[m].x;
-      As[dd + 1][rr] = av[m].y;
-      As[dd + 2][rr] = av[m].z;
-      As[dd + 3][rr] = av[m].w;
-      Bs[dd][rr] = bv[m].x;
-      Bs[dd + 1][rr] = bv[m].y;
-      Bs[dd + 2][rr] = bv[m].z;
-      Bs[dd + 3][rr] = bv[m].w;
-    }
-    __syncthreads();
-    const int nd = min(kKC, d_I - d0);
-#pragma unroll 16
-    for (int dd = 0; dd < nd; ++dd) {
-      float a[2], bb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = As[dd][ty * 2 + i];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) bb[c] = Bs[dd][tx + 16 * c];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) acc[i][c] = fmaf(a[i], bb[c], acc[i][c]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int slot = row0 + ty * 2 + i;
-    if (slot >= n_rows) continue;
-    const int64_t orow = per_head ? ((int64_t)slot * H + h_fixed) : slot;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int j = j0 + tx + 16 * c;
-      if (j < r) q_tilde[orow * r + j] = acc[i][c];
+    for (int c = 0; c < 8; ++c) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].x, bv[c].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].y, bv[c].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].z, bv[c].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].w, bv[c].w, acc, 0, 0, 0);
     }
   }
-  // beta for this tile's rows, computed once (by the column-0 tiles): eight
+  // acc[v] = D[4 g + v][i] of the tile
+  const int jo = blockIdx.x * kT + 16 * tj + i;
+  if (jo < r) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int so = blockIdx.y * kT + 16 * ti + 4 * g + v;
+      if (so >= n_rows) continue;
+      const int64_t orow = per_head ? ((int64_t)so * H + h_fixed) : so;
+      q_tilde[orow * r + jo] = acc[v];
+    }
+  }
+  // beta for this block's rows, computed once (by the column-0 blocks): eight
   // threads per row, a fixed-order combination of their partial sums.
   if (beta && blockIdx.x == 0) {
     const int rr = tid / 8, part = tid % 8;
-    const int slot = row0 + rr;
+    const int sl = blockIdx.y * kT + rr;
     float s = 0.f;
-    if (b && slot < n_rows) {
-      const int64_t off = qrow(slot);
+    if (b && sl < n_rows) {
+      const int64_t off = qrow(sl);
       for (int d = nope_off + part; d < d_I; d += 8) s = fmaf(ldq<BF16Q>(q, off + d), b[d - nope_off], s);
     }
     s += __shfl_xor(s, 1, kWave);
     s += __shfl_xor(s, 2, kWave);
     s += __shfl_xor(s, 4, kWave);
-    if (part == 0 && slot < n_rows) beta[per_head ? ((int64_t)slot * H + h_fixed) : slot] = s;
+    if (part == 0 && sl < n_rows) beta[per_head ? ((int64_t)sl * H + h_fixed) : sl] = s;
   }
 }
 
