@@ -192,7 +192,13 @@ li_status li_topk(const float *scores, int64_t ld, int32_t n_rows, const int32_t
  *              ascending token ids, -1 padded (the input of li_hs_select).
  *   k, sel     1 <= k <= B; sel device int32 [n_rows, k] (out), ascending,
  *              -1 padded.  sel may be NULL when only C is wanted.
- *   ws         device workspace of li_hs_anchor_workspace_bytes() bytes.
+ *   ws         device workspace of li_hs_anchor_workspace_bytes() bytes,
+ *              zeroed once before its first use (e.g. one hipMemsetAsync).
+ *              Each call leaves the counters it relies on zeroed again, so
+ *              the workspace serves later calls of any n_rows <= 64 and
+ *              max_len it is large enough for without another clear (with
+ *              n_rows > 64 every call clears them itself).  Calls sharing
+ *              a workspace must not overlap in time.
  * Results equal two li_topk calls with k = B and with k.
  */
 size_t li_hs_anchor_workspace_bytes(int32_t n_rows, int32_t max_len);

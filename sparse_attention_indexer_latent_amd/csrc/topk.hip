@@ -225,9 +225,20 @@ constexpr int kSegThreads = 256;
 constexpr int kSegPer = kSeg / kSegThreads;  // 8 consecutive positions per thread
 constexpr int kMaxSegs = 1024;
 
+// Workspace of the many-row path.  The row histograms must be zero when a
+// call starts; nothing reads them after the extract step, so the select step
+// zeroes them again (each workgroup a slice of its row), and a workspace that
+// starts zeroed needs no clearing launch.  For up to kHeadRows rows they sit
+// at a fixed offset at the front (the same place whatever n_rows and
+// max_len); beyond that they follow and every call clears them.  The
+// second-level histograms are zeroed by the histogram step of the same call
+// (the select step of the previous call has read them by then).
+constexpr int kHeadRows = 64;
+
 struct MultiWs {
   uint32_t *hist;     // [n_rows][kBins]
   uint32_t *h10;      // [n_rows][2][1024]: next 10 bits of each output's threshold bucket
+  uint32_t *bsel;     // [n_rows][2][2]: each output's 12-bit bucket and the count above it
   uint32_t *seg_cnt;  // [n_rows][S]
   uint32_t *lkey;     // [n_rows][S][kSeg]
   int32_t *lpos;      // [n_rows][S][kSeg]
@@ -236,14 +247,18 @@ struct MultiWs {
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+inline size_t hist_bytes(int n) { return (size_t)n * kBins * 4; }
+
 MultiWs carve(void *ws, int n_rows, int max_len) {
   MultiWs m;
   m.S = (max_len + kSeg - 1) / kSeg;
   char *p = (char *)ws;
-  m.hist = (uint32_t *)p;  // hist and h10 are adjacent: one clear covers both
-  p += (size_t)n_rows * kBins * 4;
+  m.hist = (uint32_t *)(n_rows <= kHeadRows ? p : p + hist_bytes(kHeadRows));
+  p += hist_bytes(kHeadRows) + (n_rows <= kHeadRows ? 0 : hist_bytes(n_rows));
   m.h10 = (uint32_t *)p;
   p += align256((size_t)n_rows * 2 * 1024 * 4);
+  m.bsel = (uint32_t *)p;
+  p += align256((size_t)n_rows * 4 * 4);
   m.seg_cnt = (uint32_t *)p;
   p += align256((size_t)n_rows * m.S * 4);
   m.lkey = (uint32_t *)p;
@@ -254,7 +269,8 @@ MultiWs carve(void *ws, int n_rows, int max_len) {
 
 size_t multi_ws_bytes(int n_rows, int max_len) {
   const size_t S = (max_len + kSeg - 1) / kSeg;
-  return (size_t)n_rows * kBins * 4 + align256((size_t)n_rows * 2 * 1024 * 4) +
+  return hist_bytes(kHeadRows) + (n_rows <= kHeadRows ? 0 : hist_bytes(n_rows)) +
+         align256((size_t)n_rows * 2 * 1024 * 4) + align256((size_t)n_rows * 4 * 4) +
          align256((size_t)n_rows * S * 4) + 2 * align256((size_t)n_rows * S * kSeg * 4);
 }
 
@@ -267,11 +283,21 @@ __global__ void __launch_bounds__(256) topk_clear_kernel(uint32_t *__restrict__ 
   if (i < n) hist[i] = 0;
 }
 
+// Workgroup seg of a row's nw zeroes its share of n words at p.
+template <int NT>
+__device__ __forceinline__ void zero_share(uint32_t *p, int n, int seg, int nw) {
+  const int per = (n + nw - 1) / nw;
+  const int e = min(n, (seg + 1) * per);
+  for (int i = seg * per + (int)threadIdx.x; i < e; i += NT) p[i] = 0;
+}
+
 __global__ void __launch_bounds__(kSegThreads)
 topk_hist_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ valid_len,
-                 uint32_t *__restrict__ hist) {
+                 MultiWs m) {
   __shared__ uint32_t h[kBins];
+  uint32_t *hist = m.hist;
   const int row = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
+  zero_share<kSegThreads>(m.h10 + (int64_t)row * 2 * 1024, 2 * 1024, seg, gridDim.x);
   const int n = valid_len[row];
   const int p0 = seg * kSeg;
   if (p0 >= n) return;
@@ -423,9 +449,15 @@ topk_extract_kernel(const float *__restrict__ scores, int64_t ld, const int32_t 
     if (wave < 2) {
       const int kj = wave ? k1 : k0;
       const bool on = wave ? (k1 > 0 && k1 < n) : (k0 < n);
-      uint32_t b = 0xFFFFFFFFu, above, c;
+      uint32_t b = 0xFFFFFFFFu, above = 0, c;
       if (on) b = wave_find(h12, kBins, (uint32_t)kj, &above, &c);
-      if (tid % kWave == 0) res[wave] = b;
+      if (tid % kWave == 0) {
+        res[wave] = b;
+        if (seg == 0) {  // for the select step, which no longer reads the row histogram
+          m.bsel[(int64_t)row * 4 + 2 * wave] = b;
+          m.bsel[(int64_t)row * 4 + 2 * wave + 1] = above;
+        }
+      }
     }
     lds_sync();
   }
@@ -631,10 +663,11 @@ struct FinOut {
 
 // ---------------------------------------------------------------------------
 // Select step of the multi-workgroup path, one workgroup per (row, segment).
-// Every workgroup derives the exact thresholds itself: the 12-bit bucket from
-// the row histogram, the next 10 bits from the bucket's histogram built by the
-// extract step (one wavefront per output, single-wavefront searches), the last
-// 10 bits from the row's extracted keys that share those 22 bits.  The same
+// Every workgroup derives the exact thresholds itself: the 12-bit bucket (and
+// the count above it) as the extract step found it, the next 10 bits from the
+// bucket's histogram built by the extract step (one wavefront per output, a
+// single-wavefront search), the last 10 bits from the row's extracted keys
+// that share those 22 bits.  The same
 // pass over the extracted keys (one wavefront per segment) counts, in the
 // segments before its own, the keys above each threshold and those equal to
 // it, which fixes the output offset of the segment's first selected key; the
@@ -645,7 +678,6 @@ struct FinOut {
 constexpr int kSelThreads = 512;
 
 struct SelShared {
-  __align__(16) uint32_t h12[kBins];  // the row's histograms, copied in one round trip
   __align__(16) uint32_t h10[2][1024];
   uint32_t seg_off[kMaxSegs + 1];
   __align__(16) uint32_t hlow[2][1024];  // low 10 bits of the keys sharing the 22-bit prefix: whole row
@@ -664,20 +696,18 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
   constexpr int NW = kSelThreads / kWave;
   constexpr int kOwn = kSeg / kSelThreads;  // own entries per thread
   // Every load whose address depends on no other load is issued here, before
-  // any result is used: the row's valid length and histograms, the segments'
-  // key counts, this segment's extracted keys and positions, and the first
+  // any result is used: the row's valid length, buckets and second-level
+  // histograms, the segments' key counts, this segment's extracted keys and positions, and the first
   // 256 extracted keys of the 8 segments this wavefront scans first.  Each
   // segment owns kSeg slots, so these are in bounds whatever the counts.
   const int n = valid_len[row];
-  uint32_t a[kBins / kSelThreads], b[2 * 1024 / kSelThreads];
+  uint32_t b[2 * 1024 / kSelThreads];
   {
-    const uint32_t *g12 = m.hist + (int64_t)row * kBins;
     const uint32_t *g10 = m.h10 + (int64_t)row * 2 * 1024;
-#pragma unroll
-    for (int e = 0; e < kBins / kSelThreads; ++e) a[e] = g12[e * kSelThreads + tid];
 #pragma unroll
     for (int e = 0; e < 2 * 1024 / kSelThreads; ++e) b[e] = g10[e * kSelThreads + tid];
   }
+  const uint4 bs = *reinterpret_cast<const uint4 *>(m.bsel + (int64_t)row * 4);  // bucket, above x2
   const uint32_t *cnt = m.seg_cnt + (int64_t)row * m.S;
   const uint32_t c_first = tid < m.S ? cnt[tid] : 0u;
   const int64_t own = ((int64_t)row * m.S + seg) * kSeg;
@@ -706,11 +736,11 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
     }
   }
   const int S = (n + kSeg - 1) / kSeg;
+  // the row histogram is read by no later step: zero it for the next call
+  zero_share<kSelThreads>(m.hist + (int64_t)row * kBins, kBins, seg, gridDim.x);
   if (n <= 0 || seg >= S) return;  // uniform per workgroup
   const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
   const float *u = scores + (int64_t)row * ld;
-#pragma unroll
-  for (int e = 0; e < kBins / kSelThreads; ++e) sh.h12[e * kSelThreads + tid] = a[e];
 #pragma unroll
   for (int e = 0; e < 2 * 1024 / kSelThreads; ++e) (&sh.h10[0][0])[e * kSelThreads + tid] = b[e];
   // offsets of the segments' lists in the row's flattened extracted keys
@@ -740,8 +770,8 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
   if (wave < 2 && act_w) {
     const int j = wave;
     uint32_t above, c;
-    const uint32_t b12 = wave_find(sh.h12, kBins, k_w, &above, &c);
-    const uint32_t nd = k_w - above;
+    const uint32_t b12 = j == 0 ? bs.x : bs.z;
+    const uint32_t nd = k_w - (j == 0 ? bs.y : bs.w);
     const uint32_t d10 = wave_find(sh.h10[j], 1024, nd, &above, &c);
     if (lane == 0) {
       sh.pre22[j] = (b12 << 10) | d10;
@@ -1404,12 +1434,14 @@ topk_reg_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
 
 hipError_t launch_multi(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
                         const int32_t *ids, int64_t ids_ld, int ids_rows, int max_len, FinOut o0,
-                        FinOut o1, int n_out, void *ws, hipStream_t st) {
+                        FinOut o1, int n_out, void *ws, bool ws_clean, hipStream_t st) {
   MultiWs m = carve(ws, n_rows, max_len);
-  const int nh = n_rows * (kBins + 2 * 1024);  // hist and h10
-  topk_clear_kernel<<<(nh + 255) / 256, 256, 0, st>>>(m.hist, nh);
+  if (!(ws_clean && n_rows <= kHeadRows)) {
+    const int nc = n_rows * kBins;
+    topk_clear_kernel<<<(nc + 255) / 256, 256, 0, st>>>(m.hist, nc);
+  }
   dim3 g(m.S, n_rows);
-  topk_hist_kernel<<<g, kSegThreads, 0, st>>>(scores, ld, valid_len, m.hist);
+  topk_hist_kernel<<<g, kSegThreads, 0, st>>>(scores, ld, valid_len, m);
   topk_extract_kernel<<<g, kSegThreads, 0, st>>>(scores, ld, valid_len, o0.k,
                                                  n_out == 2 ? o1.k : 0, m);
   topk_select_kernel<<<g, kSelThreads, 0, st>>>(scores, ld, valid_len, ids, ids_ld, ids_rows, o0,
@@ -1445,7 +1477,7 @@ hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_
   }
   if (use_multi(n_rows, max_len))
     return launch_multi(scores, ld, n_rows, valid_len, ids, ids_ld, ids_rows, max_len,
-                        FinOut{k, out_idx, out_val}, FinOut{0, nullptr, nullptr}, 1, ws, st);
+                        FinOut{k, out_idx, out_val}, FinOut{0, nullptr, nullptr}, 1, ws, false, st);
   if (max_len <= kRegMax) {
     if (max_len <= kRegMax / 2)
       topk_reg_kernel<8><<<n_rows, kThreads, 0, st>>>(scores, ld, valid_len, ids, ids_ld, ids_rows,
@@ -1486,7 +1518,7 @@ hipError_t launch_topk2(const float *scores, int64_t ld, int n_rows, const int32
                         int32_t *out_inner, void *ws, hipStream_t st) {
   return launch_multi(scores, ld, n_rows, valid_len, nullptr, 0, 1, max_len,
                       FinOut{k_outer, out_outer, nullptr}, FinOut{k_inner, out_inner, nullptr}, 2,
-                      ws, st);
+                      ws, true, st);
 }
 
 }  // namespace li

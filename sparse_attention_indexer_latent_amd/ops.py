@@ -265,7 +265,9 @@ def topk(scores: torch.Tensor, valid_len: torch.Tensor, max_len: int, k: int,
 
 
 def hs_anchor_workspace(n_rows: int, max_len: int, device="cuda") -> torch.Tensor:
-    return torch.empty(lib().li_hs_anchor_workspace_bytes(n_rows, max_len), dtype=torch.uint8,
+    """A zeroed workspace for li_hs_anchor_select: zeroed once here, reusable
+    by later calls of any size it covers (one call at a time)."""
+    return torch.zeros(lib().li_hs_anchor_workspace_bytes(n_rows, max_len), dtype=torch.uint8,
                        device=device)
 
 

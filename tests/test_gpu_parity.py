@@ -401,6 +401,27 @@ def test_hs_anchor_select_nested_exact(B, k):
         assert np.array_equal(sel[i], O.pad(O.topk(row, k), k)), i
 
 
+def test_hs_anchor_select_reuses_one_workspace():
+    """One workspace across calls of different row counts and lengths (each
+    call leaves its counting arrays zeroed for the next), every result exact."""
+    say("hs_anchor_select: one workspace, several calls")
+    rng = np.random.default_rng(77)
+    ws = ops.hs_anchor_workspace(6, 131072)
+    for n_rows, L, B, k in [(5, 131072, 8192, 2048), (3, 40000, 4000, 100), (6, 131072, 8192, 2048),
+                            (1, 5000, 300, 7), (5, 131072, 8192, 2048)]:
+        u = np.round(rng.standard_normal((n_rows, L)), 3).astype(np.float32)
+        lens = rng.integers(1, L + 1, n_rows).astype(np.int32)
+        lens[0] = L
+        cand, sel = ops.hs_anchor_select(torch.from_numpy(u).cuda(), torch.from_numpy(lens).cuda(),
+                                         L, B, k, ws=ws)
+        torch.cuda.synchronize()
+        cand, sel = cand.cpu().numpy(), sel.cpu().numpy()
+        for i in range(n_rows):
+            row = u[i, :lens[i]].astype(np.float64)
+            assert np.array_equal(cand[i], O.pad(O.hs_candidates(row, B), B)), (n_rows, L, i)
+            assert np.array_equal(sel[i], O.pad(O.topk(row, k), k)), (n_rows, L, i)
+
+
 @pytest.mark.parametrize("n", [16384, 9000, 8192, 5001])
 def test_topk_exact_short_rows_in_lds(n):
     """Rows of at most 16K elements take the LDS-resident path, rows of at
