@@ -243,6 +243,7 @@ struct MultiWs {
   uint32_t *lkey;     // [n_rows][S][kSeg]
   int32_t *lpos;      // [n_rows][S][kSeg]
   int S;
+  int max_len;        // allocated length of every score row (bounds speculative loads)
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -252,6 +253,7 @@ inline size_t hist_bytes(int n) { return (size_t)n * kBins * 4; }
 MultiWs carve(void *ws, int n_rows, int max_len) {
   MultiWs m;
   m.S = (max_len + kSeg - 1) / kSeg;
+  m.max_len = max_len;
   char *p = (char *)ws;
   m.hist = (uint32_t *)(n_rows <= kHeadRows ? p : p + hist_bytes(kHeadRows));
   p += hist_bytes(kHeadRows) + (n_rows <= kHeadRows ? 0 : hist_bytes(n_rows));
@@ -297,20 +299,22 @@ topk_hist_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__
   __shared__ uint32_t h[kBins];
   uint32_t *hist = m.hist;
   const int row = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
-  zero_share<kSegThreads>(m.h10 + (int64_t)row * 2 * 1024, 2 * 1024, seg, gridDim.x);
-  const int n = valid_len[row];
   const int p0 = seg * kSeg;
+  // the segment's scores are loaded before the row's valid length arrives
+  // (buffer loads bounded by the allocated row length)
+  const float *u = scores + (int64_t)row * ld;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(u), 0, m.max_len * 4, 0x00020000);
+  float v[kSegPer];
+#pragma unroll
+  for (int j = 0; j < kSegPer; ++j)
+    v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (p0 + tid + j * kSegThreads) * 4, 0, 0));
+  const int n = valid_len[row];
+  zero_share<kSegThreads>(m.h10 + (int64_t)row * 2 * 1024, 2 * 1024, seg, gridDim.x);
   if (p0 >= n) return;
   const int p1 = min(n, p0 + kSeg);
   for (int b = tid; b < kBins; b += kSegThreads) h[b] = 0;
   lds_sync();
-  const float *u = scores + (int64_t)row * ld;
-  float v[kSegPer];
-#pragma unroll
-  for (int j = 0; j < kSegPer; ++j) {
-    const int p = p0 + tid + j * kSegThreads;
-    v[j] = p < p1 ? u[p] : 0.f;
-  }
 #pragma unroll
   for (int j = 0; j < kSegPer; ++j)
     if (p0 + tid + j * kSegThreads < p1) atomicAdd(&h[score_key(v[j]) >> 20], 1u);
@@ -418,29 +422,45 @@ topk_extract_kernel(const float *__restrict__ scores, int64_t ld, const int32_t 
   __shared__ uint32_t res[4];
   __shared__ __align__(16) uint32_t h12[kBins];
   const int row = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
-  const int n = valid_len[row];
   const int p0 = seg * kSeg;
+  // One round trip: this segment's scores (buffer loads bounded by the
+  // allocated row length, issued before the row's valid length arrives) and
+  // the row histogram (into LDS).
+  const float *u = scores + (int64_t)row * ld;
+  const int pb = p0 + tid * kSegPer;
+  float sv[kSegPer];
+  {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(u), 0, m.max_len * 4, 0x00020000);
+    if ((reinterpret_cast<uintptr_t>(u) & 15) == 0) {
+#pragma unroll
+      for (int h = 0; h < kSegPer / 4; ++h) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, (pb + 4 * h) * 4, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[4 * h + e] = __uint_as_float(x[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kSegPer; ++e)
+        sv[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (pb + e) * 4, 0, 0));
+    }
+  }
+  uint32_t a[kBins / kSegThreads];
+  {
+    const uint32_t *g = m.hist + (int64_t)row * kBins;
+#pragma unroll
+    for (int e = 0; e < kBins / kSegThreads; ++e) a[e] = g[e * kSegThreads + tid];
+  }
+  const int n = valid_len[row];
   if (p0 >= n) {
     if (tid == 0) m.seg_cnt[(int64_t)row * m.S + seg] = 0;
     return;
   }
-  // one round trip: this segment's scores and the row histogram (into LDS)
-  const float *u = scores + (int64_t)row * ld;
-  const int pb = p0 + tid * kSegPer;
+#pragma unroll
+  for (int e = 0; e < kBins / kSegThreads; ++e) h12[e * kSegThreads + tid] = a[e];
   uint32_t key[kSegPer];
 #pragma unroll
-  for (int e = 0; e < kSegPer; ++e) {
-    const int p = pb + e;
-    key[e] = p < n ? score_key(u[p]) : 0u;
-  }
-  {
-    const uint32_t *g = m.hist + (int64_t)row * kBins;
-    uint32_t a[kBins / kSegThreads];
-#pragma unroll
-    for (int e = 0; e < kBins / kSegThreads; ++e) a[e] = g[e * kSegThreads + tid];
-#pragma unroll
-    for (int e = 0; e < kBins / kSegThreads; ++e) h12[e * kSegThreads + tid] = a[e];
-  }
+  for (int e = 0; e < kSegPer; ++e) key[e] = pb + e < n ? score_key(sv[e]) : 0u;
   lds_sync();
   // threshold buckets of both outputs (all ones: the output takes every key),
   // output j's by wavefront j
