@@ -729,7 +729,10 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
   }
   const uint4 bs = *reinterpret_cast<const uint4 *>(m.bsel + (int64_t)row * 4);  // bucket, above x2
   const uint32_t *cnt = m.seg_cnt + (int64_t)row * m.S;
-  const uint32_t c_first = tid < m.S ? cnt[tid] : 0u;
+  // (unconditional loads from clamped, in-bounds addresses: a load under a
+  // branch makes the compiler wait for every load before it at the join;
+  // values past the row's segments are never used)
+  const uint32_t c_first = cnt[min(tid, m.S - 1)];
   const int64_t own = ((int64_t)row * m.S + seg) * kSeg;
   const uint32_t i0 = tid * kOwn;
   static_assert(kOwn == 4, "own entries load as one 16-byte vector");
@@ -740,9 +743,8 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
   uint4 pk[kPF];
 #pragma unroll
   for (int v = 0; v < kPF; ++v) {
-    const int sg = wave + NW * v;
-    pk[v] = sg < m.S ? *reinterpret_cast<const uint4 *>(lkey + (int64_t)sg * kSeg + 4 * lane)
-                     : make_uint4(0u, 0u, 0u, 0u);
+    const int sg = min(wave + NW * v, m.S - 1);
+    pk[v] = *reinterpret_cast<const uint4 *>(lkey + (int64_t)sg * kSeg + 4 * lane);
   }
   const FinOut out[2] = {o0, o1};
   if (seg == 0) {  // padding of the outputs
