@@ -207,6 +207,28 @@ li_status li_hs_anchor_select(const float *scores, int64_t ld, int32_t n_rows,
                               int32_t k, int32_t *sel, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * li_hs_anchor -- the anchor layer's whole part of hierarchical selection in
+ * one call ("Hierarchical Selection" paragraph, eq. 8): its scores of every
+ * position (as li_score) and, from them, C and S (as li_hs_anchor_select).
+ * For a bf16 cache with H = 64, r = 256 and at most 64 queries, the scorer
+ * builds the rows' key histograms as it writes the scores, so the selection
+ * does not read them an extra time; otherwise it is the two calls in turn.
+ *   q_tilde .. ld: as for li_score; q_len[i] is also row i's valid length.
+ *   B, cand, k, sel: as for li_hs_anchor_select.
+ *   ws          device workspace of li_hs_anchor_workspace_bytes(n_q,
+ *               max_len) bytes, zeroed once before its first use and shared
+ *               with li_hs_anchor_select on the same terms.
+ *   scan_events NULL, or two hipEvent_t recorded on the stream just before
+ *               and just after the scoring launch (to time the scorer alone).
+ * Results equal li_score followed by li_hs_anchor_select.
+ */
+li_status li_hs_anchor(const void *q_tilde, li_dtype qt_dt, const float *w, const float *beta,
+                       int32_t n_q, int32_t H, const int32_t *q_seq, const int32_t *q_len,
+                       int32_t max_len, const li_cache *cache, float *scores, int64_t ld,
+                       int32_t B, int32_t *cand, int32_t k, int32_t *sel, void *ws, size_t ws_bytes,
+                       void *const *scan_events, void *stream);
+
+/*
  * li_hs_select -- the follower layers' hierarchical selection ("Hierarchical
  * Selection" paragraph): rescore only the anchor's candidate set with each
  * follower's own absorbed queries, then keep each follower's top-k within

@@ -213,6 +213,56 @@ li_status li_hs_anchor_select(const float *scores, int64_t ld, int32_t n_rows,
   return hip_status(e, "li_hs_anchor_select launch");
 }
 
+li_status li_hs_anchor(const void *q_tilde, li_dtype qt_dt, const float *w, const float *beta,
+                       int32_t n_q, int32_t H, const int32_t *q_seq, const int32_t *q_len,
+                       int32_t max_len, const li_cache *cache, float *scores, int64_t ld,
+                       int32_t B, int32_t *cand, int32_t k, int32_t *sel, void *ws, size_t ws_bytes,
+                       void *const *scan_events, void *stream) {
+  li_status s = check_score_args(q_tilde, qt_dt, w, n_q, H, q_seq, cache);
+  if (s != LI_OK) return s;
+  if (max_len < 0 || (int64_t)max_len > ld) return fail(LI_ERR_INVALID, "need 0 <= max_len <= ld");
+  if ((int64_t)max_len > (int64_t)cache->max_blocks * 64)
+    return fail(LI_ERR_INVALID, "max_len %d exceeds the block table (%d blocks)", max_len, cache->max_blocks);
+  if (B <= 0 || B > 65536) return fail(LI_ERR_INVALID, "B = %d out of [1, 65536]", B);
+  if (k <= 0) return fail(LI_ERR_INVALID, "k = %d must be positive", k);
+  if (B < k) return fail(LI_ERR_INVALID, "B (%d) < k (%d): the candidate set must hold k", B, k);
+  if (n_q == 0) return LI_OK;
+  if (!q_len || !scores || !cand) return fail(LI_ERR_INVALID, "q_len/scores/cand is NULL");
+  size_t need = li_hs_anchor_workspace_bytes(n_q, max_len > 0 ? max_len : 1);
+  if (!ws || ws_bytes < need) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
+  if ((s = check_device()) != LI_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  li::CacheView cv = li::view_of(*cache);
+  const bool fused = max_len > 0 && !li::score_prefill_supported(qt_dt, H, n_q, cv) &&
+                     li::score_scan_supported(qt_dt, H, n_q, max_len, cv) &&
+                     n_q <= li::topk2_counted_max_rows();
+  auto record = [&](int i) {
+    return scan_events ? hipEventRecord((hipEvent_t)scan_events[i], st) : hipSuccess;
+  };
+  if (!fused) {
+    hipError_t e = record(0);
+    if (e != hipSuccess) return hip_status(e, "li_hs_anchor event");
+    if ((s = li_score(q_tilde, qt_dt, w, beta, n_q, H, q_seq, q_len, max_len, cache, scores, ld,
+                      stream)) != LI_OK)
+      return s;
+    if ((e = record(1)) != hipSuccess) return hip_status(e, "li_hs_anchor event");
+    return li_hs_anchor_select(scores, ld, n_q, q_len, max_len, B, cand, k, sel, ws, ws_bytes,
+                               stream);
+  }
+  uint32_t *hist, *h10;
+  int h10_words;
+  li::topk2_count_arrays(ws, n_q, max_len, &hist, &h10, &h10_words);
+  hipError_t e = record(0);
+  if (e == hipSuccess)
+    e = li::launch_score_scan(q_tilde, qt_dt, w, beta, n_q, q_seq, q_len, max_len, cv, scores, ld,
+                              st, hist, h10, h10_words);
+  if (e == hipSuccess) e = record(1);
+  if (e == hipSuccess)
+    e = sel ? li::launch_topk2_counted(scores, ld, n_q, q_len, max_len, B, cand, k, sel, ws, st)
+            : li::launch_topk2_counted(scores, ld, n_q, q_len, max_len, B, cand, B, cand, ws, st);
+  return hip_status(e, "li_hs_anchor launch");
+}
+
 size_t li_hs_workspace_bytes(int32_t n_f, int32_t n_q, int32_t B, int32_t k) {
   if (n_f <= 0 || n_q <= 0 || B <= 0 || k <= 0) return 0;
   const int64_t rows = (int64_t)n_f * n_q;

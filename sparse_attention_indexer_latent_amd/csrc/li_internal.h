@@ -62,9 +62,12 @@ hipError_t launch_score_mfma(const void *q_tilde, int qt_dt, const float *w, con
 // score_scan.hip: full-scan decode scorer for a bf16 cache, H == 64,
 // r == 256 and at most 64 queries (page mode), one workgroup per CU.
 bool score_scan_supported(int qt_dt, int H, int n_q, int max_len, const CacheView &cv);
+// hist (may be null): [n_q][4096] row histograms of the order-preserving
+// score keys (bin = key >> 20), added to; zbuf[0 .. zwords) is zeroed.
 hipError_t launch_score_scan(const void *q_tilde, int qt_dt, const float *w, const float *beta,
                              int n_q, const int32_t *q_seq, const int32_t *q_len, int max_len,
-                             const CacheView &cv, float *out, int64_t ld, hipStream_t st);
+                             const CacheView &cv, float *out, int64_t ld, hipStream_t st,
+                             uint32_t *hist = nullptr, uint32_t *zbuf = nullptr, int zwords = 0);
 // The same kernel in candidate mode (HS followers): query i scores the B
 // slots of candidate list i % cand_rows into out[i*ld + j], -inf on padding.
 bool score_scan_cand_supported(int qt_dt, int H, int n_q, int B, int cand_rows,
@@ -97,6 +100,16 @@ size_t topk2_ws_bytes(int n_rows, int max_len);
 hipError_t launch_topk2(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
                         int max_len, int k_outer, int32_t *out_outer, int k_inner,
                         int32_t *out_inner, void *ws, hipStream_t st);
+// The anchor path whose scorer builds the row histograms itself (n_rows <= 64
+// and a workspace kept zeroed as li_hs_anchor_select requires): where the row
+// histograms go in ws (zero on entry), and the second-level histograms the
+// scorer must zero; then the selection without its histogram step.
+void topk2_count_arrays(void *ws, int n_rows, int max_len, uint32_t **hist, uint32_t **h10,
+                        int *h10_words);
+int topk2_counted_max_rows();
+hipError_t launch_topk2_counted(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
+                                int max_len, int k_outer, int32_t *out_outer, int k_inner,
+                                int32_t *out_inner, void *ws, hipStream_t st);
 
 // Fill n int32 values with v (device).
 hipError_t launch_fill_i32(int32_t *dst, int n, int32_t v, hipStream_t st);

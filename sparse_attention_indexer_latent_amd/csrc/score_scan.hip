@@ -56,9 +56,14 @@ constexpr int kSwz = 15;
 static_assert(kQst + 2 <= kNst, "q~ staging fits in the stages");
 static_assert(kPerIssuer * kAhead <= 24, "issuer wait counts stay in range");
 
+constexpr int kHistBins = 4096;  // row histogram of score keys, bits 31..20
+
 struct ScanShared {
   __align__(16) char stage[kNst][kUnitB];
   int32_t page[kTab];  // block id of page u0 + i; candidate mode: cache row of slot 64 u0 + i (-1: none)
+  // A page scan uses at most kMaxPages table entries; the rest of the table
+  // and hext hold its histogram of score keys when one is asked for.
+  uint32_t hext[kHistBins - (kTab - kMaxPages)];
   float red[2][4][kTok];    // per head group partial scores, two units
   int32_t ok, myq, mylen, myseq, u0, nu;
 };
@@ -100,13 +105,19 @@ __device__ __forceinline__ int64_t wg_start(int q, int64_t cum, int64_t T, int G
 // candidate list c = i % cand_rows (token ids of sequence q_seq[c], -1 for
 // padding) into out[i*ld + j]; units are 64 consecutive slots; q_len and
 // max_len are unused.
+// hist (page scan only, may be null): [n_q][kHistBins] histograms of the
+// order-preserving keys of the scores written (bin = key >> 20), added to
+// what the array holds; zbuf[0 .. zwords) is zeroed on the way (the
+// workgroups share it out), for a consumer that accumulates there next.
 template <bool QF32, bool CAND>
 __global__ void __launch_bounds__(kThr, 1)
 score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
                   const float *__restrict__ beta, int n_q, const int32_t *__restrict__ q_seq,
                   const int32_t *__restrict__ q_len, int max_len, CacheView cv,
                   const int32_t *__restrict__ cand, int B, int cand_rows, int xw,
-                  float *__restrict__ out, int64_t ld) {
+                  float *__restrict__ out, int64_t ld, uint32_t *__restrict__ hist,
+                  uint32_t *__restrict__ zbuf, int zwords) {
+  static_assert(kTab - kMaxPages + (kHistBins - (kTab - kMaxPages)) == kHistBins, "histogram span");
   constexpr int NT = QF32 ? 2 : 1;               // A operand terms (bf16 hi + lo, or the bf16 q~)
   constexpr int KB = kR / 32;                    // MFMA k-steps
   constexpr int QROWB = QF32 ? 4 * kR : 2 * kR;  // bytes of one head's q~ row
@@ -116,6 +127,7 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
   const int hg = wave & 3, th = (wave >> 2) & 1;  // compute: head group, token half
   const int G = gridDim.x, g = blockIdx.x;
   char *const qst = sh.stage[kQst];  // LDS copy of q~
+  uint32_t *const hl = reinterpret_cast<uint32_t *>(&sh.page[kMaxPages]);  // page scan histogram
 
   // q~ of query q -> LDS (64 x QROWB bytes), 16-byte chunk c of head row h
   // at chunk c ^ (h & 15): 1 KB per load, each compute wavefront an eighth.
@@ -261,6 +273,12 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
       pg[k] = cv.block_table[(int64_t)gq * cv.max_blocks + min(gu0 + i, cv.max_blocks - 1)];
     }
     load_wb(gq);
+    if (hist) {
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = tid; i < kHistBins / 4; i += kCT) reinterpret_cast<uint4 *>(hl)[i] = z;
+      const int per = (zwords + G - 1) / G, e = min(zwords, (g + 1) * per);
+      for (int i = g * per + tid; i < e; i += kCT) zbuf[i] = 0u;
+    }
   #pragma unroll
     for (int k = 0; k < 2; ++k)
       if (tid + k * kCT < gnu) sh.page[tid + k * kCT] = pg[k];
@@ -411,6 +429,7 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
         if (t < mylen) out[(int64_t)myq * ld + t] = sh.page[pp * kTok + lane] < 0 ? -INFINITY : v;
       } else if (t < mylen) {
         out[(int64_t)myq * ld + t] = v;
+        if (hist) atomicAdd(&hl[score_key(v) >> 20], 1u);
       }
     }
   };
@@ -462,6 +481,15 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
       lds_barrier();
       if (nu >= 2) store_final(nu - 2);
       store_final(nu - 1);
+    }
+  }
+  if (!CAND && hist) {
+    // this range's histogram into the query's row histogram
+    lds_barrier();
+    uint32_t *gh = hist + (int64_t)myq * kHistBins;
+    for (int i = tid; i < kHistBins; i += kThr) {
+      const uint32_t c = hl[i];
+      if (c) atomicAdd(gh + i, c);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load in flight at exit
@@ -526,14 +554,17 @@ bool score_scan_cand_supported(int qt_dt, int H, int n_q, int B, int cand_rows,
 
 hipError_t launch_score_scan(const void *q_tilde, int qt_dt, const float *w, const float *beta,
                              int n_q, const int32_t *q_seq, const int32_t *q_len, int max_len,
-                             const CacheView &cv, float *out, int64_t ld, hipStream_t st) {
+                             const CacheView &cv, float *out, int64_t ld, hipStream_t st,
+                             uint32_t *hist, uint32_t *zbuf, int zwords) {
   const int G = scan_grid(n_q, (max_len + kTok - 1) / kTok);
   if (qt_dt == LI_FP32)
     score_scan_kernel<true, false><<<G, kThr, 0, st>>>(q_tilde, w, beta, n_q, q_seq, q_len, max_len,
-                                                       cv, nullptr, 0, 1, 0, out, ld);
+                                                       cv, nullptr, 0, 1, 0, out, ld, hist, zbuf,
+                                                       zwords);
   else
     score_scan_kernel<false, false><<<G, kThr, 0, st>>>(q_tilde, w, beta, n_q, q_seq, q_len, max_len,
-                                                        cv, nullptr, 0, 1, 0, out, ld);
+                                                        cv, nullptr, 0, 1, 0, out, ld, hist, zbuf,
+                                                        zwords);
   return hipGetLastError();
 }
 
@@ -545,10 +576,12 @@ hipError_t launch_score_scan_cand(const void *q_tilde, int qt_dt, const float *w
   cand_plan(n_q, B, cand_rows, &G, &xw);
   if (qt_dt == LI_FP32)
     score_scan_kernel<true, true><<<G, kThr, 0, st>>>(q_tilde, w, beta, n_q, q_seq, nullptr, 0, cv,
-                                                      cand, B, cand_rows, xw, out, ld);
+                                                      cand, B, cand_rows, xw, out, ld, nullptr,
+                                                      nullptr, 0);
   else
     score_scan_kernel<false, true><<<G, kThr, 0, st>>>(q_tilde, w, beta, n_q, q_seq, nullptr, 0, cv,
-                                                       cand, B, cand_rows, xw, out, ld);
+                                                       cand, B, cand_rows, xw, out, ld, nullptr,
+                                                       nullptr, 0);
   return hipGetLastError();
 }
 

@@ -1456,14 +1456,17 @@ topk_reg_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
 
 hipError_t launch_multi(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
                         const int32_t *ids, int64_t ids_ld, int ids_rows, int max_len, FinOut o0,
-                        FinOut o1, int n_out, void *ws, bool ws_clean, hipStream_t st) {
+                        FinOut o1, int n_out, void *ws, bool ws_clean, hipStream_t st,
+                        bool counted = false) {
   MultiWs m = carve(ws, n_rows, max_len);
-  if (!(ws_clean && n_rows <= kHeadRows)) {
-    const int nc = n_rows * kBins;
-    topk_clear_kernel<<<(nc + 255) / 256, 256, 0, st>>>(m.hist, nc);
-  }
   dim3 g(m.S, n_rows);
-  topk_hist_kernel<<<g, kSegThreads, 0, st>>>(scores, ld, valid_len, m);
+  if (!counted) {  // else the scorer built the row histograms and zeroed h10
+    if (!(ws_clean && n_rows <= kHeadRows)) {
+      const int nc = n_rows * kBins;
+      topk_clear_kernel<<<(nc + 255) / 256, 256, 0, st>>>(m.hist, nc);
+    }
+    topk_hist_kernel<<<g, kSegThreads, 0, st>>>(scores, ld, valid_len, m);
+  }
   topk_extract_kernel<<<g, kSegThreads, 0, st>>>(scores, ld, valid_len, o0.k,
                                                  n_out == 2 ? o1.k : 0, m);
   topk_select_kernel<<<g, kSelThreads, 0, st>>>(scores, ld, valid_len, ids, ids_ld, ids_rows, o0,
@@ -1541,6 +1544,24 @@ hipError_t launch_topk2(const float *scores, int64_t ld, int n_rows, const int32
   return launch_multi(scores, ld, n_rows, valid_len, nullptr, 0, 1, max_len,
                       FinOut{k_outer, out_outer, nullptr}, FinOut{k_inner, out_inner, nullptr}, 2,
                       ws, true, st);
+}
+
+void topk2_count_arrays(void *ws, int n_rows, int max_len, uint32_t **hist, uint32_t **h10,
+                        int *h10_words) {
+  const MultiWs m = carve(ws, n_rows, max_len);
+  *hist = m.hist;
+  *h10 = m.h10;
+  *h10_words = n_rows * 2 * 1024;
+}
+
+int topk2_counted_max_rows() { return kHeadRows; }
+
+hipError_t launch_topk2_counted(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
+                                int max_len, int k_outer, int32_t *out_outer, int k_inner,
+                                int32_t *out_inner, void *ws, hipStream_t st) {
+  return launch_multi(scores, ld, n_rows, valid_len, nullptr, 0, 1, max_len,
+                      FinOut{k_outer, out_outer, nullptr}, FinOut{k_inner, out_inner, nullptr}, 2,
+                      ws, true, st, true);
 }
 
 }  // namespace li

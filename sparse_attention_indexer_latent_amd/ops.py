@@ -62,6 +62,9 @@ _SIGS = {
     "li_topk": (_I32, [_P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "li_hs_anchor_workspace_bytes": (_SZ, [_I32, _I32]),
     "li_hs_anchor_select": (_I32, [_P, _I64, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _SZ, _P]),
+    "li_hs_anchor": (_I32, [_P, _I32, _P, _P, _I32, _I32, _P, _P, _I32,
+                            ctypes.POINTER(LiCacheStruct), _P, _I64, _I32, _P, _I32, _P, _P, _SZ,
+                            _P, _P]),
     "li_hs_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "li_hs_select": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P,
                             ctypes.POINTER(LiCacheStruct), _I32, _P, _P, _P, _SZ, _P]),
@@ -288,6 +291,43 @@ def hs_anchor_select(scores: torch.Tensor, valid_len: torch.Tensor, max_len: int
                                      valid_len.data_ptr(), max_len, B, cand.data_ptr(), k,
                                      _ptr(sel), ws.data_ptr(), ws.numel(), _stream()))
     return cand, sel
+
+
+def hs_anchor(q_tilde: torch.Tensor, w: torch.Tensor, beta: Optional[torch.Tensor],
+              q_seq: torch.Tensor, q_len: torch.Tensor, max_len: int, cache: Cache, B: int, k: int,
+              scores: Optional[torch.Tensor] = None, cand: Optional[torch.Tensor] = None,
+              sel: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+              want_sel: bool = True, scan_events=None):
+    """The anchor's scores of every position and its candidate set (top-B) and
+    own selection (top-k), in one call.  scan_events: None, or two raw
+    hipEvent_t handles recorded around the scoring launch.  Returns
+    (scores, cand, sel)."""
+    _need(q_tilde, "q_tilde", (torch.float32, torch.bfloat16))
+    _need(w, "w", torch.float32)
+    _need(q_seq, "q_seq", torch.int32)
+    _need(q_len, "q_len", torch.int32)
+    if beta is not None:
+        _need(beta, "beta", torch.float32)
+    n_q, H, _ = q_tilde.shape
+    dev = q_tilde.device
+    if scores is None:
+        scores = torch.empty((n_q, max(1, max_len)), dtype=torch.float32, device=dev)
+    _need(scores, "scores", torch.float32)
+    if cand is None:
+        cand = torch.empty((n_q, B), dtype=torch.int32, device=dev)
+    if sel is None and want_sel:
+        sel = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = hs_anchor_workspace(n_q, max_len, dev)
+    evs = None
+    if scan_events is not None:
+        evs = (ctypes.c_void_p * 2)(*[e.value if isinstance(e, ctypes.c_void_p) else int(e)
+                                      for e in scan_events])
+    _check(lib().li_hs_anchor(q_tilde.data_ptr(), _dtype_code(q_tilde), w.data_ptr(), _ptr(beta),
+                              n_q, H, q_seq.data_ptr(), q_len.data_ptr(), max_len, cache.struct(),
+                              scores.data_ptr(), scores.shape[1], B, cand.data_ptr(), k, _ptr(sel),
+                              ws.data_ptr(), ws.numel(), evs, _stream()))
+    return scores, cand, sel
 
 
 def hs_workspace(n_q: int, B: int, k: int, device="cuda", n_f: int = 1) -> torch.Tensor:

@@ -122,6 +122,10 @@ class DeviceWorkload:
         wl = self.wl
         ops.hs_anchor_select(self.scores, self.q_len, self.max_len, wl.B, wl.k, cand=self.cand,
                              sel=self.hs_sel[0], ws=self.anchor_ws)
+        self._hs_followers(keep_scores)
+
+    def _hs_followers(self, keep_scores: bool = False) -> None:
+        wl = self.wl
         if wl.G > 1:  # every follower at once: they share the candidate set
             ops.hs_select(self.cand, self.q_tilde[1:], self.w[1:],
                           self.beta[1:], self.q_seq, self.cache, wl.k, out_idx=self.hs_sel[1:],
@@ -141,15 +145,23 @@ class DeviceWorkload:
 
     def hs_step(self, append: bool = True, keep_scores: bool = False, events=None) -> None:
         """Hierarchical-selection decode step: the anchor scans and proposes
-        its top-B, followers rescore and refine within the candidates.
-        events: optional (start, end) CUDA events recorded around the anchor scan."""
+        its top-B (one li_hs_anchor call), followers rescore and refine within
+        the candidates.  events: optional (start, end) events around the
+        anchor's scoring launch: raw HIP events (an `e` handle) go into the
+        call; torch events make the anchor run as two calls around them."""
         self._pre(append)
-        if events is not None:
+        raw = None if events is None else (getattr(events[0], "e", None), getattr(events[1], "e", None))
+        if raw is not None and (raw[0] is None or raw[1] is None):  # torch events: separate calls
             events[0].record()
-        self.score(0)
-        if events is not None:
+            self.score(0)
             events[1].record()
-        self._hs_post(keep_scores)
+            self._hs_post(keep_scores)
+            return
+        wl = self.wl
+        ops.hs_anchor(self.q_tilde[0], self.w[0], self.beta[0], self.q_seq, self.q_len,
+                      self.max_len, self.cache, wl.B, wl.k, scores=self.scores, cand=self.cand,
+                      sel=self.hs_sel[0], ws=self.anchor_ws, scan_events=raw)
+        self._hs_followers(keep_scores)
 
     def capture(self, hs: bool, append: bool = True, keep_scores: bool = False) -> "StepGraphs":
         """Capture one decode step as graphs around the scan (see StepGraphs)."""

@@ -422,6 +422,43 @@ def test_hs_anchor_select_reuses_one_workspace():
             assert np.array_equal(sel[i], O.pad(O.topk(row, k), k)), (n_rows, L, i)
 
 
+@pytest.mark.parametrize("case", ["ragged", "batch4_128k", "fp32_cache"])
+def test_hs_anchor_fused_equals_two_calls(case):
+    """li_hs_anchor (scores with the key histograms built by the scorer, then
+    the selection) gives the bits of li_score followed by
+    li_hs_anchor_select, call after call on one workspace, and the oracle's
+    selection of the dumped scores; fp32_cache takes the unfused route."""
+    say(f"hs_anchor fused: {case}")
+    if case == "ragged":
+        wl = W.small_decode(12, n_seq=5, lens=[1, 63, 700, 4000, 9000], H=64, r=256, d_I=128, G=1,
+                            k=64, B=512, cache_dtype="bf16")
+    elif case == "fp32_cache":
+        wl = W.small_decode(13, n_seq=3, lens=[40, 900, 5000], H=8, r=32, d_I=16, G=1, k=16, B=100,
+                            cache_dtype="fp32")
+    else:
+        wl = W.config(3)
+    dw = DeviceWorkload(wl, hold_last=False)
+    dw.absorb(0)
+    n_q, L = wl.n_q, dw.max_len
+    ws = ops.hs_anchor_workspace(n_q, L)
+    for rep in range(2):
+        sc, cand, sel = ops.hs_anchor(dw.q_tilde[0], dw.w[0], dw.beta[0], dw.q_seq, dw.q_len, L,
+                                      dw.cache, wl.B, wl.k, ws=ws)
+        ref = ops.score(dw.q_tilde[0], dw.w[0], dw.beta[0], dw.q_seq, dw.q_len, L, dw.cache)
+        rc, rs = ops.hs_anchor_select(ref, dw.q_len, L, wl.B, wl.k)
+        torch.cuda.synchronize()
+        u, ur = sc.cpu().numpy(), ref.cpu().numpy()
+        cand, sel = cand.cpu().numpy(), sel.cpu().numpy()
+        for i in range(n_q):
+            n = int(wl.q_len[i])
+            assert np.array_equal(u[i, :n].view(np.uint32), ur[i, :n].view(np.uint32)), (rep, i)
+        assert np.array_equal(cand, rc.cpu().numpy()) and np.array_equal(sel, rs.cpu().numpy()), rep
+        for i in range(n_q):
+            row = u[i, :int(wl.q_len[i])].astype(np.float64)
+            assert np.array_equal(cand[i], O.pad(O.hs_candidates(row, wl.B), wl.B)), (rep, i)
+            assert np.array_equal(sel[i], O.pad(O.topk(row, wl.k), wl.k)), (rep, i)
+
+
 @pytest.mark.parametrize("n", [16384, 9000, 8192, 5001])
 def test_topk_exact_short_rows_in_lds(n):
     """Rows of at most 16K elements take the LDS-resident path, rows of at
