@@ -695,7 +695,7 @@ struct FinOut {
 // outputs share every pass (their per-thread counts ride in the two halves
 // of a 32-bit word where they are bounded by 2048).
 // ---------------------------------------------------------------------------
-constexpr int kSelThreads = 512;
+constexpr int kSelThreads = 1024;
 
 struct SelShared {
   __align__(16) uint32_t h10[2][1024];
@@ -735,11 +735,11 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
   const uint32_t c_first = cnt[min(tid, m.S - 1)];
   const int64_t own = ((int64_t)row * m.S + seg) * kSeg;
   const uint32_t i0 = tid * kOwn;
-  static_assert(kOwn == 4, "own entries load as one 16-byte vector");
-  const uint4 ek4 = *reinterpret_cast<const uint4 *>(m.lkey + own + i0);
-  const int4 ep4 = *reinterpret_cast<const int4 *>(m.lpos + own + i0);
+  static_assert(kOwn == 2, "own entries load as one 8-byte vector");
+  const uint2 ek2 = *reinterpret_cast<const uint2 *>(m.lkey + own + i0);
+  const int2 ep2 = *reinterpret_cast<const int2 *>(m.lpos + own + i0);
   const uint32_t *lkey = m.lkey + (int64_t)row * m.S * kSeg;
-  constexpr int kPF = 8;  // segments wave + NW u, u < kPF: their first 256 keys, 4 per lane
+  constexpr int kPF = 4;  // segments wave + NW u, u < kPF: their first 256 keys, 4 per lane
   uint4 pk[kPF];
 #pragma unroll
   for (int v = 0; v < kPF; ++v) {
@@ -822,15 +822,13 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
     for (int j = 0; j < 2; ++j) {
       if (!act[j]) continue;  // uniform
       const uint32_t P = pre22[j];
-      uint32_t g = 0;
       bool hit = false;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t h = ks[t] >> 10;
-        g += h > P ? 1u : 0u;
-        hit |= h == P;
+      for (int t = 0; t < 4; ++t) hit |= (ks[t] >> 10) == P;
+      if (before) {  // uniform
+#pragma unroll
+        for (int t = 0; t < 4; ++t) gtc[j] += (ks[t] >> 10) > P ? 1u : 0u;
       }
-      if (before) gtc[j] += g;
       if (hit) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -841,20 +839,26 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
       }
     }
   };
-  auto seg_pass = [&](int sg, const uint4 first) __attribute__((always_inline)) {
+  auto seg_pass = [&](int sg, const uint4 first, uint32_t cn) __attribute__((always_inline)) {
     if (sg >= S) return;  // uniform
     const bool before = sg < seg;
-    const uint32_t cn = sh.seg_off[sg + 1] - sh.seg_off[sg];
     if (cn == 0) return;
     visit4(first, before);
     for (uint32_t e0 = 256; e0 < cn; e0 += 256)  // lists longer than 256 keys
       visit4(*reinterpret_cast<const uint4 *>(lkey + (int64_t)sg * kSeg + e0 + 4 * lane), before);
   };
   if (act[0] || act[1]) {
+    uint32_t cns[kPF];  // the segments' key counts, read before any is used
 #pragma unroll
-    for (int v = 0; v < kPF; ++v) seg_pass(wave + NW * v, pk[v]);
+    for (int v = 0; v < kPF; ++v) {
+      const int sg = min(wave + NW * v, S - 1);
+      cns[v] = sh.seg_off[sg + 1] - sh.seg_off[sg];
+    }
+#pragma unroll
+    for (int v = 0; v < kPF; ++v) seg_pass(wave + NW * v, pk[v], cns[v]);
     for (int sg = wave + NW * kPF; sg < S; sg += NW)
-      seg_pass(sg, *reinterpret_cast<const uint4 *>(lkey + (int64_t)sg * kSeg + 4 * lane));
+      seg_pass(sg, *reinterpret_cast<const uint4 *>(lkey + (int64_t)sg * kSeg + 4 * lane),
+               sh.seg_off[sg + 1] - sh.seg_off[sg]);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -896,8 +900,8 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
   }
   // emit this segment's selected keys in ascending positions
   const uint32_t mc = sh.seg_off[seg + 1] - my0;
-  const uint32_t ek[kOwn] = {ek4.x, ek4.y, ek4.z, ek4.w};
-  const int32_t ep[kOwn] = {ep4.x, ep4.y, ep4.z, ep4.w};
+  const uint32_t ek[kOwn] = {ek2.x, ek2.y};
+  const int32_t ep[kOwn] = {ep2.x, ep2.y};
   uint32_t eqb[2] = {eq_before[0], eq_before[1]};
   if ((act[0] && !all_eq[0]) || (act[1] && !all_eq[1])) {
     uint32_t c = 0;
