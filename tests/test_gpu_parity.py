@@ -422,7 +422,7 @@ def test_hs_anchor_select_reuses_one_workspace():
             assert np.array_equal(sel[i], O.pad(O.topk(row, k), k)), (n_rows, L, i)
 
 
-@pytest.mark.parametrize("case", ["ragged", "batch4_128k", "fp32_cache"])
+@pytest.mark.parametrize("case", ["ragged", "batch4_128k", "fp32_cache", "bf16_q_beta"])
 def test_hs_anchor_fused_equals_two_calls(case):
     """li_hs_anchor (scores with the key histograms built by the scorer, then
     the selection) gives the bits of li_score followed by
@@ -435,16 +435,22 @@ def test_hs_anchor_fused_equals_two_calls(case):
     elif case == "fp32_cache":
         wl = W.small_decode(13, n_seq=3, lens=[40, 900, 5000], H=8, r=32, d_I=16, G=1, k=16, B=100,
                             cache_dtype="fp32")
+    elif case == "bf16_q_beta":  # stored bf16 absorbed queries, a bias on half the dims
+        wl = W.small_decode(14, n_seq=4, lens=[3000, 70, 12000, 6500], H=64, r=256, d_I=128, G=1,
+                            k=100, B=1000, cache_dtype="bf16", nope_off=64, bias=True)
     else:
         wl = W.config(3)
     dw = DeviceWorkload(wl, hold_last=False)
     dw.absorb(0)
     n_q, L = wl.n_q, dw.max_len
+    qt = dw.q_tilde[0].to(torch.bfloat16) if case == "bf16_q_beta" else dw.q_tilde[0]
+    if case == "bf16_q_beta":
+        assert float(dw.beta[0].abs().max()) > 0
     ws = ops.hs_anchor_workspace(n_q, L)
     for rep in range(2):
-        sc, cand, sel = ops.hs_anchor(dw.q_tilde[0], dw.w[0], dw.beta[0], dw.q_seq, dw.q_len, L,
+        sc, cand, sel = ops.hs_anchor(qt, dw.w[0], dw.beta[0], dw.q_seq, dw.q_len, L,
                                       dw.cache, wl.B, wl.k, ws=ws)
-        ref = ops.score(dw.q_tilde[0], dw.w[0], dw.beta[0], dw.q_seq, dw.q_len, L, dw.cache)
+        ref = ops.score(qt, dw.w[0], dw.beta[0], dw.q_seq, dw.q_len, L, dw.cache)
         rc, rs = ops.hs_anchor_select(ref, dw.q_len, L, wl.B, wl.k)
         torch.cuda.synchronize()
         u, ur = sc.cpu().numpy(), ref.cpu().numpy()
@@ -457,6 +463,37 @@ def test_hs_anchor_fused_equals_two_calls(case):
             row = u[i, :int(wl.q_len[i])].astype(np.float64)
             assert np.array_equal(cand[i], O.pad(O.hs_candidates(row, wl.B), wl.B)), (rep, i)
             assert np.array_equal(sel[i], O.pad(O.topk(row, wl.k), wl.k)), (rep, i)
+
+
+def test_hs_anchor_candidates_only_and_scan_events():
+    """li_hs_anchor with sel = NULL returns the candidate set alone, and its
+    two timing events bracket the scoring launch (recorded, ordered)."""
+    import ctypes
+    say("hs_anchor: candidates only, scan events")
+    wl = W.small_decode(15, n_seq=2, lens=[5000, 9000], H=64, r=256, d_I=128, G=1, k=50, B=700,
+                        cache_dtype="bf16")
+    dw = DeviceWorkload(wl, hold_last=False)
+    dw.absorb(0)
+    hip = ctypes.CDLL("libamdhip64.so")
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    try:
+        sc, cand, sel = ops.hs_anchor(dw.q_tilde[0], dw.w[0], dw.beta[0], dw.q_seq, dw.q_len,
+                                      dw.max_len, dw.cache, wl.B, wl.k, want_sel=False,
+                                      scan_events=ev)
+        torch.cuda.synchronize()
+        assert sel is None
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+        assert 0.0 < ms.value < 1000.0
+    finally:
+        for e in ev:
+            hip.hipEventDestroy(e)
+    u, cand = sc.cpu().numpy(), cand.cpu().numpy()
+    for i in range(wl.n_q):
+        row = u[i, :int(wl.q_len[i])].astype(np.float64)
+        assert np.array_equal(cand[i], O.pad(O.hs_candidates(row, wl.B), wl.B)), i
 
 
 @pytest.mark.parametrize("n", [16384, 9000, 8192, 5001])
