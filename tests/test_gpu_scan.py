@@ -1,8 +1,9 @@
 """GPU parity of the full-scan decode scorer (li_score over a bf16 cache with
 H = 64, r = 256 and at most 64 queries): many ragged queries on remapped
 sequences with both q~ dtypes, every score against the oracle, nothing
-written past a query's length; and the batch-4 x 128K workload, sampled and
-bit-identical across launches."""
+written past a query's length; the batch-4 x 128K workload, sampled and
+bit-identical across launches; and the whole HS decode step at that shape
+(anchor, then three followers on 8192 candidates each)."""
 
 import numpy as np
 import pytest
@@ -92,3 +93,32 @@ def test_scan_batch4_128k_sampled_and_deterministic():
             C = O.store_latent(wl.latent(seq)[rows], wl.cache_dtype)[2]
             o = O.layer_scores(C, wl.q[l, s], wl.Dt[l], wl.b[l], wl.nope_off, wl.w[l, s])
             assert_scores_close(u[s, rows], o, RTOL_BF16, f"layer {l} query {s}")
+
+
+def test_hs_step_batch4_128k_followers():
+    """The whole HS decode step at the benchmark's shape (four 128K-token
+    queries, B = 8192, k = 2048, three followers): the anchor's candidates
+    and selection exact on its dumped scores, every follower's candidate
+    scores against the oracle, and every follower's selection exact on its
+    dumped candidate scores."""
+    wl = W.config(3)
+    say(f"HS step followers: {wl.name}")
+    dw = DeviceWorkload(wl, hold_last=False)
+    dw.hs_step(append=False, keep_scores=True)
+    torch.cuda.synchronize()
+    u0 = dw.scores.cpu().numpy()
+    cand = dw.cand.cpu().numpy()
+    sel = dw.hs_sel.cpu().numpy()
+    cs_all = dw.cand_scores.cpu().numpy()
+    for s in range(wl.n_q):
+        seq, L = int(wl.q_seq[s]), int(wl.q_len[s])
+        row = u0[s, :L].astype(np.float64)
+        assert np.array_equal(cand[s], O.pad(O.hs_candidates(row, wl.B), wl.B)), s
+        assert np.array_equal(sel[0, s], O.pad(O.topk(row, wl.k), wl.k)), s
+        C = O.store_latent(wl.latent(seq)[cand[s]], wl.cache_dtype)[2]
+        for l in range(1, wl.G):
+            cs = cs_all[l, s]
+            o = O.layer_scores(C, wl.q[l, s], wl.Dt[l], wl.b[l], wl.nope_off, wl.w[l, s])
+            assert_scores_close(cs, o, RTOL_BF16, f"follower {l} query {s}")
+            ref = O.pad(O.hs_follower(cand[s], cs.astype(np.float64), wl.k), wl.k)
+            assert np.array_equal(sel[l, s], ref), (l, s)
