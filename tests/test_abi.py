@@ -18,7 +18,8 @@ def test_every_declared_symbol_is_exported(L):
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
-    for core in ["li_append_latent", "li_absorb_queries", "li_score", "li_topk", "li_hs_select"]:
+    for core in ["li_append_latent", "li_absorb_queries", "li_score", "li_topk", "li_hs_anchor",
+                 "li_hs_anchor_select", "li_hs_select"]:
         assert core in names
 
 
@@ -66,6 +67,25 @@ def test_validation_errors_are_host_side(L):
                                None, None) == ops.LI_ERR_INVALID  # nope_off > d_I
     assert L.li_absorb_queries(FAKE, ops.LI_FP32, 0, 1, 64, 128, FAKE, 0, None, 64, 256, FAKE,
                                None, None) == ops.LI_ERR_INVALID  # n_layers < 1
+    # the fused anchor call: B < k, max_len > ld, NULL outputs, too small a workspace
+    big = L.li_hs_anchor_workspace_bytes(4, 256)
+    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
+                          FAKE, 256, 100, FAKE, 200, FAKE, FAKE, big, None,
+                          None) == ops.LI_ERR_INVALID
+    assert b"B (100) < k (200)" in L.li_last_error()
+    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
+                          FAKE, 128, 100, FAKE, 10, FAKE, FAKE, big, None,
+                          None) == ops.LI_ERR_INVALID  # max_len > ld
+    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
+                          None, 256, 100, FAKE, 10, FAKE, FAKE, big, None,
+                          None) == ops.LI_ERR_INVALID  # scores NULL
+    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
+                          FAKE, 256, 100, FAKE, 10, FAKE, FAKE, big - 1, None,
+                          None) == ops.LI_ERR_INVALID  # workspace too small
+    assert b"workspace needs" in L.li_last_error()
+    # no queries: a no-op that succeeds without a device
+    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 0, 64, FAKE, FAKE, 256, ctypes.byref(c),
+                          FAKE, 256, 100, FAKE, 10, FAKE, FAKE, big, None, None) == ops.LI_OK
 
 
 def test_workspace_sizes(L):
@@ -73,3 +93,6 @@ def test_workspace_sizes(L):
     assert L.li_append_workspace_bytes(4, 7168, 256, 1) > 0
     assert L.li_hs_workspace_bytes(1, 4, 8192, 2048) >= 4 * 8192 * 4
     assert L.li_hs_workspace_bytes(3, 4, 8192, 2048) >= 3 * 4 * 8192 * 4
+    # the anchor workspace: the same size whatever the call shape up to 64 rows at the front
+    assert L.li_hs_anchor_workspace_bytes(4, 131072) > L.li_hs_anchor_workspace_bytes(4, 4096)
+    assert L.li_hs_anchor_workspace_bytes(64, 4096) >= 64 * 4096 * 4
