@@ -465,6 +465,37 @@ def test_hs_anchor_fused_equals_two_calls(case):
             assert np.array_equal(sel[i], O.pad(O.topk(row, wl.k), wl.k)), (rep, i)
 
 
+@pytest.mark.parametrize("n_seq", [64, 65])
+def test_hs_anchor_many_queries(n_seq):
+    """64 queries (the most whose key histograms the scorer builds) and 65
+    (the two-call route), ragged lengths from one page to 9,000 tokens:
+    li_hs_anchor equals li_score + li_hs_anchor_select bit for bit, and the
+    selections are the oracle's on the dumped scores."""
+    say(f"hs_anchor with {n_seq} queries")
+    rng = np.random.default_rng(n_seq)
+    lens = [int(x) for x in rng.integers(40, 9001, n_seq)]
+    lens[:3] = [40, 4096, 9000]
+    wl = W.small_decode(16, n_seq=n_seq, lens=lens, H=64, r=256, d_I=128, G=1, k=32, B=300,
+                        cache_dtype="bf16")
+    dw = DeviceWorkload(wl, hold_last=False)
+    dw.absorb(0)
+    L = dw.max_len
+    sc, cand, sel = ops.hs_anchor(dw.q_tilde[0], dw.w[0], dw.beta[0], dw.q_seq, dw.q_len, L,
+                                  dw.cache, wl.B, wl.k)
+    ref = ops.score(dw.q_tilde[0], dw.w[0], dw.beta[0], dw.q_seq, dw.q_len, L, dw.cache)
+    rc, rs = ops.hs_anchor_select(ref, dw.q_len, L, wl.B, wl.k)
+    torch.cuda.synchronize()
+    u, ur = sc.cpu().numpy(), ref.cpu().numpy()
+    cand, sel = cand.cpu().numpy(), sel.cpu().numpy()
+    assert np.array_equal(cand, rc.cpu().numpy()) and np.array_equal(sel, rs.cpu().numpy())
+    for i in range(wl.n_q):
+        n = int(wl.q_len[i])
+        assert np.array_equal(u[i, :n].view(np.uint32), ur[i, :n].view(np.uint32)), i
+        row = u[i, :n].astype(np.float64)
+        assert np.array_equal(cand[i], O.pad(O.hs_candidates(row, wl.B), wl.B)), i
+        assert np.array_equal(sel[i], O.pad(O.topk(row, wl.k), wl.k)), i
+
+
 def test_hs_anchor_candidates_only_and_scan_events():
     """li_hs_anchor with sel = NULL returns the candidate set alone, and its
     two timing events bracket the scoring launch (recorded, ordered)."""
