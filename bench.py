@@ -262,8 +262,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU; every GPU box here has one, "
-                                   "so --gpus must be 1"}), flush=True)
+        print(json.dumps({"error": "the indexer runs and is measured on one GPU (sharding across "
+                                   "GPUs is a design only), so --gpus must be 1"}), flush=True)
         sys.exit(2)
 
     import torch

@@ -47,7 +47,7 @@ extern "C" {
 typedef enum li_status {
   LI_OK = 0,
   LI_ERR_INVALID = 1,      /* bad pointer, size or combination of arguments */
-  LI_ERR_UNSUPPORTED = 2,  /* valid request outside what this build handles */
+  LI_ERR_UNSUPPORTED = 2,  /* valid request outside what the library implements */
   LI_ERR_HIP = 3           /* a HIP runtime call or kernel launch failed */
 } li_status;
 
