@@ -137,6 +137,24 @@ li_status li_absorb_queries(const void *q, li_dtype q_dt, int32_t n_layers, int3
                             float *beta, void *stream);
 
 /*
+ * li_append_absorb -- li_append_latent without a projection (P = NULL,
+ * d_model = cache->r) and li_absorb_queries with r = cache->r, in one
+ * launch: the decode step's two independent preludes (the new tokens' latents
+ * c_t of "Methodology", eqs. 1-2, stored into the cache, and the queries'
+ * absorption of eq. 6).  Arguments, layouts, limits and results are those of
+ * the two calls; the results are identical to theirs, bit for bit.  The
+ * queries' absorption reads nothing the append writes, so the two halves may
+ * run in any order.  Either n_tok or n_q may be 0.  Errors as for the two
+ * calls; on an error nothing is launched.
+ */
+li_status li_append_absorb(const void *x, li_dtype x_dt, int32_t n_tok, const float *rope_theta,
+                           int32_t r_R, const int32_t *seq_idx, const int32_t *pos,
+                           const li_cache *cache, const void *q, li_dtype q_dt, int32_t n_layers,
+                           int32_t n_q, int32_t H, int32_t d_I, const float *Dt,
+                           int64_t Dt_head_stride, const float *b, int32_t nope_off,
+                           float *q_tilde, float *beta, void *stream);
+
+/*
  * li_score -- score the shared cache for n_q queries ("Methodology", eq. 8):
  * scores[i * ld + t] = sum_h w[i,h] ReLU(q~[i,h,:] . c_t + beta[i,h]) for
  * 0 <= t < q_len[i], c_t read from sequence q_seq[i].  Entries at

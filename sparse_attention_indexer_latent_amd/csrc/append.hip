@@ -7,6 +7,7 @@
 //  2. one wavefront per token: y = sum of slices (or x itself), rotate the
 //     leading r_R coordinates pairwise by pos * theta_j, then store as fp32,
 //     bf16 (RNE) or fp8 E4M3FN with a per-token scale into the paged slot.
+#include "absorb_block.h"
 #include "li_device.h"
 #include "li_internal.h"
 
@@ -55,16 +56,19 @@ project_kernel(const T *__restrict__ x, const T *__restrict__ P, int n_tok, int 
     if (tok0 + t < n_tok) partial[((int64_t)blockIdx.z * nt + tok0 + t) * r + j] = acc[t];
 }
 
-// One wavefront per token, 4 per workgroup.  Phases are separated by block
-// barriers (every wave reaches them; inactive waves just skip the work).
+// One wavefront per token, 4 per workgroup (block bx of the store launch).
+// Phases are separated by block barriers (every wave reaches them; inactive
+// waves just skip the work).  Needs 4 r floats of dynamic LDS.
 template <typename T>
-__global__ void __launch_bounds__(256)
-store_kernel(const T *__restrict__ x, const float *__restrict__ partial, int n_slices, int n_tok,
-             int r, const float *__restrict__ theta, int r_R, const int32_t *__restrict__ seq_idx,
-             const int32_t *__restrict__ pos, CacheView cv) {
+__device__ __forceinline__ void store_block(const T *__restrict__ x, const float *__restrict__ partial,
+                                            int n_slices, int n_tok, int r,
+                                            const float *__restrict__ theta, int r_R,
+                                            const int32_t *__restrict__ seq_idx,
+                                            const int32_t *__restrict__ pos, const CacheView &cv,
+                                            int bx) {
   extern __shared__ float ys_all[];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int tok = blockIdx.x * 4 + wave;
+  const int tok = bx * 4 + wave;
   const bool active = tok < n_tok;
   float *ys = ys_all + wave * r;
   if (active) {
@@ -115,6 +119,43 @@ store_kernel(const T *__restrict__ x, const float *__restrict__ partial, int n_s
   }
 }
 
+template <typename T>
+__global__ void __launch_bounds__(256)
+store_kernel(const T *__restrict__ x, const float *__restrict__ partial, int n_slices, int n_tok,
+             int r, const float *__restrict__ theta, int r_R, const int32_t *__restrict__ seq_idx,
+             const int32_t *__restrict__ pos, CacheView cv) {
+  store_block<T>(x, partial, n_slices, n_tok, r, theta, r_R, seq_idx, pos, cv, blockIdx.x);
+}
+
+// The decode step's two independent preludes in one launch (each is far too
+// small to fill the GPU, and a launch costs microseconds): the first n_abs
+// workgroups absorb the queries (grid gx x gy x gz of the absorption, x
+// fastest), the rest store the new tokens (no projection).
+struct AbsorbArgs {
+  const void *q;
+  int n_q, H, d_I;
+  const float *Dt;
+  int64_t head_stride;
+  const float *b;
+  int nope_off, r;
+  float *q_tilde, *beta;
+  int gx, gy, n_abs;
+};
+
+template <bool BF16Q, typename T>
+__global__ void __launch_bounds__(256)
+append_absorb_kernel(const T *__restrict__ x, int n_tok, int r, const float *__restrict__ theta,
+                     int r_R, const int32_t *__restrict__ seq_idx, const int32_t *__restrict__ pos,
+                     CacheView cv, AbsorbArgs a) {
+  const int blk = blockIdx.x;
+  if (blk < a.n_abs) {  // uniform per workgroup
+    absorb_block<BF16Q>(a.q, a.n_q, a.H, a.d_I, a.Dt, a.head_stride, a.b, a.nope_off, a.r,
+                        a.q_tilde, a.beta, blk % a.gx, (blk / a.gx) % a.gy, blk / (a.gx * a.gy));
+  } else {
+    store_block<T>(x, nullptr, 0, n_tok, r, theta, r_R, seq_idx, pos, cv, blk - a.n_abs);
+  }
+}
+
 }  // namespace
 
 size_t append_ws_bytes(int n_tok, int d_model, int r, bool has_P) {
@@ -151,6 +192,39 @@ hipError_t launch_append(const void *x, int x_dt, int n_tok, int d_model, const 
   else
     store_kernel<uint16_t><<<grid, 256, lds, st>>>((const uint16_t *)x, partial, n_slices, n_tok,
                                                    r, theta, r_R, seq_idx, pos, cv);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_absorb(const void *x, int x_dt, int n_tok, const float *theta, int r_R,
+                                const int32_t *seq_idx, const int32_t *pos, const li_cache &cache,
+                                const void *q, int q_dt, int n_layers, int n_q, int H, int d_I,
+                                const float *Dt, int64_t Dt_head_stride, const float *b,
+                                int nope_off, float *q_tilde, float *beta, hipStream_t st) {
+  const int r = cache.r;
+  const CacheView cv = view_of(cache);
+  const bool per_head = Dt_head_stride != 0;
+  const int n_rows = per_head ? n_q : n_q * H;
+  AbsorbArgs a{q, n_q, H, d_I, Dt, Dt_head_stride, b, nope_off, r, q_tilde, beta,
+               (r + 31) / 32, (n_rows + 31) / 32, 0};
+  const int64_t n_abs = (int64_t)a.gx * a.gy * n_layers * (per_head ? H : 1);
+  const int64_t n_store = (n_tok + 3) / 4;
+  if (n_abs + n_store > (int64_t)1 << 30) return hipErrorInvalidConfiguration;
+  a.n_abs = (int)n_abs;
+  const dim3 grid((unsigned)(n_abs + n_store));
+  const size_t lds = 4 * r * sizeof(float);
+  const bool bq = q_dt == LI_BF16, bx = x_dt == LI_BF16;
+  if (bq && bx)
+    append_absorb_kernel<true, uint16_t><<<grid, 256, lds, st>>>(
+        (const uint16_t *)x, n_tok, r, theta, r_R, seq_idx, pos, cv, a);
+  else if (bq)
+    append_absorb_kernel<true, float><<<grid, 256, lds, st>>>((const float *)x, n_tok, r, theta,
+                                                              r_R, seq_idx, pos, cv, a);
+  else if (bx)
+    append_absorb_kernel<false, uint16_t><<<grid, 256, lds, st>>>(
+        (const uint16_t *)x, n_tok, r, theta, r_R, seq_idx, pos, cv, a);
+  else
+    append_absorb_kernel<false, float><<<grid, 256, lds, st>>>((const float *)x, n_tok, r, theta,
+                                                               r_R, seq_idx, pos, cv, a);
   return hipGetLastError();
 }
 

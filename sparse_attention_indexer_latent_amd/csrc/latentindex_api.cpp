@@ -81,10 +81,14 @@ size_t li_append_workspace_bytes(int32_t n_tok, int32_t d_model, int32_t r, int3
   return li::append_ws_bytes(n_tok, d_model, r, has_P != 0);
 }
 
-li_status li_append_latent(const void *x, li_dtype x_dt, int32_t n_tok, int32_t d_model,
-                           const void *P, const float *rope_theta, int32_t r_R,
-                           const int32_t *seq_idx, const int32_t *pos, const li_cache *cache,
-                           void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+// Argument checks shared by li_append_latent and li_append_absorb (pointers
+// only when n_tok > 0).
+static li_status check_append_args(const void *x, li_dtype x_dt, int32_t n_tok, int32_t d_model,
+                                   const void *P, const float *rope_theta, int32_t r_R,
+                                   const int32_t *seq_idx, const int32_t *pos,
+                                   const li_cache *cache) {
   li_status s = check_cache(cache, true);
   if (s != LI_OK) return s;
   if (n_tok < 0) return fail(LI_ERR_INVALID, "n_tok < 0");
@@ -93,8 +97,36 @@ li_status li_append_latent(const void *x, li_dtype x_dt, int32_t n_tok, int32_t 
   if (!P && d_model != cache->r) return fail(LI_ERR_INVALID, "P is NULL but d_model (%d) != r (%d)", d_model, cache->r);
   if (r_R < 0 || r_R > cache->r || (r_R & 1)) return fail(LI_ERR_INVALID, "r_R = %d must be even and in [0, r]", r_R);
   if ((r_R > 0) != (rope_theta != nullptr)) return fail(LI_ERR_INVALID, "rope_theta must be given exactly when r_R > 0");
+  if (n_tok > 0 && (!x || !seq_idx || !pos)) return fail(LI_ERR_INVALID, "x/seq_idx/pos is NULL");
+  return LI_OK;
+}
+
+// Argument checks shared by li_absorb_queries and li_append_absorb.
+static li_status check_absorb_args(const void *q, li_dtype q_dt, int32_t n_layers, int32_t n_q,
+                                   int32_t H, int32_t d_I, const float *Dt,
+                                   int64_t Dt_head_stride, int32_t nope_off, int32_t r,
+                                   const float *q_tilde) {
+  if (q_dt != LI_FP32 && q_dt != LI_BF16) return fail(LI_ERR_INVALID, "q dtype must be FP32 or BF16");
+  if (n_layers < 1 || n_layers > 64) return fail(LI_ERR_INVALID, "n_layers = %d out of [1, 64]", n_layers);
+  if (n_q < 0) return fail(LI_ERR_INVALID, "n_q < 0");
+  if (H <= 0 || H > 1024 || d_I <= 0 || d_I > 1024 || r <= 0 || r > 1024)
+    return fail(LI_ERR_INVALID, "H/d_I/r out of range (1..1024)");
+  if (nope_off < 0 || nope_off > d_I) return fail(LI_ERR_INVALID, "nope_off out of [0, d_I]");
+  if (Dt_head_stride < 0) return fail(LI_ERR_INVALID, "Dt_head_stride < 0");
+  if (d_I % 4 || Dt_head_stride % 4) return fail(LI_ERR_UNSUPPORTED, "d_I and Dt_head_stride must be multiples of 4");
+  if (n_q > 0 && (!q || !Dt || !q_tilde)) return fail(LI_ERR_INVALID, "q/Dt/q_tilde is NULL");
+  return LI_OK;
+}
+
+extern "C" {
+
+li_status li_append_latent(const void *x, li_dtype x_dt, int32_t n_tok, int32_t d_model,
+                           const void *P, const float *rope_theta, int32_t r_R,
+                           const int32_t *seq_idx, const int32_t *pos, const li_cache *cache,
+                           void *ws, size_t ws_bytes, void *stream) {
+  li_status s = check_append_args(x, x_dt, n_tok, d_model, P, rope_theta, r_R, seq_idx, pos, cache);
+  if (s != LI_OK) return s;
   if (n_tok == 0) return LI_OK;
-  if (!x || !seq_idx || !pos) return fail(LI_ERR_INVALID, "x/seq_idx/pos is NULL");
   size_t need = li::append_ws_bytes(n_tok, d_model, cache->r, P != nullptr);
   if (need && (!ws || ws_bytes < need)) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
   if ((s = check_device()) != LI_OK) return s;
@@ -107,21 +139,33 @@ li_status li_absorb_queries(const void *q, li_dtype q_dt, int32_t n_layers, int3
                             int32_t H, int32_t d_I, const float *Dt, int64_t Dt_head_stride,
                             const float *b, int32_t nope_off, int32_t r, float *q_tilde,
                             float *beta, void *stream) {
-  if (q_dt != LI_FP32 && q_dt != LI_BF16) return fail(LI_ERR_INVALID, "q dtype must be FP32 or BF16");
-  if (n_layers < 1 || n_layers > 64) return fail(LI_ERR_INVALID, "n_layers = %d out of [1, 64]", n_layers);
-  if (n_q < 0) return fail(LI_ERR_INVALID, "n_q < 0");
-  if (H <= 0 || H > 1024 || d_I <= 0 || d_I > 1024 || r <= 0 || r > 1024)
-    return fail(LI_ERR_INVALID, "H/d_I/r out of range (1..1024)");
-  if (nope_off < 0 || nope_off > d_I) return fail(LI_ERR_INVALID, "nope_off out of [0, d_I]");
-  if (Dt_head_stride < 0) return fail(LI_ERR_INVALID, "Dt_head_stride < 0");
-  if (d_I % 4 || Dt_head_stride % 4) return fail(LI_ERR_UNSUPPORTED, "d_I and Dt_head_stride must be multiples of 4");
-  if (n_q == 0) return LI_OK;
-  if (!q || !Dt || !q_tilde) return fail(LI_ERR_INVALID, "q/Dt/q_tilde is NULL");
-  li_status s = check_device();
-  if (s != LI_OK) return s;
+  li_status s = check_absorb_args(q, q_dt, n_layers, n_q, H, d_I, Dt, Dt_head_stride, nope_off, r,
+                                  q_tilde);
+  if (s != LI_OK || n_q == 0) return s;
+  if ((s = check_device()) != LI_OK) return s;
   return hip_status(li::launch_absorb(q, q_dt, n_layers, n_q, H, d_I, Dt, Dt_head_stride, b, nope_off, r,
                                       q_tilde, beta, (hipStream_t)stream),
                     "li_absorb_queries launch");
+}
+
+li_status li_append_absorb(const void *x, li_dtype x_dt, int32_t n_tok, const float *rope_theta,
+                           int32_t r_R, const int32_t *seq_idx, const int32_t *pos,
+                           const li_cache *cache, const void *q, li_dtype q_dt, int32_t n_layers,
+                           int32_t n_q, int32_t H, int32_t d_I, const float *Dt,
+                           int64_t Dt_head_stride, const float *b, int32_t nope_off,
+                           float *q_tilde, float *beta, void *stream) {
+  li_status s = check_append_args(x, x_dt, n_tok, cache ? cache->r : 1, nullptr, rope_theta, r_R,
+                                   seq_idx, pos, cache);
+  if (s != LI_OK) return s;
+  if ((s = check_absorb_args(q, q_dt, n_layers, n_q, H, d_I, Dt, Dt_head_stride, nope_off,
+                             cache->r, q_tilde)) != LI_OK)
+    return s;
+  if (n_tok == 0 && n_q == 0) return LI_OK;
+  if ((s = check_device()) != LI_OK) return s;
+  return hip_status(li::launch_append_absorb(x, x_dt, n_tok, rope_theta, r_R, seq_idx, pos, *cache,
+                                             q, q_dt, n_layers, n_q, H, d_I, Dt, Dt_head_stride,
+                                             b, nope_off, q_tilde, beta, (hipStream_t)stream),
+                    "li_append_absorb launch");
 }
 
 static li_status check_score_args(const void *q_tilde, li_dtype qt_dt, const float *w, int32_t n_q,

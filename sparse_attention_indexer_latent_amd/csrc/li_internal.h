@@ -34,6 +34,13 @@ size_t append_ws_bytes(int n_tok, int d_model, int r, bool has_P);
 hipError_t launch_append(const void *x, int x_dt, int n_tok, int d_model, const void *P,
                          const float *theta, int r_R, const int32_t *seq_idx,
                          const int32_t *pos, const li_cache &cache, void *ws, hipStream_t st);
+// Append without projection (x has cache.r columns) and absorption with
+// r = cache.r, in one launch.
+hipError_t launch_append_absorb(const void *x, int x_dt, int n_tok, const float *theta, int r_R,
+                                const int32_t *seq_idx, const int32_t *pos, const li_cache &cache,
+                                const void *q, int q_dt, int n_layers, int n_q, int H, int d_I,
+                                const float *Dt, int64_t Dt_head_stride, const float *b,
+                                int nope_off, float *q_tilde, float *beta, hipStream_t st);
 
 // absorb.hip
 hipError_t launch_absorb(const void *q, int q_dt, int n_layers, int n_q, int H, int d_I,

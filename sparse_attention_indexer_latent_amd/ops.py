@@ -56,6 +56,9 @@ _SIGS = {
                                 ctypes.POINTER(LiCacheStruct), _P, _SZ, _P]),
     "li_absorb_queries": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _I32, _I32, _P, _P,
                                  _P]),
+    "li_append_absorb": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, ctypes.POINTER(LiCacheStruct),
+                                _P, _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _I32, _P, _P,
+                                _P]),
     "li_score": (_I32, [_P, _I32, _P, _P, _I32, _I32, _P, _P, _I32,
                         ctypes.POINTER(LiCacheStruct), _P, _I64, _P]),
     "li_topk_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
@@ -209,6 +212,41 @@ def absorb_queries(q: torch.Tensor, Dt: torch.Tensor, b: Optional[torch.Tensor] 
                                    stride, _ptr(b), no, r, q_tilde.data_ptr(), _ptr(beta),
                                    _stream()))
     return q_tilde, beta
+
+
+def append_absorb(x: torch.Tensor, cache: Cache, seq_idx: torch.Tensor, pos: torch.Tensor,
+                  q: torch.Tensor, Dt: torch.Tensor, b: Optional[torch.Tensor],
+                  nope_off: Optional[int], q_tilde: torch.Tensor, beta: Optional[torch.Tensor],
+                  rope_theta: Optional[torch.Tensor] = None, per_head: bool = False) -> None:
+    """append_latent(x, cache, seq_idx, pos, rope_theta=rope_theta) (no
+    projection: x is [n_tok, r]) and absorb_queries(q, Dt, b, nope_off,
+    q_tilde, beta, per_head) in one launch; operands as for those two."""
+    _need(x, "x", (torch.float32, torch.bfloat16))
+    _need(seq_idx, "seq_idx", torch.int32)
+    _need(pos, "pos", torch.int32)
+    _need(q, "q", (torch.float32, torch.bfloat16))
+    _need(Dt, "Dt", torch.float32)
+    _need(q_tilde, "q_tilde", torch.float32)
+    if b is not None:
+        _need(b, "b", torch.float32)
+    if beta is not None:
+        _need(beta, "beta", torch.float32)
+    n_tok, d_model = x.shape
+    if d_model != cache.r or Dt.shape[-2] != cache.r:
+        raise ValueError(f"x and Dt must have r = {cache.r} columns / rows")
+    r_R = 0
+    if rope_theta is not None:
+        _need(rope_theta, "rope_theta", torch.float32)
+        r_R = 2 * rope_theta.numel()
+    L = q.shape[0] if q.dim() == 4 else 1
+    n_q, H, d_I = q.shape[-3:]
+    stride = cache.r * d_I if per_head else 0
+    no = d_I if nope_off is None else nope_off
+    _check(lib().li_append_absorb(x.data_ptr(), _dtype_code(x), n_tok, _ptr(rope_theta), r_R,
+                                  seq_idx.data_ptr(), pos.data_ptr(), cache.struct(),
+                                  q.data_ptr(), _dtype_code(q), L, n_q, H, d_I, Dt.data_ptr(),
+                                  stride, _ptr(b), no, q_tilde.data_ptr(), _ptr(beta),
+                                  _stream()))
 
 
 def score(q_tilde: torch.Tensor, w: torch.Tensor, beta: Optional[torch.Tensor],

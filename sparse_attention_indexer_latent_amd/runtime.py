@@ -106,9 +106,11 @@ class DeviceWorkload:
     # cache (the dominant kernel) can be timed with events on its stream:
     # pre (append + every layer's absorb), scan (layer-0 score), post (the rest).
     def _pre(self, append: bool) -> None:
-        if append:
-            self.append()
-        self.absorb()
+        if append:  # both in one launch
+            ops.append_absorb(self.x_new, self.cache, self.new_seq, self.new_pos, self.q, self.Dt,
+                              self.b, self.wl.nope_off, self.q_tilde, self.beta)
+        else:
+            self.absorb()
 
     def _full_post(self) -> None:
         wl = self.wl

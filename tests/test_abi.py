@@ -18,7 +18,7 @@ def test_every_declared_symbol_is_exported(L):
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
-    for core in ["li_append_latent", "li_absorb_queries", "li_score", "li_topk", "li_hs_anchor",
+    for core in ["li_append_latent", "li_absorb_queries", "li_append_absorb", "li_score", "li_topk", "li_hs_anchor",
                  "li_hs_anchor_select", "li_hs_select"]:
         assert core in names
 
@@ -67,6 +67,19 @@ def test_validation_errors_are_host_side(L):
                                None, None) == ops.LI_ERR_INVALID  # nope_off > d_I
     assert L.li_absorb_queries(FAKE, ops.LI_FP32, 0, 1, 64, 128, FAKE, 0, None, 64, 256, FAKE,
                                None, None) == ops.LI_ERR_INVALID  # n_layers < 1
+    # the one-launch prelude: each half's own checks
+    assert L.li_append_absorb(FAKE, ops.LI_FP32, 4, FAKE, 3, FAKE, FAKE, ctypes.byref(c), FAKE,
+                              ops.LI_FP32, 1, 1, 64, 128, FAKE, 0, None, 64, FAKE, None,
+                              None) == ops.LI_ERR_INVALID  # odd r_R
+    assert L.li_append_absorb(FAKE, ops.LI_FP32, 4, None, 0, FAKE, FAKE, ctypes.byref(c), FAKE,
+                              ops.LI_FP32, 0, 1, 64, 128, FAKE, 0, None, 64, FAKE, None,
+                              None) == ops.LI_ERR_INVALID  # n_layers < 1
+    assert L.li_append_absorb(FAKE, ops.LI_FP32, 4, None, 0, FAKE, FAKE, ctypes.byref(c), FAKE,
+                              ops.LI_FP32, 1, 1, 64, 130, FAKE, 0, None, 64, FAKE, None,
+                              None) == ops.LI_ERR_UNSUPPORTED  # d_I not a multiple of 4
+    assert L.li_append_absorb(FAKE, ops.LI_FP32, 0, None, 0, FAKE, FAKE, ctypes.byref(c), FAKE,
+                              ops.LI_FP32, 1, 0, 64, 128, FAKE, 0, None, 64, FAKE, None,
+                              None) == ops.LI_OK  # nothing to do: no launch
     # the fused anchor call: B < k, max_len > ld, NULL outputs, too small a workspace
     big = L.li_hs_anchor_workspace_bytes(4, 256)
     assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),

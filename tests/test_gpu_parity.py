@@ -124,6 +124,53 @@ def test_absorb_matches_oracle(per_head, qdt, n_layers):
             assert np.max(np.abs(beta[l, s] - ob)) <= 1e-5 * (np.abs(ob).max() + 1), (l, s)
 
 
+@pytest.mark.parametrize("dtype,per_head,xdt,qdt,n_tok,n_q", [
+    ("bf16", False, torch.float32, torch.float32, 37, 4),
+    ("fp8", True, torch.bfloat16, torch.bfloat16, 61, 3),
+    ("fp32", False, torch.float32, torch.bfloat16, 0, 2),
+    ("bf16", True, torch.bfloat16, torch.float32, 5, 0),
+])
+def test_append_absorb_equals_the_two_calls(dtype, per_head, xdt, qdt, n_tok, n_q):
+    """The one-launch prelude writes exactly what li_append_latent (no
+    projection, with rope) and li_absorb_queries write, bit for bit; both of
+    those are checked against the oracle above."""
+    say(f"append_absorb dtype={dtype} per_head={per_head} x={xdt} q={qdt} n_tok={n_tok} n_q={n_q}")
+    rng = np.random.default_rng(17 + n_tok + n_q)
+    r, r_R, L, H, d_I, no = 256, 64, 3, 64, 128, 64
+    x = torch.from_numpy(rng.standard_normal((n_tok, r)).astype(np.float32)).cuda().to(xdt)
+    theta = torch.from_numpy((10000.0 ** (-np.arange(r_R // 2) * 2.0 / r_R)).astype(np.float32)).cuda()
+    seq = torch.from_numpy(rng.integers(0, 2, n_tok).astype(np.int32)).cuda()
+    pos = torch.from_numpy(rng.permutation(256)[:n_tok].astype(np.int32)).cuda()
+    q = torch.from_numpy(rng.standard_normal((L, n_q, H, d_I)).astype(np.float32)).cuda().to(qdt)
+    Dt = torch.from_numpy((rng.standard_normal((L, H, r, d_I) if per_head else (L, r, d_I)) / 16
+                           ).astype(np.float32)).cuda()
+    b = torch.from_numpy(rng.standard_normal((L, d_I - no)).astype(np.float32)).cuda()
+    bt = torch.arange(8, dtype=torch.int32, device="cuda").reshape(2, 4)
+    caches, outs = [], []
+    for fused in (False, True):
+        cache = ops.Cache.empty(8, r, dtype, bt)
+        cache.data.view(torch.uint8).fill_(0x5a)  # same prior contents for both
+        if cache.scale is not None:
+            cache.scale.fill_(3.0)
+        qt = torch.full((L, n_q, H, r), 7.0, device="cuda")
+        beta = torch.full((L, n_q, H), 7.0, device="cuda")
+        if fused:
+            ops.append_absorb(x, cache, seq, pos, q, Dt, b, no, qt, beta, rope_theta=theta,
+                              per_head=per_head)
+        else:
+            if n_tok:
+                ops.append_latent(x, cache, seq, pos, rope_theta=theta)
+            if n_q:
+                ops.absorb_queries(q, Dt, b, no, q_tilde=qt, beta=beta, per_head=per_head)
+        caches.append(cache)
+        outs.append((qt, beta))
+    torch.cuda.synchronize()
+    assert torch.equal(caches[0].data.view(torch.uint8), caches[1].data.view(torch.uint8))
+    if dtype == "fp8":
+        assert torch.equal(caches[0].scale, caches[1].scale)
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 # ------------------------------------------------------------------- score ---
 
 def _scores_vs_oracle(wl, dw, rtol, layers=None, sample=None):
