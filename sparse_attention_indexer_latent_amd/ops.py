@@ -242,6 +242,17 @@ def append_absorb(x: torch.Tensor, cache: Cache, seq_idx: torch.Tensor, pos: tor
     n_q, H, d_I = q.shape[-3:]
     stride = cache.r * d_I if per_head else 0
     no = d_I if nope_off is None else nope_off
+    # the library takes raw pointers: check the extents it will touch
+    if seq_idx.numel() != n_tok or pos.numel() != n_tok:
+        raise ValueError("seq_idx and pos must hold n_tok entries")
+    if Dt.numel() != L * (H if per_head else 1) * cache.r * d_I:
+        raise ValueError(f"Dt must hold {L} layers of {'H x ' if per_head else ''}[r, d_I]")
+    if q_tilde.numel() != L * n_q * H * cache.r:
+        raise ValueError("q_tilde must be [layers, n_q, H, r]")
+    if beta is not None and beta.numel() != L * n_q * H:
+        raise ValueError("beta must be [layers, n_q, H]")
+    if b is not None and b.numel() != L * (d_I - no):
+        raise ValueError("b must be [layers, d_I - nope_off]")
     _check(lib().li_append_absorb(x.data_ptr(), _dtype_code(x), n_tok, _ptr(rope_theta), r_R,
                                   seq_idx.data_ptr(), pos.data_ptr(), cache.struct(),
                                   q.data_ptr(), _dtype_code(q), L, n_q, H, d_I, Dt.data_ptr(),
