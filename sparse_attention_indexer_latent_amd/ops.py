@@ -172,8 +172,12 @@ def append_latent(x: torch.Tensor, cache: Cache, seq_idx: torch.Tensor, pos: tor
     _need(seq_idx, "seq_idx", torch.int32)
     _need(pos, "pos", torch.int32)
     n_tok, d_model = x.shape
+    if seq_idx.numel() != n_tok or pos.numel() != n_tok:
+        raise ValueError("seq_idx and pos must hold n_tok entries")
     if P is not None:
         _need(P, "P", x.dtype)
+        if P.numel() != d_model * cache.r:
+            raise ValueError("P must be [d_model, r]")
     r_R = 0
     if rope_theta is not None:
         _need(rope_theta, "rope_theta", torch.float32)
@@ -204,10 +208,18 @@ def absorb_queries(q: torch.Tensor, Dt: torch.Tensor, b: Optional[torch.Tensor] 
     if b is not None:
         _need(b, "b", torch.float32)
     lead = (L,) if layered else ()
+    if Dt.numel() != L * (H if per_head else 1) * r * d_I:
+        raise ValueError("Dt must hold [r, d_I] (per head with per_head) for every layer")
+    if b is not None and b.numel() != L * (d_I - no):
+        raise ValueError("b must be [layers, d_I - nope_off]")
     if q_tilde is None:
         q_tilde = torch.empty(lead + (n_q, H, r), dtype=torch.float32, device=q.device)
     if beta is None:
         beta = torch.empty(lead + (n_q, H), dtype=torch.float32, device=q.device)
+    _need(q_tilde, "q_tilde", torch.float32)
+    _need(beta, "beta", torch.float32)
+    if q_tilde.numel() != L * n_q * H * r or beta.numel() != L * n_q * H:
+        raise ValueError("q_tilde must be [layers, n_q, H, r] and beta [layers, n_q, H]")
     _check(lib().li_absorb_queries(q.data_ptr(), _dtype_code(q), L, n_q, H, d_I, Dt.data_ptr(),
                                    stride, _ptr(b), no, r, q_tilde.data_ptr(), _ptr(beta),
                                    _stream()))
