@@ -21,18 +21,28 @@ Sources (the pages this follows; sections, equations and tables named):
        no infinities, one NaN mantissa, max 448) -- named by the cache layout,
        not by the pages.
 
-Pins (tests/test_oracle_*.py; none re-types the formula it checks):
+Pins (tests/test_oracle_pins.py; none re-types the formula it checks):
   e4m3 decode/encode  torch.float8_e4m3fn over all 256 codes and all ties
-  bf16 rounding       torch.bfloat16 cast, including every tie case
+  bf16_encode         torch.bfloat16 cast, including every tie case
+  bf16_decode         torch.bfloat16 -> float64 over all 65,536 bit patterns
   quantize_fp8        invariants: amax code is +-448, |error| <= half step
   reconstructed score eq. 7 identity vs the absorbed score (1e-5 rel, fp64);
                       D = I, H = 1 reduces to max(C q, 0) (library matmul);
                       all-positive operands reduce to one GEMV;
                       exact positive homogeneity u(4c) = 4 u(c)
   topk                brute-force rank definition on tiny inputs with ties
-  hs_select           subset / equality invariants of the HS definition
-  rope                norm preservation, identity at t = 0, and eq. 4
+  hs_candidates/      subset / equality invariants of the HS definition
+    hs_follower
+  rope_rotate         norm preservation, identity at t = 0, and eq. 4
                       commutation with a complex-block decoder
+  project_latent      a per-column dot-product loop (no rotation); P = I
+                      equals rope_rotate; a rotation built with Python
+                      complex numbers fixes the R-branch-first column order
+                      and projection-then-rotation (eqs. 1-2)
+  decode_group        every score against plain-Python sums and every
+                      selection against the brute-force rank; B >= L gives
+                      HS = full for every follower; a follower with the
+                      anchor's operands returns S_anchor; HS picks stay in C
   accounting          the numbers printed in [P4] and [P1] (tests/golden)
 Parity unpinned: none of the functions above.  The planted-token structure of
 the synthetic workloads is not pinned by the pages (they print no scores).
@@ -97,8 +107,10 @@ def e4m3fn_encode(x32: np.ndarray) -> np.ndarray:
 
 
 def bf16_decode(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns: the upper half of an fp32 pattern."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
-    return b.view(np.float32).astype(F64)
+    with np.errstate(invalid="ignore"):  # NaN patterns stay NaN
+        return b.view(np.float32).astype(F64)
 
 
 def bf16_encode(x32: np.ndarray) -> np.ndarray:

@@ -258,3 +258,174 @@ def test_storage_and_scoring_accounting_golden():
     assert full // 4 // ((hs - T) // 3) == g["expect_follower_ratio"]
     # at L = B the HS count equals the full scan count (no positions saved)
     assert O.scored_positions(8192, 4, 8192) == O.scored_positions(8192, 4)
+
+
+# ---------------------------------------------------- bf16 decode (codec) ---
+
+def test_bf16_decode_matches_torch_every_pattern():
+    """All 65,536 bit patterns: the exact value torch.bfloat16 assigns them
+    (NaN patterns decode to NaN)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_decode(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    # landmarks of the format: 1.0, -2.0, the smallest subnormal, +inf
+    assert got[0x3F80] == 1.0 and got[0xC000] == -2.0
+    assert got[0x0001] == 2.0 ** -133 and np.isposinf(got[0x7F80])
+    # encode then decode is the identity on every finite, non-NaN pattern
+    fin = np.isfinite(ref)
+    assert np.array_equal(O.bf16_encode(got[fin].astype(np.float32)), bits[fin])
+
+
+# ------------------------------------------------ latent projection + RoPE ---
+
+def _loop_projection(x, P):
+    """z[t, j] = sum_i x[t, i] P[i, j], one column at a time in plain Python."""
+    n, d = x.shape
+    r = P.shape[1]
+    z = np.zeros((n, r))
+    for t in range(n):
+        for j in range(r):
+            z[t, j] = math.fsum(float(x[t, i]) * float(P[i, j]) for i in range(d))
+    return z
+
+
+def test_project_latent_without_rotation_is_the_projection():
+    rng = np.random.default_rng(20)
+    x = rng.standard_normal((5, 9))
+    P = rng.standard_normal((9, 6))
+    pos = np.arange(5)
+    for theta in (None, np.zeros(0)):
+        z = O.project_latent(x, P, theta, pos)
+        assert np.allclose(z, _loop_projection(x, P), rtol=1e-13, atol=1e-13)
+    assert np.array_equal(O.project_latent(x, None, None, pos), x)   # P = None: x is the latent
+
+
+def test_project_latent_identity_projection_is_the_rotation():
+    rng = np.random.default_rng(21)
+    z = rng.standard_normal((7, 8))
+    pos = rng.integers(0, 5000, 7)
+    theta = np.array([0.5, 0.03])
+    assert np.allclose(O.project_latent(z, np.eye(8), theta, pos), O.rope_rotate(z, pos, theta),
+                       rtol=0, atol=1e-14)
+
+
+def test_project_latent_branch_order_and_rotation_after_projection():
+    """eqs. 1-2: c_t = [Q_t P_R^T x ; P_N^T x] -- the R branch takes the first
+    r_R columns, it is rotated after the projection, and the N branch is the
+    plain projection.  The expected value is built with Python complex
+    numbers: pair (2j, 2j+1) of P_R^T x times exp(i t theta_j)."""
+    import cmath
+    rng = np.random.default_rng(22)
+    n, d, r, rR = 4, 7, 10, 4
+    x = rng.standard_normal((n, d))
+    P = rng.standard_normal((d, r))
+    theta = np.array([0.7, 0.011])
+    pos = np.array([0, 3, 1000, 77777])
+    y = _loop_projection(x, P)
+    ref = y.copy()
+    for t in range(n):
+        for j in range(rR // 2):
+            zc = complex(y[t, 2 * j], y[t, 2 * j + 1]) * cmath.exp(1j * pos[t] * theta[j])
+            ref[t, 2 * j], ref[t, 2 * j + 1] = zc.real, zc.imag
+    got = O.project_latent(x, P, theta, pos)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # the alternative readings give other values: rotation before projection,
+    # or the rotated branch at the end of the latent
+    x_rot = O.rope_rotate(x, pos, theta)
+    assert not np.allclose(x_rot @ P, got, atol=1e-3)
+    tail_first = np.concatenate([P[:, rR:], P[:, :rR]], axis=1)
+    alt = O.project_latent(x, tail_first, theta, pos)
+    assert not np.allclose(np.concatenate([alt[:, r - rR:], alt[:, :r - rR]], axis=1), got,
+                           atol=1e-3)
+
+
+# --------------------------------------------------------- whole group step ---
+
+def _tiny_group(seed=30, L=300, B=None, tie=False):
+    from sparse_attention_indexer_latent_amd import workloads as W
+    wl = W.small_decode(seed, n_seq=1, lens=[L], H=3, r=6, d_I=5, G=4, k=7, B=B,
+                        cache_dtype="fp32", nope_off=2, bias=True)
+    if tie:  # duplicated latent rows force exact score ties
+        lat = wl.latent(0)
+        lat[100:110] = lat[5]
+    return wl
+
+
+def _brute_scores(C, q, Dt, b, nope_off, w):
+    """u_t = sum_h w_h max(q_h . k_t, 0), k_t[d] = sum_j Dt[j, d] c_t[j]
+    (+ b on d >= nope_off), every sum in plain Python."""
+    L, r = C.shape
+    H, d_I = q.shape
+    u = np.zeros(L)
+    for t in range(L):
+        k = [math.fsum(Dt[j, d] * C[t, j] for j in range(r)) + (b[d - nope_off] if d >= nope_off else 0.0)
+             for d in range(d_I)]
+        u[t] = math.fsum(w[h] * max(math.fsum(q[h, d] * k[d] for d in range(d_I)), 0.0)
+                         for h in range(H))
+    return u
+
+
+def test_decode_group_scores_are_the_brute_force_sums():
+    wl = _tiny_group(L=60, B=16)
+    out = O.decode_group(wl, 0, hs=True)
+    C = wl.latent(0).astype(np.float64)
+    for l in range(wl.G):
+        ref = _brute_scores(C, wl.q[l, 0].astype(np.float64), wl.Dt[l].astype(np.float64),
+                            wl.b[l].astype(np.float64), wl.nope_off, wl.w[l, 0].astype(np.float64))
+        assert np.allclose(out["u"][l], ref, rtol=1e-12, atol=1e-12), l
+        assert np.array_equal(out["sel"][l], _brute(list(ref), wl.k))
+    cand = out["cand"]
+    assert np.array_equal(cand, _brute(list(out["u"][0]), wl.B))
+    for l in range(1, wl.G):
+        # the follower's scores on C are its full-scan scores restricted to C
+        assert np.array_equal(out["u_f"][l], out["u"][l][cand])
+        assert set(out["hs_sel"][l]) <= set(cand)
+
+
+@pytest.mark.parametrize("tie", [False, True])
+def test_decode_group_hs_equals_full_when_budget_covers_context(tie):
+    """B >= L: the candidate set is every position, so HS selects what the
+    full scan selects, for every follower (ties included)."""
+    wl = _tiny_group(L=300, B=300, tie=tie)
+    out = O.decode_group(wl, 0, hs=True)
+    assert np.array_equal(out["cand"], np.arange(300))
+    for l in range(wl.G):
+        assert np.array_equal(out["hs_sel"][l], out["sel"][l]), l
+
+
+def test_decode_group_follower_with_the_anchors_operands_returns_its_selection():
+    """A follower whose query, decoder, bias and head weights equal the
+    anchor's scores exactly like it, so its top-k within C is S_anchor."""
+    wl = _tiny_group(L=400, B=40, tie=True)
+    for l in range(1, wl.G):
+        wl.q[l], wl.Dt[l], wl.b[l], wl.w[l] = wl.q[0], wl.Dt[0], wl.b[0], wl.w[0]
+    out = O.decode_group(wl, 0, hs=True)
+    assert len(out["cand"]) == 40
+    for l in range(1, wl.G):
+        assert np.array_equal(out["hs_sel"][l], out["hs_sel"][0]), l
+        assert np.array_equal(out["hs_sel"][l], out["sel"][0]), l
+
+
+def test_decode_group_hs_differs_from_full_when_budget_is_small():
+    """With B < L a follower may lose tokens the anchor did not propose:
+    HS selections stay inside C, and for some follower (distinct decoders)
+    differ from the full scan.  Only the anchor's layer is scanned fully
+    when layers=[0]."""
+    wl = _tiny_group(L=500, B=10)
+    out = O.decode_group(wl, 0, hs=True)
+    differs = False
+    for l in range(1, wl.G):
+        assert set(out["hs_sel"][l]) <= set(out["cand"])
+        differs |= not np.array_equal(out["hs_sel"][l], out["sel"][l])
+    assert differs
+    part = O.decode_group(wl, 0, layers=[0], hs=True)
+    assert list(part["u"].keys()) == [0]
+    for l in range(1, wl.G):
+        assert np.array_equal(part["hs_sel"][l], out["hs_sel"][l])
+    rows = np.array([3, 17, 250])
+    samp = O.decode_group(wl, 0, rows=rows)
+    for l in range(wl.G):
+        assert np.array_equal(samp["u"][l], out["u"][l][rows]) and samp["sel"] == {}
