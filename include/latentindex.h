@@ -27,8 +27,10 @@
  *    is trusted: out-of-range block-table entries, token ids or lengths are
  *    undefined behaviour.
  *  - Only gfx950 devices are supported (LI_ERR_UNSUPPORTED otherwise).
- *  - Calls are reentrant; the library holds no state besides the
- *    thread-local error string and a per-device architecture check.
+ *  - Calls are reentrant.  Besides the thread-local error string the library
+ *    keeps, per device and behind locks or atomics: the result of the
+ *    architecture check, the compute-unit count, and whether a kernel's
+ *    dynamic-LDS limit has been raised.  None of it changes results.
  *  - Scores are never NaN for finite inputs.  Ordering of scores treats
  *    -0.0 and +0.0 as equal.  "Top-k" always means: the first min(k, n)
  *    positions under (score descending, token id ascending), returned as
@@ -168,11 +170,22 @@ li_status li_append_absorb(const void *x, li_dtype x_dt, int32_t n_tok, const fl
  *            q_len[i] <= max_len, and the sequence holds that many tokens).
  *   max_len  host bound on every q_len (used to size the launch), <= ld.
  *   scores   device fp32 [n_q, ld] (out).
- * Arithmetic: products and sums in fp32 from exact operands.  An FP32 q~
- * against a BF16 cache is carried as a pair of bf16 values (hi + lo), whose
- * sum is within 2^-16 relative of q~; against an FP8 cache q~ is rounded to
- * a single bf16.  The FP8 per-token scale multiplies the dot product before
- * beta and ReLU.
+ * Arithmetic, by cache:
+ *  - FP32 cache (any H, r), and BF16 / FP8 caches outside H = 64, r = 256:
+ *    vector ALU; cache values and q~ decoded exactly to fp32, products and
+ *    sums in fp32.
+ *  - BF16 cache, H = 64, r = 256: bf16 matrix cores.  An FP32 q~ is carried
+ *    as a pair of bf16 values (hi = RNE(q~), lo = RNE(q~ - hi)) whose sum is
+ *    within 2^-16 relative of q~; a BF16 q~ is used as is.  Products are
+ *    exact, sums in fp32.
+ *  - FP8 cache, H = 64, r = 256: fp8 matrix cores.  Each head's q~ is scaled
+ *    by a power of two (largest element into (224, 448]) and split into three
+ *    E4M3 terms, each the rounding of what the earlier terms left (two terms
+ *    for a BF16 q~), which represents q~ to about 2^-12 relative; the matrix
+ *    core accumulates each 128-long group of exact fp8 products in fp32 to
+ *    about 2^-11 of the group's largest product.
+ *  The FP8 per-token scale (and the head's power of two) multiply the dot
+ *  product before beta and ReLU.
  */
 li_status li_score(const void *q_tilde, li_dtype qt_dt, const float *w, const float *beta,
                    int32_t n_q, int32_t H, const int32_t *q_seq, const int32_t *q_len,
@@ -206,6 +219,7 @@ li_status li_topk(const float *scores, int64_t ld, int32_t n_rows, const int32_t
  * selection S = top-min(k, |V|) (S is inside C because B >= k), both in one
  * pass over the scores.
  *   scores, ld, n_rows, valid_len, max_len: as for li_topk.
+ *   max_len    at most 2,097,152 (LI_ERR_UNSUPPORTED beyond).
  *   B, cand    1 <= B <= 65536; cand device int32 [n_rows, B] (out):
  *              ascending token ids, -1 padded (the input of li_hs_select).
  *   k, sel     1 <= k <= B; sel device int32 [n_rows, k] (out), ascending,
@@ -231,7 +245,8 @@ li_status li_hs_anchor_select(const float *scores, int64_t ld, int32_t n_rows,
  * For a bf16 cache with H = 64, r = 256 and at most 64 queries, the scorer
  * builds the rows' key histograms as it writes the scores, so the selection
  * does not read them an extra time; otherwise it is the two calls in turn.
- *   q_tilde .. ld: as for li_score; q_len[i] is also row i's valid length.
+ *   q_tilde .. ld: as for li_score; q_len[i] is also row i's valid length;
+ *               max_len at most 2,097,152 (LI_ERR_UNSUPPORTED beyond).
  *   B, cand, k, sel: as for li_hs_anchor_select.
  *   ws          device workspace of li_hs_anchor_workspace_bytes(n_q,
  *               max_len) bytes, zeroed once before its first use and shared

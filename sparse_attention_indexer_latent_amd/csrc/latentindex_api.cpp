@@ -3,6 +3,7 @@
 // allocates, frees or synchronises device memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -69,6 +70,48 @@ li_status check_cache(const li_cache *c, bool writable) {
 }
 
 }  // namespace
+
+namespace li {
+
+struct DeviceOnce {
+  std::mutex mu;
+  bool done[kMaxDev] = {};
+};
+
+DeviceOnce *device_once_new() { return new DeviceOnce(); }  // one per kernel, kept for the process
+
+hipError_t raise_lds_limit(DeviceOnce *once, const void *fn, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(once->mu);
+  if (!once->done[dev]) {
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    once->done[dev] = true;
+  }
+  return hipSuccess;
+}
+
+namespace {
+std::atomic<int> g_cu[kMaxDev];
+}
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  int n = g_cu[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    g_cu[dev].store(n, std::memory_order_relaxed);  // every thread stores the same value
+  }
+  return n;
+}
+
+}  // namespace li
 
 extern "C" {
 
@@ -244,6 +287,9 @@ li_status li_hs_anchor_select(const float *scores, int64_t ld, int32_t n_rows,
   if (k <= 0) return fail(LI_ERR_INVALID, "k = %d must be positive", k);
   if (B < k) return fail(LI_ERR_INVALID, "B (%d) < k (%d): the candidate set must hold k", B, k);
   if (max_len < 0 || (int64_t)max_len > ld) return fail(LI_ERR_INVALID, "need 0 <= max_len <= ld");
+  if ((int64_t)max_len > li::topk2_max_len())
+    return fail(LI_ERR_UNSUPPORTED, "max_len %d exceeds %lld positions per row", max_len,
+                (long long)li::topk2_max_len());
   if (n_rows == 0) return LI_OK;
   if (!scores || !valid_len || !cand) return fail(LI_ERR_INVALID, "scores/valid_len/cand is NULL");
   size_t need = li_hs_anchor_workspace_bytes(n_rows, max_len > 0 ? max_len : 1);
@@ -270,6 +316,9 @@ li_status li_hs_anchor(const void *q_tilde, li_dtype qt_dt, const float *w, cons
   if (B <= 0 || B > 65536) return fail(LI_ERR_INVALID, "B = %d out of [1, 65536]", B);
   if (k <= 0) return fail(LI_ERR_INVALID, "k = %d must be positive", k);
   if (B < k) return fail(LI_ERR_INVALID, "B (%d) < k (%d): the candidate set must hold k", B, k);
+  if ((int64_t)max_len > li::topk2_max_len())
+    return fail(LI_ERR_UNSUPPORTED, "max_len %d exceeds %lld positions per row", max_len,
+                (long long)li::topk2_max_len());
   if (n_q == 0) return LI_OK;
   if (!q_len || !scores || !cand) return fail(LI_ERR_INVALID, "q_len/scores/cand is NULL");
   size_t need = li_hs_anchor_workspace_bytes(n_q, max_len > 0 ? max_len : 1);

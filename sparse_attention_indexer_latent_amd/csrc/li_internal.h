@@ -29,6 +29,15 @@ inline CacheView view_of(const li_cache &c) {
                    c.n_blocks};
 }
 
+// Per-device state of the library (latentindex_api.cpp), thread-safe.
+// Raises `fn`'s dynamic-LDS limit to `bytes` once per device (the attribute
+// is a property of the kernel on the current device).
+struct DeviceOnce;
+DeviceOnce *device_once_new();
+hipError_t raise_lds_limit(DeviceOnce *once, const void *fn, int bytes);
+// Compute units of the current device (read once per device).
+int device_cu_count();
+
 // append.hip
 size_t append_ws_bytes(int n_tok, int d_model, int r, bool has_P);
 hipError_t launch_append(const void *x, int x_dt, int n_tok, int d_model, const void *P,
@@ -102,8 +111,10 @@ hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_
                        float *out_val, void *ws, hipStream_t st);
 
 // Two nested selections (k_outer >= k_inner) in one pass; ws of
-// topk2_ws_bytes(n_rows, max_len) bytes.
+// topk2_ws_bytes(n_rows, max_len) bytes; rows of at most topk2_max_len()
+// positions.
 size_t topk2_ws_bytes(int n_rows, int max_len);
+int64_t topk2_max_len();
 hipError_t launch_topk2(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
                         int max_len, int k_outer, int32_t *out_outer, int k_inner,
                         int32_t *out_inner, void *ws, hipStream_t st);

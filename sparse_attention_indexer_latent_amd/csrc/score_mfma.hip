@@ -691,23 +691,15 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
   }
 }
 
-int g_num_cu = 0;
-
 template <int R, int NSTAGE, bool C8, bool QF32, bool GATHER, int TOK>
 hipError_t launch_t(const void *q_tilde, const float *w, const float *beta, int n_q,
                       const int32_t *q_seq, const int32_t *q_len, int max_len, const CacheView &cv,
                       const int32_t *cand, int B, int cand_rows, float *out, int64_t ld,
                       hipStream_t st) {
-  if (g_num_cu == 0) {
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    (void)hipDeviceGetAttribute(&g_num_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (g_num_cu <= 0) g_num_cu = 256;
-  }
   const int64_t per_q = GATHER ? (B + TOK - 1) / TOK : (max_len + TOK - 1) / TOK;
   const int64_t T_ub = (int64_t)n_q * per_q;
   const int cap = GATHER ? kMaxPagesGather : kMaxPagesPerWG;
-  int64_t G = std::min<int64_t>(T_ub, (int64_t)g_num_cu * (64 / TOK));
+  int64_t G = std::min<int64_t>(T_ub, (int64_t)device_cu_count() * (64 / TOK));
   G = std::max<int64_t>(G, (T_ub + cap - 1) / cap);
   if (G <= 0) return hipSuccess;
   score_mfma_kernel<R, NSTAGE, C8, QF32, GATHER, TOK><<<(unsigned)G, TOK * 8, 0, st>>>(

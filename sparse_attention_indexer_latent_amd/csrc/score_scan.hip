@@ -495,18 +495,10 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
   __builtin_amdgcn_s_waitcnt(0);  // no load in flight at exit
 }
 
-int g_scan_cu = 0;
-
 // One workgroup per CU, two units each at least, one per query at least.
 int scan_grid(int n_q, int64_t units_per_query) {
-  if (g_scan_cu == 0) {
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    (void)hipDeviceGetAttribute(&g_scan_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (g_scan_cu <= 0) g_scan_cu = 256;
-  }
   const int64_t T = (int64_t)n_q * units_per_query;
-  return (int)std::max<int64_t>(std::min<int64_t>(g_scan_cu, (T + 1) / 2), n_q);
+  return (int)std::max<int64_t>(std::min<int64_t>(device_cu_count(), (T + 1) / 2), n_q);
 }
 
 // Most units one workgroup gets: a query with U units gets W > (G - n) U / T
@@ -522,8 +514,7 @@ int64_t max_units_per_wg(int n_q, int64_t units_per_query) {
 void cand_plan(int n_q, int B, int cand_rows, int *G, int *xw) {
   const int64_t U = (B + kTok - 1) / kTok;
   if (n_q % cand_rows == 0) {
-    (void)scan_grid(n_q, U);  // reads the CU count
-    *xw = (int)std::max<int64_t>(1, std::min<int64_t>(g_scan_cu / n_q, U));
+    *xw = (int)std::max<int64_t>(1, std::min<int64_t>(device_cu_count() / n_q, U));
     *G = n_q * *xw;
   } else {
     *xw = 0;

@@ -99,12 +99,9 @@ hipError_t launch_score_valu(const void *q_tilde, int qt_dt, const float *w, con
   while (TT > 4 && valu_lds_bytes(H, cv.r, TT) > 160 * 1024) TT >>= 1;
   const size_t lds = valu_lds_bytes(H, cv.r, TT);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)score_valu_kernel,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_set = true;
-  }
+  static DeviceOnce *const once = device_once_new();
+  const hipError_t e = raise_lds_limit(once, (const void *)score_valu_kernel, 160 * 1024);
+  if (e != hipSuccess) return e;
   dim3 grid((max_len + TT - 1) / TT, n_q);
   score_valu_kernel<<<grid, 256, lds, st>>>(q_tilde, qt_dt, w, beta, H, q_seq, q_len, cv, cand, B,
                                             max(cand_rows, 1), out, ld, TT);

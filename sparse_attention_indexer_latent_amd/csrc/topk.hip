@@ -1494,12 +1494,9 @@ hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_
   }
   if (max_len <= kLdsRow) {
     const size_t lds = sizeof(LdsRowShared);
-    static bool attr_lds = false;
-    if (!attr_lds) {
-      (void)hipFuncSetAttribute((const void *)topk_lds_kernel,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      attr_lds = true;
-    }
+    static DeviceOnce *const once = device_once_new();
+    const hipError_t e = raise_lds_limit(once, (const void *)topk_lds_kernel, (int)lds);
+    if (e != hipSuccess) return e;
     topk_lds_kernel<<<n_rows, kThreads, lds, st>>>(scores, ld, valid_len, max_len, ids, ids_ld, ids_rows, k,
                                                    out_idx, out_val);
     return hipGetLastError();
@@ -1517,18 +1514,17 @@ hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_
     return hipGetLastError();
   }
   const size_t lds = sizeof(TopkShared);
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)topk_row_kernel,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    attr_set = true;
-  }
+  static DeviceOnce *const once = device_once_new();
+  const hipError_t e = raise_lds_limit(once, (const void *)topk_row_kernel, (int)lds);
+  if (e != hipSuccess) return e;
   topk_row_kernel<<<n_rows, kThreads, lds, st>>>(scores, ld, valid_len, ids, ids_ld, ids_rows, k, out_idx,
                                                  out_val);
   return hipGetLastError();
 }
 
 size_t topk2_ws_bytes(int n_rows, int max_len) { return multi_ws_bytes(n_rows, max_len); }
+
+int64_t topk2_max_len() { return (int64_t)kMaxSegs * kSeg; }
 
 namespace {
 __global__ void fill_i32_kernel(int32_t *__restrict__ dst, int n, int32_t v) {

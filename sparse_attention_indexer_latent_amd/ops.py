@@ -128,6 +128,12 @@ def _need(t: torch.Tensor, name: str, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _numel(t: torch.Tensor, n: int, name: str):
+    """The library takes raw pointers: check the extent it will touch."""
+    if t.numel() != n:
+        raise ValueError(f"{name} must hold {n} elements, got {t.numel()}")
+
+
 class Cache:
     """A paged shared latent cache of one layer group (device tensors).
 
@@ -282,9 +288,16 @@ def score(q_tilde: torch.Tensor, w: torch.Tensor, beta: Optional[torch.Tensor],
     if beta is not None:
         _need(beta, "beta", torch.float32)
     n_q, H, _ = q_tilde.shape
+    _numel(w, n_q * H, "w")
+    if beta is not None:
+        _numel(beta, n_q * H, "beta")
+    _numel(q_seq, n_q, "q_seq")
+    _numel(q_len, n_q, "q_len")
     if scores is None:
         scores = torch.empty((n_q, max(1, max_len)), dtype=torch.float32, device=q_tilde.device)
     _need(scores, "scores", torch.float32)
+    if scores.dim() != 2 or scores.shape[0] < n_q or scores.shape[1] < max_len:
+        raise ValueError(f"scores must be [>= {n_q}, >= {max_len}]")
     _check(lib().li_score(q_tilde.data_ptr(), _dtype_code(q_tilde), w.data_ptr(), _ptr(beta), n_q,
                           H, q_seq.data_ptr(), q_len.data_ptr(), max_len, cache.struct(),
                           scores.data_ptr(), scores.shape[1], _stream()))
@@ -315,13 +328,21 @@ def topk(scores: torch.Tensor, valid_len: torch.Tensor, max_len: int, k: int,
     _need(scores, "scores", torch.float32)
     _need(valid_len, "valid_len", torch.int32)
     n_rows = scores.shape[0]
+    _numel(valid_len, n_rows, "valid_len")
     if out_idx is None:
         out_idx = torch.empty((n_rows, k), dtype=torch.int32, device=scores.device)
     if out_val is None and want_val:
         out_val = torch.empty((n_rows, k), dtype=torch.float32, device=scores.device)
+    _need(out_idx, "out_idx", torch.int32)
+    _numel(out_idx, n_rows * k, "out_idx")
+    if out_val is not None:
+        _need(out_val, "out_val", torch.float32)
+        _numel(out_val, n_rows * k, "out_val")
     need = lib().li_topk_workspace_bytes(n_rows, max_len, k)
     if need and ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    if ws is not None:
+        _need(ws, "ws")
     _check(lib().li_topk(scores.data_ptr(), scores.shape[1], n_rows, valid_len.data_ptr(), max_len,
                          k, out_idx.data_ptr(), _ptr(out_val), _ptr(ws),
                          0 if ws is None else ws.numel(), _stream()))
@@ -342,12 +363,19 @@ def hs_anchor_select(scores: torch.Tensor, valid_len: torch.Tensor, max_len: int
     _need(scores, "scores", torch.float32)
     _need(valid_len, "valid_len", torch.int32)
     n_rows = scores.shape[0]
+    _numel(valid_len, n_rows, "valid_len")
     if cand is None:
         cand = torch.empty((n_rows, B), dtype=torch.int32, device=scores.device)
     if sel is None and want_sel:
         sel = torch.empty((n_rows, k), dtype=torch.int32, device=scores.device)
+    _need(cand, "cand", torch.int32)
+    _numel(cand, n_rows * B, "cand")
+    if sel is not None:
+        _need(sel, "sel", torch.int32)
+        _numel(sel, n_rows * k, "sel")
     if ws is None:
         ws = hs_anchor_workspace(n_rows, max_len, scores.device)
+    _need(ws, "ws")
     _check(lib().li_hs_anchor_select(scores.data_ptr(), scores.shape[1], n_rows,
                                      valid_len.data_ptr(), max_len, B, cand.data_ptr(), k,
                                      _ptr(sel), ws.data_ptr(), ws.numel(), _stream()))
@@ -371,15 +399,28 @@ def hs_anchor(q_tilde: torch.Tensor, w: torch.Tensor, beta: Optional[torch.Tenso
         _need(beta, "beta", torch.float32)
     n_q, H, _ = q_tilde.shape
     dev = q_tilde.device
+    _numel(w, n_q * H, "w")
+    if beta is not None:
+        _numel(beta, n_q * H, "beta")
+    _numel(q_seq, n_q, "q_seq")
+    _numel(q_len, n_q, "q_len")
     if scores is None:
         scores = torch.empty((n_q, max(1, max_len)), dtype=torch.float32, device=dev)
     _need(scores, "scores", torch.float32)
+    if scores.dim() != 2 or scores.shape[0] < n_q or scores.shape[1] < max_len:
+        raise ValueError(f"scores must be [>= {n_q}, >= {max_len}]")
     if cand is None:
         cand = torch.empty((n_q, B), dtype=torch.int32, device=dev)
     if sel is None and want_sel:
         sel = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    _need(cand, "cand", torch.int32)
+    _numel(cand, n_q * B, "cand")
+    if sel is not None:
+        _need(sel, "sel", torch.int32)
+        _numel(sel, n_q * k, "sel")
     if ws is None:
         ws = hs_anchor_workspace(n_q, max_len, dev)
+    _need(ws, "ws")
     evs = None
     if scan_events is not None:
         evs = (ctypes.c_void_p * 2)(*[e.value if isinstance(e, ctypes.c_void_p) else int(e)
@@ -405,17 +446,33 @@ def hs_select(cand: torch.Tensor, q_tilde: torch.Tensor, w: torch.Tensor,
     [n_f, n_q, H] -> out_idx [n_f, n_q, k] (cand_scores likewise)."""
     _need(cand, "cand", torch.int32)
     _need(q_tilde, "q_tilde", (torch.float32, torch.bfloat16))
+    _need(w, "w", torch.float32)
+    _need(q_seq, "q_seq", torch.int32)
+    if beta is not None:
+        _need(beta, "beta", torch.float32)
     n_q, B = cand.shape
     layered = q_tilde.dim() == 4
     n_f = q_tilde.shape[0] if layered else 1
     H = q_tilde.shape[-2]
+    if q_tilde.shape[-3] != n_q or q_tilde.shape[-1] != cache.r:
+        raise ValueError(f"q_tilde must be [{n_f}, {n_q}, H, {cache.r}] to match cand and the cache")
+    _numel(w, n_f * n_q * H, "w")
+    if beta is not None:
+        _numel(beta, n_f * n_q * H, "beta")
+    _numel(q_seq, n_q, "q_seq")
     lead = (n_f,) if layered else ()
     if out_idx is None:
         out_idx = torch.empty(lead + (n_q, k), dtype=torch.int32, device=cand.device)
     if cand_scores is None and want_scores:
         cand_scores = torch.empty(lead + (n_q, B), dtype=torch.float32, device=cand.device)
+    _need(out_idx, "out_idx", torch.int32)
+    _numel(out_idx, n_f * n_q * k, "out_idx")
+    if cand_scores is not None:
+        _need(cand_scores, "cand_scores", torch.float32)
+        _numel(cand_scores, n_f * n_q * B, "cand_scores")
     if ws is None:
         ws = hs_workspace(n_q, B, k, cand.device, n_f=n_f)
+    _need(ws, "ws")
     _check(lib().li_hs_select(cand.data_ptr(), B, n_f, q_tilde.data_ptr(), _dtype_code(q_tilde),
                               w.data_ptr(), _ptr(beta), n_q, H, q_seq.data_ptr(), cache.struct(),
                               k, out_idx.data_ptr(), _ptr(cand_scores), ws.data_ptr(), ws.numel(),

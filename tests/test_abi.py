@@ -109,3 +109,23 @@ def test_workspace_sizes(L):
     # the anchor workspace: the same size whatever the call shape up to 64 rows at the front
     assert L.li_hs_anchor_workspace_bytes(4, 131072) > L.li_hs_anchor_workspace_bytes(4, 4096)
     assert L.li_hs_anchor_workspace_bytes(64, 4096) >= 64 * 4096 * 4
+
+
+def test_anchor_selection_rejects_rows_beyond_its_segment_table(L):
+    """The anchor selection handles rows of at most 1024 segments of 2048
+    positions; longer rows are refused on the host, before any launch."""
+    FAKE = 0x1000
+    lim = 1024 * 2048
+    big_ws = 1 << 40  # never reached: the length check comes first
+    assert L.li_hs_anchor_select(FAKE, lim + 1, 1, FAKE, lim + 1, 8192, FAKE, 2048, FAKE, FAKE,
+                                 big_ws, None) == ops.LI_ERR_UNSUPPORTED
+    assert b"exceeds" in L.li_last_error()
+    c = _cache(max_blocks=(lim // 64) + 2, n_blocks=(lim // 64) + 2)
+    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 1, 64, FAKE, FAKE, lim + 1,
+                          ctypes.byref(c), FAKE, lim + 1, 8192, FAKE, 2048, FAKE, FAKE, big_ws, None,
+                          None) == ops.LI_ERR_UNSUPPORTED
+    assert b"exceeds" in L.li_last_error()
+    # at the limit the length check passes (the workspace check fails next)
+    assert L.li_hs_anchor_select(FAKE, lim, 1, FAKE, lim, 8192, FAKE, 2048, FAKE, FAKE, 1, None) \
+        == ops.LI_ERR_INVALID
+    assert b"workspace needs" in L.li_last_error()
