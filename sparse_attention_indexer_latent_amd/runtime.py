@@ -112,11 +112,15 @@ class DeviceWorkload:
         else:
             self.absorb()
 
-    def _full_post(self) -> None:
+    def _full_post(self, keep_scores: bool = False) -> None:
         wl = self.wl
+        if keep_scores:
+            self.full_scores[0].copy_(self.scores)
         ops.topk(self.scores, self.q_len, self.max_len, wl.k, out_idx=self.sel[0], ws=self.topk_ws)
         for l in range(1, wl.G):
             self.score(l)
+            if keep_scores:
+                self.full_scores[l].copy_(self.scores)
             ops.topk(self.scores, self.q_len, self.max_len, wl.k, out_idx=self.sel[l],
                      ws=self.topk_ws)
 
@@ -134,16 +138,20 @@ class DeviceWorkload:
                           cand_scores=self.cand_scores[1:] if keep_scores else None,
                           ws=self.hs_ws)
 
-    def full_step(self, append: bool = True, events=None) -> None:
+    def full_step(self, append: bool = True, events=None, keep_scores: bool = False) -> None:
         """Full-scan decode step of the group: per layer absorb, score, top-k.
-        events: optional (start, end) CUDA events recorded around layer 0's scan."""
+        events: optional (start, end) CUDA events recorded around layer 0's scan.
+        keep_scores: also copy every layer's scores to full_scores [G, n_q, L]."""
         self._pre(append)
+        if keep_scores and getattr(self, "full_scores", None) is None:
+            self.full_scores = torch.empty((self.wl.G,) + tuple(self.scores.shape),
+                                           dtype=torch.float32, device=self.device)
         if events is not None:
             events[0].record()
         self.score(0)
         if events is not None:
             events[1].record()
-        self._full_post()
+        self._full_post(keep_scores)
 
     def hs_step(self, append: bool = True, keep_scores: bool = False, events=None) -> None:
         """Hierarchical-selection decode step: the anchor scans and proposes

@@ -26,3 +26,19 @@ def pytest_collection_modifyitems(config, items):
         for it in items:
             if "gpu" in it.keywords:
                 it.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    """The error margins of every score comparison that ran (worst per
+    group), so that a quiet run's log still shows them."""
+    try:
+        from parity_util import margins_summary
+    except Exception:  # pragma: no cover
+        return
+    groups = margins_summary()
+    if not groups:
+        return
+    terminalreporter.write_sep("-", "parity margins (worst per group and tolerance)")
+    for (key, tol), (mx, p, ratio, c, n) in sorted(groups.items()):
+        terminalreporter.write_line(f"{key}: max {mx:.3e} p99.99 {p:.3e} tol {tol:.3e} "
+                                    f"(worst {ratio:.3f} of tol; {c} checks, {n} values)")

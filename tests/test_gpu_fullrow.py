@@ -1,0 +1,119 @@
+"""Full-row GPU parity at the decode workloads' real sizes.
+
+For the 32K batch-1 bf16 workload, the 16 ragged fp8 sequences (8K-128K) and
+the batch-4 x 128K bf16 workload, one full-scan decode step (append, absorb,
+then per layer li_score + li_topk) is run as the benchmark runs it, and:
+  * every score of every query on every layer is compared with the oracle's
+    reconstructed-key scores (tolerance of the cache's precision);
+  * every layer's selection is bit-exact against the oracle's selection over
+    the dumped GPU scores, and inside the threshold band of the oracle's own
+    scores (ids that differ must score within 2 rtol (|theta_k| + rho) of the
+    k-th score).
+At 4 x 128K the hierarchical-selection step is checked the same way: the
+anchor's fused scan (scores with in-scan key histograms) on every token, its
+candidates (top-B) and selection (top-k) exact on its dumped scores and in
+the band of the oracle's scores, and every follower's candidate scores,
+exact selection on its dumped candidate scores, and band within the
+candidate set.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from sparse_attention_indexer_latent_amd import workloads as W
+from sparse_attention_indexer_latent_amd.runtime import DeviceWorkload
+
+from parity_util import RTOL_BF16, RTOL_FP8, assert_scores_close, assert_selection_band, say
+
+pytestmark = pytest.mark.gpu
+
+RTOL = {"bf16": RTOL_BF16, "fp8": RTOL_FP8}
+
+
+def _oracle_rows(wl):
+    """Oracle scores of every layer, query and valid token: {(l, s): [L]}."""
+    out = {}
+    for s in range(wl.n_q):
+        seq, L = int(wl.q_seq[s]), int(wl.q_len[s])
+        C = O.sequence_latent(wl, seq)[:L]
+        for l in range(wl.G):
+            out[l, s] = O.layer_scores(C, wl.q[l, s], wl.Dt[l], wl.b[l], wl.nope_off, wl.w[l, s])
+        del C
+    wl.drop_latents()
+    return out
+
+
+@pytest.fixture(scope="module", params=[1, 2, 3], ids=["cfg1-32k-b1-bf16", "cfg2-ragged16-fp8",
+                                                         "cfg3-128k-b4-bf16"])
+def stepped(request):
+    cfg = request.param
+    wl = W.config(cfg)
+    say(f"full-row parity: {wl.name}: device step")
+    dw = DeviceWorkload(wl, hold_last=True)
+    dw.full_step(append=True, keep_scores=True)
+    torch.cuda.synchronize()
+    u = dw.full_scores.cpu().numpy()
+    sel = dw.sel.cpu().numpy()
+    hs = None
+    if wl.B:
+        dw.hs_step(append=True, keep_scores=True)
+        torch.cuda.synchronize()
+        hs = {"u0": dw.scores.cpu().numpy(), "cand": dw.cand.cpu().numpy(),
+              "sel": dw.hs_sel.cpu().numpy(), "cs": dw.cand_scores.cpu().numpy()}
+    del dw
+    torch.cuda.empty_cache()
+    say(f"full-row parity: {wl.name}: oracle")
+    o = _oracle_rows(wl)
+    return wl, u, sel, hs, o
+
+
+def test_full_scan_every_score(stepped):
+    wl, u, _, _, o = stepped
+    rtol = RTOL[wl.cache_dtype]
+    for l in range(wl.G):
+        for s in range(wl.n_q):
+            L = int(wl.q_len[s])
+            assert_scores_close(u[l, s, :L], o[l, s], rtol,
+                                f"{wl.name} full scan layer {l} query {s} (L={L})")
+
+
+def test_full_scan_selection_exact_and_in_band(stepped):
+    wl, u, sel, _, o = stepped
+    rtol = RTOL[wl.cache_dtype]
+    for l in range(wl.G):
+        for s in range(wl.n_q):
+            L = int(wl.q_len[s])
+            ref = O.pad(O.topk(u[l, s, :L].astype(np.float64), wl.k), wl.k)
+            assert np.array_equal(sel[l, s], ref), f"layer {l} query {s}: li_topk differs"
+            assert_selection_band(sel[l, s], o[l, s], wl.k, rtol,
+                                  f"{wl.name} full-scan top-{wl.k} layer {l} query {s}")
+
+
+def test_hs_step_anchor_and_followers(stepped):
+    wl, _, _, hs, o = stepped
+    if hs is None:
+        pytest.skip("full-scan workload (no candidate budget)")
+    rtol = RTOL[wl.cache_dtype]
+    for s in range(wl.n_q):
+        L = int(wl.q_len[s])
+        row = hs["u0"][s, :L]
+        assert_scores_close(row, o[0, s], rtol, f"{wl.name} HS anchor fused scan query {s}")
+        r64 = row.astype(np.float64)
+        cand = hs["cand"][s]
+        assert np.array_equal(cand, O.pad(O.hs_candidates(r64, wl.B), wl.B)), s
+        assert np.array_equal(hs["sel"][0, s], O.pad(O.topk(r64, wl.k), wl.k)), s
+        assert_selection_band(cand, o[0, s], wl.B, rtol, f"{wl.name} HS candidates query {s}")
+        assert_selection_band(hs["sel"][0, s], o[0, s], wl.k, rtol,
+                              f"{wl.name} HS anchor top-{wl.k} query {s}")
+        nc = min(wl.B, L)
+        c = cand[:nc]
+        for l in range(1, wl.G):
+            cs = hs["cs"][l, s]
+            assert np.all(np.isneginf(cs[nc:]))
+            assert_scores_close(cs[:nc], o[l, s][c], rtol, f"{wl.name} HS follower {l} query {s}")
+            ref = O.pad(O.hs_follower(c, cs[:nc].astype(np.float64), wl.k), wl.k)
+            assert np.array_equal(hs["sel"][l, s], ref), (l, s)
+            assert_selection_band(hs["sel"][l, s], o[l, s][c], wl.k, rtol,
+                                  f"{wl.name} HS follower {l} top-{wl.k} query {s}", ids=c)

@@ -225,6 +225,18 @@ def test_score_bf16_queries_single_pass():
         assert_scores_close(u[s, :len(o)].cpu().numpy(), o, 1e-5, f"bf16 q~ query {s}")
 
 
+@pytest.mark.parametrize("dtype,H", [("bf16", 8), ("fp8", 8), ("bf16", 64), ("fp8", 64)])
+def test_score_valu_r192(dtype, H):
+    """A latent of 192 values (the pages' DeepSeek-V3.2 width) takes the
+    vector-ALU scorer for every cache type: ragged lengths, a bias on half
+    of the key, every score against the oracle."""
+    say(f"score r=192 dtype={dtype} H={H} (VALU path)")
+    wl = W.small_decode(31, n_seq=3, lens=[1, 200, 1500], H=H, r=192, d_I=128, G=2, k=16,
+                        cache_dtype=dtype, nope_off=64, bias=True, plant=5, factor=3.0)
+    dw = DeviceWorkload(wl, hold_last=False)
+    _scores_vs_oracle(wl, dw, {"bf16": RTOL_BF16, "fp8": RTOL_FP8}[dtype])
+
+
 def test_score_config1_32k_bf16():
     say("score config 1 (32K, H=64, r=256, bf16): all 4 layers")
     wl = W.config(1)

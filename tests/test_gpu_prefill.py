@@ -90,19 +90,34 @@ def test_prefill_queries_over_several_sequences():
     _check_rows(u, bits, w, beta, q_seq, q_len, lat, range(n_q), "3 sequences")
 
 
-def test_prefill_config4_sampled_scores_and_topk():
+def _prefill_rows(n_q, rng):
+    """64 rows checked in full (the first and last rows, the edges of the
+    first and last eight-query workgroups, the middle, random rows) and every
+    eight-query workgroup boundary pair (8j - 1, 8j) checked on sampled
+    tokens."""
+    fixed = [0, 1, 7, 8, 15, 16, 1023, 1024, n_q - 8, n_q - 2, n_q - 1]
+    rest = rng.choice(np.setdiff1d(np.arange(n_q), fixed), 64 - len(fixed), replace=False)
+    full = sorted(set(fixed) | set(int(x) for x in rest))
+    bound = sorted(set(j for b in range(8, n_q, 8) for j in (b - 1, b)) - set(full))
+    return full, bound
+
+
+def test_prefill_config4_all_layers_scores_and_topk():
     """2,048 queries at positions 63,488..65,535 over a 64K-token bf16
-    latent, per-row top-2,048: sampled rows of the score matrix against the
-    oracle; sampled rows' selections bit-exact against the oracle's selection
-    over the same (GPU) scores and within the threshold band of the oracle's
-    own scores."""
+    latent, per-row top-2,048, all four layers: 64 full rows per layer
+    against the oracle, their selections bit-exact against the oracle's
+    selection over the same (GPU) scores and within the threshold band of the
+    oracle's own scores; every workgroup-boundary row on sampled tokens (the
+    first and last 64 positions of its prefix and 512 random ones)."""
     wl = W.config(4)
     say(f"prefill config: {wl.name}")
     dw = DeviceWorkload(wl, hold_last=False)
     lat = O.sequence_latent(wl, 0)
     n_q, L, k = wl.n_q, int(wl.lens[0]), wl.k
-    rows = [0, 7, 8, 1000, 2046, 2047]
-    for layer in (0, 3):
+    rng = np.random.default_rng(44)
+    full, bound = _prefill_rows(n_q, rng)
+    assert len(full) == 64 and 0 in full and n_q - 1 in full
+    for layer in range(wl.G):
         bits, w = wl.prefill_queries(layer)
         say(f"  layer {layer}: score")
         u_dev = torch.full((n_q, L), SENTINEL, dtype=torch.float32, device="cuda")
@@ -111,16 +126,24 @@ def test_prefill_config4_sampled_scores_and_topk():
         say(f"  layer {layer}: top-{k}")
         idx = ops.topk(u_dev, dw.q_len, L, k)
         torch.cuda.synchronize()
-        sample = rows if layer == 0 else rows[:2]
-        u = u_dev[sample].cpu().numpy()
-        sel = idx[sample].cpu().numpy()
-        qt = O.bf16_decode(bits[sample])
-        for j, i in enumerate(sample):
+        u = u_dev[full].cpu().numpy()
+        sel = idx[full].cpu().numpy()
+        qt = O.bf16_decode(bits[full])
+        for j, i in enumerate(full):
             n = int(wl.q_len[i])
             assert n == 63489 + i
             o = O.absorbed_scores(lat[:n], qt[j], None, w[i])
-            assert_scores_close(u[j, :n], o, RTOL_BF16, f"layer {layer} query {i}")
+            assert_scores_close(u[j, :n], o, RTOL_BF16, f"prefill layer {layer} full row {i}")
             assert np.all(u[j, n:] == SENTINEL)
             ref = O.pad(O.topk(u[j, :n].astype(np.float64), k), k)
             assert np.array_equal(sel[j], ref), f"layer {layer} row {i}: top-k differs"
-            assert_selection_band(sel[j], o, k, RTOL_BF16, f"layer {layer} row {i}")
+            assert_selection_band(sel[j], o, k, RTOL_BF16, f"prefill layer {layer} full row {i}")
+        ub = u_dev[bound].cpu().numpy()
+        qb = O.bf16_decode(bits[bound])
+        for j, i in enumerate(bound):
+            n = int(wl.q_len[i])
+            t = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n),
+                                          rng.integers(0, n, 512)]))
+            o = O.absorbed_scores(lat[t], qb[j], None, w[i])
+            assert_scores_close(ub[j, t], o, RTOL_BF16, f"prefill layer {layer} boundary row {i}")
+            assert np.all(ub[j, n:] == SENTINEL)
