@@ -288,6 +288,26 @@ li_status li_hs_select(const int32_t *cand, int32_t B, int32_t n_f, const void *
                        const int32_t *q_seq, const li_cache *cache, int32_t k, int32_t *out_idx,
                        float *cand_scores, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * li_hs_select_noalloc -- li_hs_select for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Arguments, checks and results are li_hs_select's
+ * without the ws / ws_bytes pair: the workspace is a fixed array of
+ * LI_HS_NOALLOC_SCRATCH_BYTES bytes of the library's own device memory, one
+ * per device, held until the process ends.  The call allocates and frees
+ * nothing.  A call whose li_hs_workspace_bytes(n_f, n_q, B, k) exceeds that
+ * size returns LI_ERR_UNSUPPORTED with nothing enqueued.  Every call on a
+ * device uses that device's one array: calls that overlap in time on one
+ * device (two streams, two threads without ordering) race and must be
+ * serialised by the caller.  The array keeps nothing between calls: each call
+ * writes or clears everything it reads there.
+ */
+#define LI_HS_NOALLOC_SCRATCH_BYTES (8u << 20)
+li_status li_hs_select_noalloc(const int32_t *cand, int32_t B, int32_t n_f, const void *q_tilde,
+                               li_dtype qt_dt, const float *w, const float *beta, int32_t n_q,
+                               int32_t H, const int32_t *q_seq, const li_cache *cache, int32_t k,
+                               int32_t *out_idx, float *cand_scores, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -364,10 +364,13 @@ size_t li_hs_workspace_bytes(int32_t n_f, int32_t n_q, int32_t B, int32_t k) {
          li::topk_ws_bytes((int)rows, B, k);
 }
 
-li_status li_hs_select(const int32_t *cand, int32_t B, int32_t n_f, const void *q_tilde,
-                       li_dtype qt_dt, const float *w, const float *beta, int32_t n_q, int32_t H,
-                       const int32_t *q_seq, const li_cache *cache, int32_t k, int32_t *out_idx,
-                       float *cand_scores, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+// li_hs_select's argument checks (all but the workspace).
+static li_status check_hs_select_args(const int32_t *cand, int32_t B, int32_t n_f,
+                                      const void *q_tilde, li_dtype qt_dt, const float *w,
+                                      int32_t n_q, int32_t H, const int32_t *q_seq,
+                                      const li_cache *cache, int32_t k, const int32_t *out_idx) {
   li_status s = check_score_args(q_tilde, qt_dt, w, n_q, H, q_seq, cache);
   if (s != LI_OK) return s;
   if (B <= 0 || B > 65536) return fail(LI_ERR_INVALID, "B = %d out of [1, 65536]", B);
@@ -375,11 +378,15 @@ li_status li_hs_select(const int32_t *cand, int32_t B, int32_t n_f, const void *
   if (k <= 0) return fail(LI_ERR_INVALID, "k = %d must be positive", k);
   if (B < k) return fail(LI_ERR_INVALID, "B (%d) < k (%d): the candidate set must hold k", B, k);
   if ((int64_t)n_f * n_q > (1 << 20)) return fail(LI_ERR_INVALID, "n_f * n_q too large");
-  if (n_q == 0) return LI_OK;
-  if (!cand || !out_idx) return fail(LI_ERR_INVALID, "cand/out_idx is NULL");
-  size_t need = li_hs_workspace_bytes(n_f, n_q, B, k);
-  if (!ws || ws_bytes < need) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
-  if ((s = check_device()) != LI_OK) return s;
+  if (n_q > 0 && (!cand || !out_idx)) return fail(LI_ERR_INVALID, "cand/out_idx is NULL");
+  return LI_OK;
+}
+
+// li_hs_select's launches on a workspace of li_hs_workspace_bytes() bytes.
+static li_status hs_select_on(const int32_t *cand, int32_t B, int32_t n_f, const void *q_tilde,
+                              li_dtype qt_dt, const float *w, const float *beta, int32_t n_q,
+                              int32_t H, const int32_t *q_seq, const li_cache *cache, int32_t k,
+                              int32_t *out_idx, float *cand_scores, void *ws, void *stream) {
   const int rows = n_f * n_q;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   char *p = (char *)ws;
@@ -415,6 +422,71 @@ li_status li_hs_select(const int32_t *cand, int32_t B, int32_t n_f, const void *
   if (e == hipSuccess)
     e = li::launch_topk(dst, B, rows, vl, cand, B, n_q, B, k, out_idx, nullptr, tws, st);
   return hip_status(e, "li_hs_select launch");
+}
+
+// li_hs_select_noalloc's workspace: a fixed array of device memory of this
+// library, one per device, held until the process ends, for callers that
+// cannot allocate.  Host code never takes the array's name as an address:
+// each device's address comes from hipGetSymbolAddress, once, with that
+// device current.  Every call on a device shares its array.
+static __device__ __align__(256) char scratch[LI_HS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDev];
+
+li_status scratch_of_current_device(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDev) return fail(LI_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(LI_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LI_OK;
+}
+}  // namespace
+
+extern "C" {
+
+li_status li_hs_select(const int32_t *cand, int32_t B, int32_t n_f, const void *q_tilde,
+                       li_dtype qt_dt, const float *w, const float *beta, int32_t n_q, int32_t H,
+                       const int32_t *q_seq, const li_cache *cache, int32_t k, int32_t *out_idx,
+                       float *cand_scores, void *ws, size_t ws_bytes, void *stream) {
+  li_status s = check_hs_select_args(cand, B, n_f, q_tilde, qt_dt, w, n_q, H, q_seq, cache, k,
+                                     out_idx);
+  if (s != LI_OK || n_q == 0) return s;
+  size_t need = li_hs_workspace_bytes(n_f, n_q, B, k);
+  if (!ws || ws_bytes < need) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
+  if ((s = check_device()) != LI_OK) return s;
+  return hs_select_on(cand, B, n_f, q_tilde, qt_dt, w, beta, n_q, H, q_seq, cache, k, out_idx,
+                      cand_scores, ws, stream);
+}
+
+li_status li_hs_select_noalloc(const int32_t *cand, int32_t B, int32_t n_f, const void *q_tilde,
+                               li_dtype qt_dt, const float *w, const float *beta, int32_t n_q,
+                               int32_t H, const int32_t *q_seq, const li_cache *cache, int32_t k,
+                               int32_t *out_idx, float *cand_scores, void *stream) {
+  li_status s = check_hs_select_args(cand, B, n_f, q_tilde, qt_dt, w, n_q, H, q_seq, cache, k,
+                                     out_idx);
+  if (s != LI_OK || n_q == 0) return s;
+  const size_t need = li_hs_workspace_bytes(n_f, n_q, B, k);
+  if (need > (size_t)LI_HS_NOALLOC_SCRATCH_BYTES)
+    return fail(LI_ERR_UNSUPPORTED,
+                "li_hs_select_noalloc: n_f = %d, n_q = %d, B = %d, k = %d need %zu bytes of "
+                "scratch, more than its %zu",
+                n_f, n_q, B, k, need, (size_t)LI_HS_NOALLOC_SCRATCH_BYTES);
+  if ((s = check_device()) != LI_OK) return s;
+  void *ws = nullptr;
+  if ((s = scratch_of_current_device(&ws)) != LI_OK) return s;
+  return hs_select_on(cand, B, n_f, q_tilde, qt_dt, w, beta, n_q, H, q_seq, cache, k, out_idx,
+                      cand_scores, ws, stream);
 }
 
 }  // extern "C"

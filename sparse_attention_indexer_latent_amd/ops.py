@@ -71,7 +71,11 @@ _SIGS = {
     "li_hs_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "li_hs_select": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P,
                             ctypes.POINTER(LiCacheStruct), _I32, _P, _P, _P, _SZ, _P]),
+    "li_hs_select_noalloc": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P,
+                                    ctypes.POINTER(LiCacheStruct), _I32, _P, _P, _P]),
 }
+
+HS_NOALLOC_SCRATCH_BYTES = 8 << 20  # LI_HS_NOALLOC_SCRATCH_BYTES
 
 
 def lib() -> ctypes.CDLL:
@@ -440,10 +444,14 @@ def hs_workspace(n_q: int, B: int, k: int, device="cuda", n_f: int = 1) -> torch
 def hs_select(cand: torch.Tensor, q_tilde: torch.Tensor, w: torch.Tensor,
               beta: Optional[torch.Tensor], q_seq: torch.Tensor, cache: Cache, k: int,
               out_idx: Optional[torch.Tensor] = None, cand_scores: Optional[torch.Tensor] = None,
-              ws: Optional[torch.Tensor] = None, want_scores: bool = False):
+              ws: Optional[torch.Tensor] = None, want_scores: bool = False,
+              noalloc: bool = False):
     """One follower: q_tilde [n_q, H, r], w/beta [n_q, H] -> out_idx [n_q, k].
     n_f followers sharing the candidates: q_tilde [n_f, n_q, H, r], w/beta
-    [n_f, n_q, H] -> out_idx [n_f, n_q, k] (cand_scores likewise)."""
+    [n_f, n_q, H] -> out_idx [n_f, n_q, k] (cand_scores likewise).
+    noalloc: call li_hs_select_noalloc (the library's own fixed workspace;
+    ws is ignored; pass out_idx, and cand_scores if wanted, to allocate
+    nothing here either)."""
     _need(cand, "cand", torch.int32)
     _need(q_tilde, "q_tilde", (torch.float32, torch.bfloat16))
     _need(w, "w", torch.float32)
@@ -470,6 +478,12 @@ def hs_select(cand: torch.Tensor, q_tilde: torch.Tensor, w: torch.Tensor,
     if cand_scores is not None:
         _need(cand_scores, "cand_scores", torch.float32)
         _numel(cand_scores, n_f * n_q * B, "cand_scores")
+    if noalloc:
+        _check(lib().li_hs_select_noalloc(cand.data_ptr(), B, n_f, q_tilde.data_ptr(),
+                                          _dtype_code(q_tilde), w.data_ptr(), _ptr(beta), n_q, H,
+                                          q_seq.data_ptr(), cache.struct(), k, out_idx.data_ptr(),
+                                          _ptr(cand_scores), _stream()))
+        return (out_idx, cand_scores) if want_scores else out_idx
     if ws is None:
         ws = hs_workspace(n_q, B, k, cand.device, n_f=n_f)
     _need(ws, "ws")

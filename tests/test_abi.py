@@ -129,3 +129,30 @@ def test_anchor_selection_rejects_rows_beyond_its_segment_table(L):
     assert L.li_hs_anchor_select(FAKE, lim, 1, FAKE, lim, 8192, FAKE, 2048, FAKE, FAKE, 1, None) \
         == ops.LI_ERR_INVALID
     assert b"workspace needs" in L.li_last_error()
+
+
+def test_hs_select_noalloc_checks_on_the_host(L):
+    """The no-allocation follower step takes li_hs_select's checks, and
+    refuses calls whose workspace would not fit its fixed array, before
+    touching a device."""
+    FAKE = 0x1000
+    c = _cache()
+    assert "li_hs_select_noalloc" in ops.header_symbols()
+    assert L.li_hs_select_noalloc(FAKE, 100, 3, FAKE, ops.LI_FP32, FAKE, None, 1, 64, FAKE,
+                                  ctypes.byref(c), 200, FAKE, None, None) == ops.LI_ERR_INVALID
+    assert b"B (100) < k (200)" in L.li_last_error()
+    assert L.li_hs_workspace_bytes(64, 1, 65536, 16) > ops.HS_NOALLOC_SCRATCH_BYTES
+    assert L.li_hs_select_noalloc(FAKE, 65536, 64, FAKE, ops.LI_FP32, FAKE, None, 1, 64, FAKE,
+                                  ctypes.byref(c), 16, FAKE, None, None) == ops.LI_ERR_UNSUPPORTED
+    assert b"scratch" in L.li_last_error()
+    # the benchmark's follower step fits
+    assert L.li_hs_workspace_bytes(3, 4, 8192, 2048) <= ops.HS_NOALLOC_SCRATCH_BYTES
+    assert L.li_hs_select_noalloc(None, 8192, 3, None, ops.LI_FP32, None, None, 0, 64, None,
+                                  ctypes.byref(c), 2048, None, None, None) == ops.LI_OK  # no queries
+
+
+def test_header_constant_matches_binding():
+    import re
+    txt = open(ops.HEADER).read()
+    m = re.search(r"#define LI_HS_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", txt)
+    assert m and int(m.group(1)) << int(m.group(2)) == ops.HS_NOALLOC_SCRATCH_BYTES
