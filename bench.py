@@ -3,22 +3,29 @@
 
 One step = one decode step of a 4-layer group under hierarchical selection
 (LatentIndex summary, "Methodology", Hierarchical Selection): append the new
-token's latent, absorb the anchor's queries, scan and score the whole shared
-cache, select the anchor's top-B candidates and top-k, then for each of the
-three followers absorb, rescore the candidates and select top-k.  Workload:
-batch 4, 128K context, H = 64, r = 256, bf16 latent, B = 8192, k = 2048
-(synthetic, seeded).
+token's latent, absorb every layer's queries, scan and score the whole shared
+cache with the anchor, select its top-B candidates and top-k, then rescore the
+candidates with the three followers and select their top-k.  Workload: batch
+4, 128K context, H = 64, r = 256, bf16 latent, B = 8192, k = 2048 (synthetic,
+seeded).
 
 Printed: one JSON line with the throughput in scored tokens per second
 (L + 3*min(B, L) positions per query per step), the group-step time, the
 dominant kernel's roofline fraction (the anchor's latent scan, timed with HIP
-events on its stream), the same workload's full-scan step for the HS speedup,
-and the CPU oracle timed on a bounded sample of the same step.
-
-A second leg measures the prefill chunk on the matrix cores: 2,048 causal
-query positions (62K-64K) against a 64K-token bf16 latent, four layers of
-li_score (bf16 absorbed queries, H = 64, r = 256) each followed by li_topk
-(k = 2048 per row), reported as MFMA utilisation against the bf16 dense peak.
+events on its stream inside the timed loop), and the CPU oracle timed on a
+bounded sample of the same step.  Beside them:
+  cold      the same step and scan after the 256 MB last-level cache (MALL)
+            was flushed (a 1 GiB write, then a 1 GiB read of another buffer,
+            so no dirty line is left to write back inside the timing);
+  legs      the full-scan group step of the same workload (HS speedup); the
+            128K batch-1 group (full scan and HS); the 32K batch-1 bf16 and
+            16 ragged fp8 sequences full-scan steps -- each with its scan's
+            warm (back-to-back launches) and cold time and HBM fraction;
+  ceiling   a plain device copy of the anchor scan's byte count, warm and
+            cold, as the practical bandwidth ceiling of this part;
+  prefill   2,048 causal query positions against a 64K-token bf16 latent,
+            four layers of li_score + li_topk (k = 2048 per row), as matrix-
+            core utilisation against the bf16 dense peak.
 """
 
 from __future__ import annotations
@@ -43,7 +50,7 @@ def parse():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-extra", action="store_true", help="skip full-scan and cold-MALL legs")
+    ap.add_argument("--no-extra", action="store_true", help="skip the cold, legs and ceiling parts")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run warmup + this many steps (for profilers); prints nothing else")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -51,8 +58,11 @@ def parse():
                          "three times (calibrates hardware byte counters)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk leg")
     ap.add_argument("--prefill-iters", type=int, default=10)
-    ap.add_argument("--path", choices=["hs", "prefill"], default="hs",
-                    help="with --profile-steps: which path to run")
+    ap.add_argument("--path", choices=["hs", "full", "b1", "c1", "c2", "prefill"], default="hs",
+                    help="with --profile-steps: which step to run (hs / full: the 4 x 128K HS or "
+                         "full-scan step; b1: the 128K batch-1 full-scan step; c1: 32K batch 1; "
+                         "c2: 16 ragged fp8 sequences; prefill: the prefill chunk)")
+    ap.add_argument("--no-legs", action="store_true", help="skip the legs beside the headline")
     ap.add_argument("--graphs", action="store_true",
                     help="replay the step as two HIP graphs around a direct scan launch instead of "
                          "launching every kernel from the host (on this stack a graph's end costs "
@@ -258,6 +268,117 @@ def prefill_leg(torch, ops, W, DeviceWorkload, iters: int) -> dict:
             "tokens_scored_per_s": wl.G * pairs / el}
 
 
+class Flusher:
+    """Empties the last-level cache between timed runs without leaving dirty
+    lines behind: a 1 GiB write of one buffer, then a 1 GiB read of another
+    (the read evicts the written lines, whose write-back happens during the
+    flush).  Enqueued without a host synchronisation, it keeps the GPU busy
+    for about 0.5 ms while the host enqueues the timed work behind it, so the
+    events that follow time the device only."""
+
+    def __init__(self, torch):
+        self.a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        self.b = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        self.acc = torch.empty(1 << 16, dtype=torch.float32, device="cuda")
+        self.torch = torch
+
+    def __call__(self):
+        self.a.fill_(1.0)
+        self.torch.sum(self.b.view(1 << 16, -1), dim=1, out=self.acc)
+
+
+def timed_pair(torch, fn, flush=None, scan=False):
+    """(step us, scan us) of one run of fn, device-timed with events; flush
+    first when given.  fn takes events= for its scoring launch when scan."""
+    a, b = ScanEvent(), ScanEvent()
+    sev = (ScanEvent(), ScanEvent()) if scan else None
+    if flush is not None:
+        flush()
+    a.record()
+    if scan:
+        fn(events=sev)
+    else:
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3, (sev[0].elapsed_time(sev[1]) * 1e3 if scan else None)
+
+
+def scan_b2b_us(torch, scan, n=20):
+    """Average time of n back-to-back launches of one scan (warm), between
+    two events: no per-launch event overhead, the launch gaps included."""
+    for _ in range(3):
+        scan()
+    a, b = ScanEvent(), ScanEvent()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(n):
+        scan()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
+
+
+def loop_us(torch, step, K, warm=3):
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / K * 1e6
+
+
+def leg(torch, flush, dw, hs, K=20, Kc=8):
+    """Warm and cold figures of one decode workload: the group step (warm:
+    wall clock of K back-to-back steps; cold: device time after a flush), and
+    the layer-0 scan (warm: back-to-back launches; cold: after a flush)."""
+    wl = dw.wl
+    step = dw.hs_step if hs else dw.full_step
+    us = loop_us(torch, step, K)
+    dw.absorb()
+    from sparse_attention_indexer_latent_amd import ops
+    # pre-marshalled, so that back-to-back launches are not host-bound
+    scan = ops.prepared_score(dw.q_tilde[0], dw.w[0], dw.beta[0], dw.q_seq, dw.q_len,
+                              dw.max_len, dw.cache, dw.scores)
+    warm_scan = scan_b2b_us(torch, scan)
+    cold = [timed_pair(torch, step, flush, scan=True) for _ in range(Kc)]
+    cold_scan = [timed_pair(torch, scan, flush)[0] for _ in range(Kc)]
+    bpt = latent_bytes_per_token(wl)
+    scan_tokens = int(wl.q_len.sum())
+    sbytes = scan_tokens * (bpt + 4)
+    cs = float(np.median(cold_scan))
+    pos = scored_positions(wl, hs)
+    return {"us_per_group_step": us,
+            "cold_us_per_group_step": float(np.median([c[0] for c in cold])),
+            "scored_tokens_per_s": pos / (us * 1e-6),
+            "scan_bytes_per_launch": sbytes,
+            "scan_us_warm": warm_scan, "scan_frac_warm": sbytes / (warm_scan * 1e-6) / HBM_PEAK,
+            "scan_us_cold": cs, "scan_frac_cold": sbytes / (cs * 1e-6) / HBM_PEAK,
+            "scan_us_cold_in_step": float(np.median([c[1] for c in cold]))}
+
+
+def copy_ceiling(torch, flush, nbytes):
+    """A plain device copy of nbytes (read nbytes, write nbytes), warm and
+    cold, in TB/s of bytes moved."""
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    warm = scan_b2b_us(torch, lambda: y.copy_(x), n=10)
+    cold = float(np.median([timed_pair(torch, lambda: y.copy_(x), flush)[0] for _ in range(6)]))
+    del x, y
+    return {"bytes_moved": 2 * nbytes, "warm_us": warm, "warm_TBps": 2 * nbytes / warm / 1e6,
+            "cold_us": cold, "cold_TBps": 2 * nbytes / cold / 1e6}
+
+
+def batch1_128k(W):
+    """The 128K batch-1 group: the batch-4 workload's generator for one
+    sequence."""
+    return W.make_decode("hs-128k-b1", 3, 0, G=4, H=64, r=256, d_I=128, k=2048, B=8192,
+                         cache_dtype="bf16", lens=[131072], plant_frac=0.01, plant_factor=3.0,
+                         permute_blocks=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -281,8 +402,15 @@ def main():
             prefill_chunk(ops, *pf)
         torch.cuda.synchronize()
         return
+    if args.profile_steps and args.path in ("b1", "c1", "c2"):
+        wl = batch1_128k(W) if args.path == "b1" else W.config(int(args.path[1]))
+        dw = DeviceWorkload(wl, hold_last=True)
+        for _ in range(args.warmup + args.profile_steps):
+            dw.full_step()
+        torch.cuda.synchronize()
+        return
     wl = W.config(args.config)
-    hs = wl.B is not None
+    hs = wl.B is not None and args.path != "full"
     dw = DeviceWorkload(wl, hold_last=True)
     if args.graphs:
         graphs = dw.capture(hs)
@@ -306,8 +434,8 @@ def main():
 
     K = args.steps
     # Events bracket the anchor scan on every EV_EVERY-th timed step: even a
-    # fence-free pair of event records costs ~3 us of a ~115 us step, so
-    # timing every step would slow the very loop whose throughput is reported.
+    # fence-free pair of event records costs ~3 us of the step, so timing
+    # every step would slow the very loop whose throughput is reported.
     evs = {i: (ScanEvent(), ScanEvent()) for i in range(0, K, EV_EVERY)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -339,9 +467,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.cache_dtype == "bf16" else wl.cache_dtype,
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: HS decode step of a 4-layer group, batch {wl.n_q}, "
-                               f"L={wl.max_len}, H={wl.H}, r={wl.r}, {wl.cache_dtype} latent, "
-                               f"B={wl.B}, k={wl.k}, 64-token pages, random block table",
+        "config": {"workload": f"{wl.name}: {'HS' if hs else 'full-scan'} decode step of a "
+                               f"4-layer group, batch {wl.n_q}, L={wl.max_len}, H={wl.H}, "
+                               f"r={wl.r}, {wl.cache_dtype} latent, B={wl.B}, k={wl.k}, "
+                               f"64-token pages, random block table",
                    "global_batch": wl.n_q, "seq_len": wl.max_len, "parallelism": "none (1 GPU)",
                    "launch": "hipGraph pre | direct anchor scan | hipGraph post" if args.graphs
                    else "direct launches from the host on one stream"},
@@ -352,42 +481,50 @@ def main():
                      "achieved": scan_bytes / (scan_ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": scan_bytes / (scan_ms * 1e-3) / HBM_PEAK,
                      "traffic": measured_traffic(wl), "avg_kernel_us": scan_ms * 1e3,
-                     "bytes_per_launch": scan_bytes},
+                     "bytes_per_launch": scan_bytes,
+                     "timing": "warm: inside the timed loop of back-to-back steps (the 256 MB "
+                               "MALL may hold part of the 268 MB the scan reads); the cold "
+                               "figure is under roofline.cold"},
     }
 
     if not args.no_extra:
-        # Full scan of the same group (every layer scans everything).
-        Kf = max(5, K // 2)
-        fstep = dw.capture(False).replay if args.graphs else dw.full_step
-        for _ in range(2):
-            fstep()
-        fevs = {i: (ScanEvent(), ScanEvent()) for i in range(0, Kf, EV_EVERY)}
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(Kf):
-            fstep(events=fevs.get(i))
-        torch.cuda.synchronize()
-        elf = time.perf_counter() - t0
-        fscan = float(np.mean([a.elapsed_time(b) for a, b in fevs.values()]))
-        fpos = scored_positions(wl, False)
-        out["full_scan"] = {"us_per_group_step": elf / Kf * 1e6,
-                            "scored_tokens_per_s": fpos * Kf / elf,
-                            "hbm_frac_step": scan_tokens * bpt * wl.G / (elf / Kf) / HBM_PEAK,
-                            "scan_kernel_us": fscan * 1e3}
-        out["hs_speedup_vs_full_scan"] = (elf / Kf) / (el / K)
-        # Cold MALL: stream 1 GiB through the memory system before each step.
-        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        flush = Flusher(torch)
         Kc = 10
-        cold = []
-        for i in range(Kc):
-            flush.fill_(float(i))
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            step()
-            b.record()
-            torch.cuda.synchronize()
-            cold.append(a.elapsed_time(b))
-        out["cold_mall_us_per_group_step"] = float(np.median(cold)) * 1e3
+        cold = [timed_pair(torch, step, flush, scan=True) for _ in range(Kc)]
+        cscan = float(np.median([c[1] for c in cold]))
+        out["roofline"]["cold"] = {"avg_kernel_us": cscan,
+                                   "achieved": scan_bytes / (cscan * 1e-6) / 1e9,
+                                   "frac": scan_bytes / (cscan * 1e-6) / HBM_PEAK,
+                                   "timing": f"median of {Kc} steps, each after a flush of the "
+                                             "last-level cache (1 GiB written, then 1 GiB of "
+                                             "another buffer read)"}
+        out["cold_us_per_group_step"] = float(np.median([c[0] for c in cold]))
+        out["ceiling"] = copy_ceiling(torch, flush, scan_bytes)
+        if not args.no_legs:
+            legs = {}
+            full = leg(torch, flush, dw, False, K=max(5, K // 2))
+            legs["full_scan_128k_b4"] = full
+            out["hs_speedup_vs_full_scan"] = full["us_per_group_step"] / us_step
+            out["hs_speedup_vs_full_scan_cold"] = (full["cold_us_per_group_step"]
+                                                  / out["cold_us_per_group_step"])
+            del dw
+            torch.cuda.empty_cache()
+            for name, wlf, with_hs in (("128k_b1", batch1_128k(W), True),
+                                       ("cfg1_32k_b1_bf16", W.config(1), False),
+                                       ("cfg2_ragged16_fp8", W.config(2), False)):
+                d = DeviceWorkload(wlf, hold_last=True)
+                lf = leg(torch, flush, d, False)
+                lf["workload"] = (f"{wlf.name}: full-scan step, {wlf.n_q} x L "
+                                  f"{int(wlf.q_len.min())}..{int(wlf.q_len.max())}, "
+                                  f"{wlf.cache_dtype} latent, r={wlf.r}, H={wlf.H}, k={wlf.k}")
+                legs["full_scan_" + name] = lf
+                if with_hs:
+                    lh = leg(torch, flush, d, True)
+                    lh["workload"] = f"{wlf.name}: HS step, B={wlf.B}"
+                    legs["hs_" + name] = lh
+                del d
+                torch.cuda.empty_cache()
+            out["legs"] = legs
         del flush
 
     if not args.no_prefill:

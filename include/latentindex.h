@@ -262,6 +262,30 @@ li_status li_hs_anchor(const void *q_tilde, li_dtype qt_dt, const float *w, cons
                        void *const *scan_events, void *stream);
 
 /*
+ * li_score_topk -- one layer's full-scan selection in one call ("Methodology",
+ * eq. 8 and the TopK definition after it): the scores of every position (as
+ * li_score) and each query's top-min(k, q_len[i]) positions (as li_topk with
+ * valid_len = q_len).  For a bf16 cache with H = 64, r = 256 and at most 64
+ * queries the scorer builds the rows' key histograms as it writes the
+ * scores, so the selection reads them once fewer.
+ *   q_tilde .. ld: as for li_score; max_len at most 2,097,152.
+ *   k, out_idx   1 <= k <= 65536; out_idx device int32 [n_q, k] (out):
+ *                ascending token ids, -1 padded.
+ *   ws           device workspace of li_hs_anchor_workspace_bytes(n_q,
+ *                max_len) bytes, zeroed once before its first use and kept
+ *                valid by every call (shared with li_hs_anchor and
+ *                li_hs_anchor_select on the same terms).
+ *   scan_events  NULL, or two hipEvent_t recorded just before and just after
+ *                the scoring launch.
+ * Results equal li_score followed by li_topk.
+ */
+li_status li_score_topk(const void *q_tilde, li_dtype qt_dt, const float *w, const float *beta,
+                        int32_t n_q, int32_t H, const int32_t *q_seq, const int32_t *q_len,
+                        int32_t max_len, const li_cache *cache, float *scores, int64_t ld,
+                        int32_t k, int32_t *out_idx, void *ws, size_t ws_bytes,
+                        void *const *scan_events, void *stream);
+
+/*
  * li_hs_select -- the follower layers' hierarchical selection ("Hierarchical
  * Selection" paragraph): rescore only the anchor's candidate set with each
  * follower's own absorbed queries, then keep each follower's top-k within

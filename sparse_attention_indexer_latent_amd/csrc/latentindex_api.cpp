@@ -356,6 +356,18 @@ li_status li_hs_anchor(const void *q_tilde, li_dtype qt_dt, const float *w, cons
   return hip_status(e, "li_hs_anchor launch");
 }
 
+li_status li_score_topk(const void *q_tilde, li_dtype qt_dt, const float *w, const float *beta,
+                        int32_t n_q, int32_t H, const int32_t *q_seq, const int32_t *q_len,
+                        int32_t max_len, const li_cache *cache, float *scores, int64_t ld,
+                        int32_t k, int32_t *out_idx, void *ws, size_t ws_bytes,
+                        void *const *scan_events, void *stream) {
+  if (k <= 0 || k > 65536) return fail(LI_ERR_INVALID, "k = %d out of [1, 65536]", k);
+  // The anchor's nested selection with one level: its candidate set with
+  // B = k is the layer's top-k.
+  return li_hs_anchor(q_tilde, qt_dt, w, beta, n_q, H, q_seq, q_len, max_len, cache, scores, ld,
+                      k, out_idx, k, nullptr, ws, ws_bytes, scan_events, stream);
+}
+
 size_t li_hs_workspace_bytes(int32_t n_f, int32_t n_q, int32_t B, int32_t k) {
   if (n_f <= 0 || n_q <= 0 || B <= 0 || k <= 0) return 0;
   const int64_t rows = (int64_t)n_f * n_q;

@@ -68,6 +68,8 @@ _SIGS = {
     "li_hs_anchor": (_I32, [_P, _I32, _P, _P, _I32, _I32, _P, _P, _I32,
                             ctypes.POINTER(LiCacheStruct), _P, _I64, _I32, _P, _I32, _P, _P, _SZ,
                             _P, _P]),
+    "li_score_topk": (_I32, [_P, _I32, _P, _P, _I32, _I32, _P, _P, _I32,
+                             ctypes.POINTER(LiCacheStruct), _P, _I64, _I32, _P, _P, _SZ, _P, _P]),
     "li_hs_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "li_hs_select": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P,
                             ctypes.POINTER(LiCacheStruct), _I32, _P, _P, _P, _SZ, _P]),
@@ -434,6 +436,51 @@ def hs_anchor(q_tilde: torch.Tensor, w: torch.Tensor, beta: Optional[torch.Tenso
                               scores.data_ptr(), scores.shape[1], B, cand.data_ptr(), k, _ptr(sel),
                               ws.data_ptr(), ws.numel(), evs, _stream()))
     return scores, cand, sel
+
+
+def _events(scan_events):
+    if scan_events is None:
+        return None
+    return (ctypes.c_void_p * 2)(*[e.value if isinstance(e, ctypes.c_void_p) else int(e)
+                                  for e in scan_events])
+
+
+def score_topk(q_tilde: torch.Tensor, w: torch.Tensor, beta: Optional[torch.Tensor],
+               q_seq: torch.Tensor, q_len: torch.Tensor, max_len: int, cache: Cache, k: int,
+               scores: Optional[torch.Tensor] = None, out_idx: Optional[torch.Tensor] = None,
+               ws: Optional[torch.Tensor] = None, scan_events=None):
+    """One layer's full-scan step: scores of every position and each query's
+    top-k, in one call.  ws: a workspace from hs_anchor_workspace (zeroed
+    once, reusable).  Returns (scores, out_idx)."""
+    _need(q_tilde, "q_tilde", (torch.float32, torch.bfloat16))
+    _need(w, "w", torch.float32)
+    _need(q_seq, "q_seq", torch.int32)
+    _need(q_len, "q_len", torch.int32)
+    if beta is not None:
+        _need(beta, "beta", torch.float32)
+        _numel(beta, q_tilde.shape[0] * q_tilde.shape[1], "beta")
+    n_q, H, _ = q_tilde.shape
+    dev = q_tilde.device
+    _numel(w, n_q * H, "w")
+    _numel(q_seq, n_q, "q_seq")
+    _numel(q_len, n_q, "q_len")
+    if scores is None:
+        scores = torch.empty((n_q, max(1, max_len)), dtype=torch.float32, device=dev)
+    _need(scores, "scores", torch.float32)
+    if scores.dim() != 2 or scores.shape[0] < n_q or scores.shape[1] < max_len:
+        raise ValueError(f"scores must be [>= {n_q}, >= {max_len}]")
+    if out_idx is None:
+        out_idx = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    _need(out_idx, "out_idx", torch.int32)
+    _numel(out_idx, n_q * k, "out_idx")
+    if ws is None:
+        ws = hs_anchor_workspace(n_q, max_len, dev)
+    _need(ws, "ws")
+    _check(lib().li_score_topk(q_tilde.data_ptr(), _dtype_code(q_tilde), w.data_ptr(), _ptr(beta),
+                               n_q, H, q_seq.data_ptr(), q_len.data_ptr(), max_len, cache.struct(),
+                               scores.data_ptr(), scores.shape[1], k, out_idx.data_ptr(),
+                               ws.data_ptr(), ws.numel(), _events(scan_events), _stream()))
+    return scores, out_idx
 
 
 def hs_workspace(n_q: int, B: int, k: int, device="cuda", n_f: int = 1) -> torch.Tensor:

@@ -66,6 +66,8 @@ class DeviceWorkload:
             self.cand_scores = torch.empty((G, n_q, wl.B), dtype=torch.float32, device=device)
             self.hs_ws = ops.hs_workspace(n_q, wl.B, wl.k, device, n_f=max(G - 1, 1))
             self.anchor_ws = ops.hs_anchor_workspace(n_q, self.max_len, device)
+        # the full-scan step's selections (li_score_topk; zeroed once)
+        self.full_ws = ops.hs_anchor_workspace(n_q, self.max_len, device)
 
     def _ws(self, n):
         return torch.empty(n, dtype=torch.uint8, device=self.device) if n else None
@@ -113,6 +115,9 @@ class DeviceWorkload:
             self.absorb()
 
     def _full_post(self, keep_scores: bool = False) -> None:
+        """Graph-capturable remainder of the two-call full-scan step: layer
+        0's top-k (its scores are in place), then li_score + li_topk for the
+        other layers."""
         wl = self.wl
         if keep_scores:
             self.full_scores[0].copy_(self.scores)
@@ -123,6 +128,14 @@ class DeviceWorkload:
                 self.full_scores[l].copy_(self.scores)
             ops.topk(self.scores, self.q_len, self.max_len, wl.k, out_idx=self.sel[l],
                      ws=self.topk_ws)
+
+    def score_topk(self, layer: int, events=None) -> None:
+        """One layer's full-scan step (li_score_topk): scores into
+        self.scores, selection into self.sel[layer]."""
+        raw = None if events is None else (events[0].e, events[1].e)
+        ops.score_topk(self.q_tilde[layer], self.w[layer], self.beta[layer], self.q_seq,
+                       self.q_len, self.max_len, self.cache, self.wl.k, scores=self.scores,
+                       out_idx=self.sel[layer], ws=self.full_ws, scan_events=raw)
 
     def _hs_post(self, keep_scores: bool = False) -> None:
         wl = self.wl
@@ -138,20 +151,34 @@ class DeviceWorkload:
                           cand_scores=self.cand_scores[1:] if keep_scores else None,
                           ws=self.hs_ws)
 
-    def full_step(self, append: bool = True, events=None, keep_scores: bool = False) -> None:
-        """Full-scan decode step of the group: per layer absorb, score, top-k.
-        events: optional (start, end) CUDA events recorded around layer 0's scan.
-        keep_scores: also copy every layer's scores to full_scores [G, n_q, L]."""
+    def full_step(self, append: bool = True, events=None, keep_scores: bool = False,
+                  two_call: bool = False) -> None:
+        """Full-scan decode step of the group: every layer's queries absorbed,
+        then per layer one li_score_topk call (scores and top-k).
+        events: optional (start, end) events around layer 0's scoring launch
+        (raw HIP events with an `e` handle, or torch events, which make layer
+        0 run as li_score + li_topk around them).
+        keep_scores (tests): also copy every layer's scores to full_scores
+        [G, n_q, L] (allocated on first use).
+        two_call: li_score + li_topk per layer instead (the graph-captured
+        form of the step)."""
         self._pre(append)
         if keep_scores and getattr(self, "full_scores", None) is None:
             self.full_scores = torch.empty((self.wl.G,) + tuple(self.scores.shape),
                                            dtype=torch.float32, device=self.device)
-        if events is not None:
-            events[0].record()
-        self.score(0)
-        if events is not None:
-            events[1].record()
-        self._full_post(keep_scores)
+        raw_ev = events is not None and getattr(events[0], "e", None) is not None
+        if two_call or (events is not None and not raw_ev):
+            if events is not None:
+                events[0].record()
+            self.score(0)
+            if events is not None:
+                events[1].record()
+            self._full_post(keep_scores)
+            return
+        for l in range(self.wl.G):
+            self.score_topk(l, events if l == 0 else None)
+            if keep_scores:
+                self.full_scores[l].copy_(self.scores)
 
     def hs_step(self, append: bool = True, keep_scores: bool = False, events=None) -> None:
         """Hierarchical-selection decode step: the anchor scans and proposes

@@ -156,3 +156,19 @@ def test_header_constant_matches_binding():
     txt = open(ops.HEADER).read()
     m = re.search(r"#define LI_HS_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", txt)
     assert m and int(m.group(1)) << int(m.group(2)) == ops.HS_NOALLOC_SCRATCH_BYTES
+
+
+def test_score_topk_checks_on_the_host(L):
+    FAKE = 0x1000
+    c = _cache()
+    big = L.li_hs_anchor_workspace_bytes(4, 256)
+    assert L.li_score_topk(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
+                           FAKE, 256, 0, FAKE, FAKE, big, None, None) == ops.LI_ERR_INVALID
+    assert b"k = 0" in L.li_last_error()
+    assert L.li_score_topk(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
+                           FAKE, 256, 70000, FAKE, FAKE, big, None, None) == ops.LI_ERR_INVALID
+    assert L.li_score_topk(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
+                           FAKE, 256, 16, FAKE, FAKE, big - 1, None, None) == ops.LI_ERR_INVALID
+    assert b"workspace needs" in L.li_last_error()
+    assert L.li_score_topk(FAKE, ops.LI_FP32, FAKE, None, 0, 64, FAKE, FAKE, 256, ctypes.byref(c),
+                           FAKE, 256, 16, FAKE, FAKE, big, None, None) == ops.LI_OK

@@ -524,6 +524,46 @@ def test_hs_anchor_fused_equals_two_calls(case):
             assert np.array_equal(sel[i], O.pad(O.topk(row, wl.k), wl.k)), (rep, i)
 
 
+@pytest.mark.parametrize("case", ["bf16_fused", "fp8", "fp32_tiny", "65_queries"])
+def test_score_topk_equals_score_then_topk(case):
+    """li_score_topk (one call; the scorer builds the key histograms for a
+    bf16 cache with H = 64, r = 256 and <= 64 queries) gives the bits of
+    li_score followed by li_topk, call after call on one workspace."""
+    say(f"score_topk: {case}")
+    if case == "bf16_fused":
+        wl = W.small_decode(70, n_seq=4, lens=[9000, 40, 4100, 13000], H=64, r=256, d_I=128, G=1,
+                            k=2048, cache_dtype="bf16", nope_off=64, bias=True)
+    elif case == "fp8":
+        wl = W.small_decode(71, n_seq=3, lens=[5000, 12000, 700], H=64, r=256, d_I=128, G=1,
+                            k=512, cache_dtype="fp8")
+    elif case == "fp32_tiny":
+        wl = W.small_decode(72, n_seq=2, lens=[4096, 300], H=8, r=32, d_I=16, G=1, k=256,
+                            cache_dtype="fp32")
+    else:
+        rng = np.random.default_rng(73)
+        wl = W.small_decode(73, n_seq=65, lens=[int(x) for x in rng.integers(100, 6000, 65)],
+                            H=64, r=256, d_I=128, G=1, k=64, cache_dtype="bf16")
+    dw = DeviceWorkload(wl, hold_last=False)
+    dw.absorb(0)
+    L = dw.max_len
+    ws = ops.hs_anchor_workspace(wl.n_q, L)
+    for rep in range(2):
+        sc, idx = ops.score_topk(dw.q_tilde[0], dw.w[0], dw.beta[0], dw.q_seq, dw.q_len, L,
+                                 dw.cache, wl.k, ws=ws)
+        ref = ops.score(dw.q_tilde[0], dw.w[0], dw.beta[0], dw.q_seq, dw.q_len, L, dw.cache)
+        ridx = ops.topk(ref, dw.q_len, L, wl.k)
+        torch.cuda.synchronize()
+        u, ur = sc.cpu().numpy(), ref.cpu().numpy()
+        for i in range(wl.n_q):
+            n = int(wl.q_len[i])
+            assert np.array_equal(u[i, :n].view(np.uint32), ur[i, :n].view(np.uint32)), (rep, i)
+        assert torch.equal(idx, ridx), rep
+        got = idx.cpu().numpy()
+        for i in range(wl.n_q):
+            n = int(wl.q_len[i])
+            assert np.array_equal(got[i], O.pad(O.topk(u[i, :n].astype(np.float64), wl.k), wl.k))
+
+
 @pytest.mark.parametrize("n_seq", [64, 65])
 def test_hs_anchor_many_queries(n_seq):
     """64 queries (the most whose key histograms the scorer builds) and 65
