@@ -65,11 +65,18 @@ typedef enum li_dtype {
  * block_table[s * max_blocks + t / block_size], row t % block_size.
  *   data        device [n_blocks, block_size, r] of `dtype` (FP32, BF16 or
  *               FP8_E4M3).  Row-major: one token's r values are contiguous.
- *   scale       device fp32 [n_blocks, block_size]: per-token dequantisation
- *               scale, FP8 only (NULL otherwise).  Value = code * scale.
+ *   scale       device fp32 [n_blocks, block_size, n_scales]: per-token
+ *               dequantisation scales, FP8 only (NULL otherwise).  Value of
+ *               element j = code * scale[j / scale_block] (one scale per
+ *               token when scale_block == 0).
  *   block_table device int32 [n_seq, max_blocks] physical block ids.
  *   block_size  must be 64.
  *   r           latent width d_C; a multiple of 16, at most 1024.
+ *   scale_block FP8: 0 (one scale per token, n_scales = 1) or 128 (one scale
+ *               per 128-value block, n_scales = ceil(r / 128): with r = 192,
+ *               a 200-byte token record of 192 codes and two fp32 scales, the
+ *               "200-byte latent including FP8 scales" of the LatentIndex
+ *               explainer's storage paragraph).  Must be 0 for other types.
  */
 typedef struct li_cache {
   void *data;
@@ -81,6 +88,7 @@ typedef struct li_cache {
   int32_t block_size;
   int32_t r;
   li_dtype dtype;
+  int32_t scale_block;
 } li_cache;
 
 /* Thread-local message describing the last non-OK status of this thread. */
@@ -102,9 +110,10 @@ li_status li_check_device(void);
  *              times exp(i * angle)); the angle is formed in double.
  *   seq_idx, pos device int32 [n_tok]: destination sequence and position.
  *   cache      destination; BF16: round to nearest even; FP8: per token
- *              amax = max|c|, scale = amax / 448, codes = RNE(c * (448 /
- *              amax)) saturated to +-448 (amax == 0: scale 1, codes 0);
- *              FP32: stored as is.  The projection accumulates in fp32.
+ *              (per 128-value block when scale_block == 128) amax = max|c|,
+ *              scale = amax / 448, codes = RNE(c * (448 / amax)) saturated
+ *              to +-448 (amax == 0: scale 1, codes 0); FP32: stored as is.
+ *              The projection accumulates in fp32.
  *   ws         device workspace of li_append_workspace_bytes() bytes
  *              (may be NULL when that is 0, i.e. when P is NULL).
  * Tokens with equal (seq_idx, pos) race.  n_tok == 0 is a no-op.
@@ -171,21 +180,23 @@ li_status li_append_absorb(const void *x, li_dtype x_dt, int32_t n_tok, const fl
  *   max_len  host bound on every q_len (used to size the launch), <= ld.
  *   scores   device fp32 [n_q, ld] (out).
  * Arithmetic, by cache:
- *  - FP32 cache (any H, r), and BF16 / FP8 caches outside H = 64, r = 256:
- *    vector ALU; cache values and q~ decoded exactly to fp32, products and
- *    sums in fp32.
- *  - BF16 cache, H = 64, r = 256: bf16 matrix cores.  An FP32 q~ is carried
+ *  - FP32 cache (any H, r), and BF16 / FP8 caches of other shapes: vector
+ *    ALU; cache values and q~ decoded exactly to fp32, products and sums in
+ *    fp32.
+ *  - BF16 cache, H = 64, r = 256 (or r = 192 with at most 64 queries): bf16
+ *    matrix cores.  An FP32 q~ is carried
  *    as a pair of bf16 values (hi = RNE(q~), lo = RNE(q~ - hi)) whose sum is
  *    within 2^-16 relative of q~; a BF16 q~ is used as is.  Products are
  *    exact, sums in fp32.
- *  - FP8 cache, H = 64, r = 256: fp8 matrix cores.  Each head's q~ is scaled
+ *  - FP8 cache, H = 64, r = 128, 192 or 256 (and at most 64 queries, or
+ *    r = 256 with one scale per token): fp8 matrix cores.  Each head's q~ is scaled
  *    by a power of two (largest element into (224, 448]) and split into three
  *    E4M3 terms, each the rounding of what the earlier terms left (two terms
  *    for a BF16 q~), which represents q~ to about 2^-12 relative; the matrix
  *    core accumulates each 128-long group of exact fp8 products in fp32 to
  *    about 2^-11 of the group's largest product.
- *  The FP8 per-token scale (and the head's power of two) multiply the dot
- *  product before beta and ReLU.
+ *  The FP8 scales (and the head's power of two) multiply the dot products
+ *  of their blocks before beta and ReLU.
  */
 li_status li_score(const void *q_tilde, li_dtype qt_dt, const float *w, const float *beta,
                    int32_t n_q, int32_t H, const int32_t *q_seq, const int32_t *q_len,

@@ -173,26 +173,41 @@ def project_latent(x: np.ndarray, P: Optional[np.ndarray], theta: Optional[np.nd
     return z
 
 
-def quantize_fp8(c32: np.ndarray):
-    """Per-token fp8 storage of fp32 latent rows [n, r]: amax = max|c| (fp32),
-    scale = amax/448 and inv = 448/amax as IEEE fp32 divisions (scale = inv
-    = 1 when amax = 0), codes = E4M3FN-RNE(fp32(c * inv)).  Returns
-    (codes uint8 [n, r], scale float32 [n])."""
+def quantize_fp8(c32: np.ndarray, block: int = 0):
+    """fp8 storage of fp32 latent rows [n, r], one scale per row (block = 0)
+    or per `block` consecutive values of a row: amax = max|c| over the row
+    or block (fp32), scale = amax/448 and inv = 448/amax as IEEE fp32
+    divisions (scale = inv = 1 when amax = 0), codes = E4M3FN-RNE(fp32(c *
+    inv)).  Returns (codes uint8 [n, r], scale float32 [n] for block = 0,
+    else [n, ceil(r / block)])."""
     c = np.asarray(c32, dtype=np.float32)
-    amax = np.max(np.abs(c), axis=1).astype(np.float32)
-    zero = amax == 0
-    safe = np.where(zero, np.float32(1.0), amax).astype(np.float32)
-    scale = np.where(zero, np.float32(1.0), safe / np.float32(448.0)).astype(np.float32)
-    inv = np.where(zero, np.float32(1.0), np.float32(448.0) / safe).astype(np.float32)
-    y = (c * inv[:, None]).astype(np.float32)
-    return e4m3fn_encode(y), scale
+    n, r = c.shape
+    blk = block or r
+    nb = -(-r // blk)
+    codes = np.empty((n, r), dtype=np.uint8)
+    scales = np.empty((n, nb), dtype=np.float32)
+    for g in range(nb):
+        part = c[:, g * blk:(g + 1) * blk]
+        amax = np.max(np.abs(part), axis=1).astype(np.float32)
+        zero = amax == 0
+        safe = np.where(zero, np.float32(1.0), amax).astype(np.float32)
+        scales[:, g] = np.where(zero, np.float32(1.0), safe / np.float32(448.0))
+        inv = np.where(zero, np.float32(1.0), np.float32(448.0) / safe).astype(np.float32)
+        codes[:, g * blk:(g + 1) * blk] = e4m3fn_encode((part * inv[:, None]).astype(np.float32))
+    return codes, (scales[:, 0].copy() if block == 0 else scales)
 
 
-def dequantize_fp8(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
-    return e4m3fn_decode(codes) * np.asarray(scale, dtype=F64)[:, None]
+def dequantize_fp8(codes: np.ndarray, scale: np.ndarray, block: int = 0) -> np.ndarray:
+    """Exact value of fp8 codes [n, r] with their scales (per row, or per
+    `block` values of a row)."""
+    vals = e4m3fn_decode(codes)
+    sc = np.asarray(scale, dtype=F64)
+    if block == 0:
+        return vals * sc[:, None]
+    return vals * np.repeat(sc, block, axis=1)[:, :vals.shape[1]]
 
 
-def store_latent(c32: np.ndarray, dtype: str):
+def store_latent(c32: np.ndarray, dtype: str, scale_block: int = 0):
     """What the cache stores for fp32 rows c32, and its exact float64 value.
     Returns (stored, scale_or_None, exact_f64)."""
     c32 = np.asarray(c32, dtype=np.float32)
@@ -202,8 +217,8 @@ def store_latent(c32: np.ndarray, dtype: str):
         bits = bf16_encode(c32)
         return bits, None, bf16_decode(bits)
     if dtype == "fp8":
-        codes, scale = quantize_fp8(c32)
-        return codes, scale, dequantize_fp8(codes, scale)
+        codes, scale = quantize_fp8(c32, scale_block)
+        return codes, scale, dequantize_fp8(codes, scale, scale_block)
     raise ValueError(dtype)
 
 
@@ -304,7 +319,7 @@ def hs_follower(cand: np.ndarray, u_f_cand: np.ndarray, k: int) -> np.ndarray:
 
 def sequence_latent(wl, s: int) -> np.ndarray:
     """Exact float64 latent of sequence s as the configured cache stores it."""
-    return store_latent(wl.latent(s), wl.cache_dtype)[2]
+    return store_latent(wl.latent(s), wl.cache_dtype, getattr(wl, "scale_block", 0))[2]
 
 
 def decode_group(wl, s: int, C: Optional[np.ndarray] = None, layers=None,

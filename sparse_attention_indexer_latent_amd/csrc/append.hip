@@ -107,15 +107,21 @@ __device__ __forceinline__ void store_block(const T *__restrict__ x, const float
     uint16_t *dst = (uint16_t *)cv.data + row * r;
     for (int j = lane; j < r; j += kWave) dst[j] = (uint16_t)f32_to_bf16_bits(ys[j]);
   } else {
-    float amax = 0.f;
-    for (int j = lane; j < r; j += kWave) amax = fmaxf(amax, fabsf(ys[j]));
-    amax = wave_max(amax);
-    // IEEE divisions (HIP keeps fp32 division correctly rounded by default).
-    const float scale = amax == 0.f ? 1.f : amax / 448.f;
-    const float inv = amax == 0.f ? 1.f : 448.f / amax;
+    // one scale per token, or per scale_block values of it
+    const int sbk = cv.scale_block ? cv.scale_block : r;
+    const int ns = (r + sbk - 1) / sbk;
     uint8_t *dst = (uint8_t *)cv.data + row * r;
-    for (int j = lane; j < r; j += kWave) dst[j] = (uint8_t)f32_to_e4m3(__fmul_rn(ys[j], inv));
-    if (lane == 0) ((float *)cv.scale)[row] = scale;
+    for (int g = 0; g < ns; ++g) {
+      const int j0 = g * sbk, j1 = min(r, j0 + sbk);
+      float amax = 0.f;
+      for (int j = j0 + lane; j < j1; j += kWave) amax = fmaxf(amax, fabsf(ys[j]));
+      amax = wave_max(amax);
+      // IEEE divisions (HIP keeps fp32 division correctly rounded by default).
+      const float scale = amax == 0.f ? 1.f : amax / 448.f;
+      const float inv = amax == 0.f ? 1.f : 448.f / amax;
+      for (int j = j0 + lane; j < j1; j += kWave) dst[j] = (uint8_t)f32_to_e4m3(__fmul_rn(ys[j], inv));
+      if (lane == 0) ((float *)cv.scale)[row * ns + g] = scale;
+    }
   }
 }
 

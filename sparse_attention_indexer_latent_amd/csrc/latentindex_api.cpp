@@ -65,6 +65,8 @@ li_status check_cache(const li_cache *c, bool writable) {
     return fail(LI_ERR_INVALID, "cache n_seq/max_blocks/n_blocks must be positive");
   if ((c->dtype == LI_FP8_E4M3) != (c->scale != nullptr))
     return fail(LI_ERR_INVALID, "scale must be given exactly for an FP8 cache");
+  if (c->scale_block != 0 && !(c->dtype == LI_FP8_E4M3 && c->scale_block == 128))
+    return fail(LI_ERR_INVALID, "scale_block %d: 0, or 128 for an FP8 cache", c->scale_block);
   (void)writable;
   return LI_OK;
 }

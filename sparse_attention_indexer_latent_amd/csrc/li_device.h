@@ -96,6 +96,13 @@ __device__ __forceinline__ void dma16_to_lds(const void *g,
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
 }
 
+// As dma16_to_lds for 4 bytes per lane (lane i's dword lands at lds + 4 i).
+__device__ __forceinline__ void dma4_to_lds(const void *g,
+                                            __attribute__((address_space(3))) void *lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+}
+
 // Inclusive prefix sum across a wavefront with DPP moves (row shifts within
 // 16-lane rows, then row broadcasts 15 and 31 across rows).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {

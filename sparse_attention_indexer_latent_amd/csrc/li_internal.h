@@ -22,11 +22,18 @@ struct CacheView {
   int32_t dtype;  // li_dtype
   int32_t n_seq;
   int32_t n_blocks;
+  int32_t scale_block;  // fp8: 0 (one scale per token) or 128
 };
 
 inline CacheView view_of(const li_cache &c) {
   return CacheView{c.data, c.scale, c.block_table, c.max_blocks, c.r, (int32_t)c.dtype, c.n_seq,
-                   c.n_blocks};
+                   c.n_blocks, c.scale_block};
+}
+
+// Scales per token of a cache (0 for caches without scales).
+__host__ __device__ inline int n_scales(const CacheView &cv) {
+  if (cv.dtype != LI_FP8_E4M3) return 0;
+  return cv.scale_block ? (cv.r + cv.scale_block - 1) / cv.scale_block : 1;
 }
 
 // Per-device state of the library (latentindex_api.cpp), thread-safe.

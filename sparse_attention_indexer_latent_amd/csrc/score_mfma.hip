@@ -729,7 +729,7 @@ hipError_t launch_mode(const void *q_tilde, const float *w, const float *beta, i
 
 bool score_mfma_supported(int qt_dt, int H, const CacheView &cv) {
   return H == 64 && cv.r == 256 && (cv.dtype == LI_BF16 || cv.dtype == LI_FP8_E4M3) &&
-         (qt_dt == LI_FP32 || qt_dt == LI_BF16);
+         cv.scale_block == 0 && (qt_dt == LI_FP32 || qt_dt == LI_BF16);
 }
 
 hipError_t launch_score_mfma(const void *q_tilde, int qt_dt, const float *w, const float *beta,

@@ -9,6 +9,8 @@
 // reading different tokens hit different banks) are staged in LDS; thread
 // (token, head group) accumulates its heads, and the head groups are summed
 // in a fixed order.
+#include <algorithm>
+
 #include "li_device.h"
 #include "li_internal.h"
 
@@ -30,8 +32,10 @@ score_valu_kernel(const void *__restrict__ q_tilde, int qt_dt, const float *__re
   float *qs = lds;                      // [H][r]
   float *wsm = qs + H * r;              // [H]
   float *bsm = wsm + H;                 // [H]
-  float *ssm = bsm + H;                 // [TT] per-token scale
-  float *cs = ssm + TT;                 // [TT][r + 1]
+  const int ns = max(n_scales(cv), 1);  // scales per token (fp8), else 1
+  const int sbk = cv.scale_block ? cv.scale_block : r;  // values per scale
+  float *ssm = bsm + H;                 // [TT][ns] token scales
+  float *cs = ssm + TT * ns;            // [TT][r + 1]
   float *red = cs + TT * (r + 1);       // [256 / TT][TT]
   const int tid = threadIdx.x;
   const int64_t qoff = (int64_t)i * H * r;
@@ -52,10 +56,11 @@ score_valu_kernel(const void *__restrict__ q_tilde, int qt_dt, const float *__re
     const int t = token_of(slot);
     return t >= 0 ? (int64_t)bt[t / kPage] * kPage + t % kPage : 0;
   };
-  for (int tok = tid; tok < TT; tok += 256) {
+  for (int e = tid; e < TT * ns; e += 256) {
+    const int tok = e / ns, g = e % ns;
     float sc = 1.f;
-    if (tok < nt && cv.dtype == LI_FP8_E4M3) sc = cv.scale[phys_row(t0 + tok)];
-    ssm[tok] = sc;
+    if (tok < nt && cv.dtype == LI_FP8_E4M3) sc = cv.scale[phys_row(t0 + tok) * ns + g];
+    ssm[e] = sc;
   }
   for (int e = tid; e < TT * r; e += 256) {
     const int tok = e / r, j = e % r;
@@ -67,13 +72,23 @@ score_valu_kernel(const void *__restrict__ q_tilde, int qt_dt, const float *__re
   const int n_groups = 256 / TT;
   const int tok = tid % TT, hg = tid / TT;
   const float *c = cs + tok * (r + 1);
-  const float sc = ssm[tok];
+  const float *sc = ssm + tok * ns;
   float acc = 0.f;
   for (int h = hg; h < H; h += n_groups) {
     const float *qh = qs + h * r;
-    float dot = 0.f;
-    for (int j = 0; j < r; ++j) dot = fmaf(qh[j], c[j], dot);
-    const float x = fmaf(dot, sc, bsm[h]);
+    float x;
+    if (ns == 1) {
+      float dot = 0.f;
+      for (int j = 0; j < r; ++j) dot = fmaf(qh[j], c[j], dot);
+      x = fmaf(dot, sc[0], bsm[h]);
+    } else {  // each block's dot product times its scale
+      x = bsm[h];
+      for (int g = 0; g < ns; ++g) {
+        float dot = 0.f;
+        for (int j = g * sbk; j < min(r, (g + 1) * sbk); ++j) dot = fmaf(qh[j], c[j], dot);
+        x = fmaf(dot, sc[g], x);
+      }
+    }
     acc = fmaf(wsm[h], fmaxf(x, 0.f), acc);
   }
   red[hg * TT + tok] = acc;
@@ -85,8 +100,8 @@ score_valu_kernel(const void *__restrict__ q_tilde, int qt_dt, const float *__re
   }
 }
 
-size_t valu_lds_bytes(int H, int r, int TT) {
-  return sizeof(float) * ((size_t)H * r + 2 * H + TT + (size_t)TT * (r + 1) + 256);
+size_t valu_lds_bytes(int H, int r, int TT, int ns) {
+  return sizeof(float) * ((size_t)H * r + 2 * H + (size_t)TT * ns + (size_t)TT * (r + 1) + 256);
 }
 
 }  // namespace
@@ -96,8 +111,9 @@ hipError_t launch_score_valu(const void *q_tilde, int qt_dt, const float *w, con
                              int max_len, const CacheView &cv, const int32_t *cand, int B,
                              int cand_rows, float *out, int64_t ld, hipStream_t st) {
   int TT = 64;
-  while (TT > 4 && valu_lds_bytes(H, cv.r, TT) > 160 * 1024) TT >>= 1;
-  const size_t lds = valu_lds_bytes(H, cv.r, TT);
+  const int ns = std::max(n_scales(cv), 1);
+  while (TT > 4 && valu_lds_bytes(H, cv.r, TT, ns) > 160 * 1024) TT >>= 1;
+  const size_t lds = valu_lds_bytes(H, cv.r, TT, ns);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   static DeviceOnce *const once = device_once_new();
   const hipError_t e = raise_lds_limit(once, (const void *)score_valu_kernel, 160 * 1024);

@@ -42,6 +42,7 @@ class LiCacheStruct(ctypes.Structure):
         ("block_size", ctypes.c_int32),
         ("r", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("scale_block", ctypes.c_int32),
     ]
 
 
@@ -144,30 +145,47 @@ class Cache:
     """A paged shared latent cache of one layer group (device tensors).
 
     data: [n_blocks, 64, r] float32 | bfloat16 | uint8 (E4M3FN codes)
-    scale: [n_blocks, 64] float32 for fp8, else None
+    scale: fp8 only: float32 [n_blocks, 64] (one scale per token) or
+           [n_blocks, 64, ceil(r / 128)] with scale_block = 128
     block_table: int32 [n_seq, max_blocks]
     """
 
     def __init__(self, data: torch.Tensor, block_table: torch.Tensor,
-                 scale: Optional[torch.Tensor] = None):
+                 scale: Optional[torch.Tensor] = None, scale_block: int = 0):
         _need(data, "cache data")
         _need(block_table, "block_table", torch.int32)
         if scale is not None:
             _need(scale, "scale", torch.float32)
+            ns = 1 if scale_block == 0 else -(-data.shape[2] // scale_block)
+            if scale.numel() != data.shape[0] * data.shape[1] * ns:
+                raise ValueError(f"scale must hold [n_blocks, 64, {ns}] values")
         self.data, self.block_table, self.scale = data, block_table, scale
+        self.scale_block = scale_block
         self.dtype = _dtype_code(data)
         self._s = LiCacheStruct(
             data=data.data_ptr(), scale=_ptr(scale), block_table=block_table.data_ptr(),
             n_seq=block_table.shape[0], max_blocks=block_table.shape[1],
-            n_blocks=data.shape[0], block_size=data.shape[1], r=data.shape[2], dtype=self.dtype)
+            n_blocks=data.shape[0], block_size=data.shape[1], r=data.shape[2], dtype=self.dtype,
+            scale_block=scale_block)
 
     @classmethod
-    def empty(cls, n_blocks: int, r: int, dtype: str, block_table: torch.Tensor, device="cuda"):
+    def empty(cls, n_blocks: int, r: int, dtype: str, block_table: torch.Tensor, device="cuda",
+              scale_block: int = 0):
         tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[dtype]
         data = torch.empty((n_blocks, BLOCK, r), dtype=tdt, device=device)
-        scale = torch.empty((n_blocks, BLOCK), dtype=torch.float32, device=device) \
-            if dtype == "fp8" else None
-        return cls(data, block_table, scale)
+        scale = None
+        if dtype == "fp8":
+            ns = 1 if scale_block == 0 else -(-r // scale_block)
+            shape = (n_blocks, BLOCK) if scale_block == 0 else (n_blocks, BLOCK, ns)
+            scale = torch.empty(shape, dtype=torch.float32, device=device)
+        return cls(data, block_table, scale, scale_block)
+
+    @property
+    def bytes_per_token(self) -> int:
+        """Bytes one token occupies in the cache (codes plus scales)."""
+        el = self.data.element_size() * self.data.shape[2]
+        return el + (0 if self.scale is None else
+                     4 * (self.scale.numel() // (self.data.shape[0] * self.data.shape[1])))
 
     @property
     def r(self) -> int:

@@ -36,7 +36,8 @@ class DeviceWorkload:
         self.wl = wl
         self.device = device
         bt = _t(wl.block_table, torch.int32, device)
-        self.cache = ops.Cache.empty(wl.n_phys_blocks, wl.r, wl.cache_dtype, bt, device)
+        self.cache = ops.Cache.empty(wl.n_phys_blocks, wl.r, wl.cache_dtype, bt, device,
+                                     scale_block=wl.scale_block)
         self.q_seq = _t(wl.q_seq, torch.int32, device)
         self.q_len = _t(wl.q_len, torch.int32, device)
         self.max_len = int(wl.q_len.max())
@@ -256,5 +257,9 @@ def read_cache_rows(cache: ops.Cache, block_table: np.ndarray, s: int, L: int):
         data = data.view(np.uint16)
     scale = None
     if cache.scale is not None:
-        scale = cache.scale.index_select(0, blocks).reshape(-1)[:L].cpu().numpy()
+        sc = cache.scale.index_select(0, blocks)
+        ns = sc.numel() // (nblk * BLOCK)
+        scale = sc.reshape(nblk * BLOCK, ns)[:L].cpu().numpy()
+        if cache.scale_block == 0:
+            scale = scale[:, 0].copy()
     return data, scale

@@ -78,6 +78,7 @@ class Workload:
     plant_factor: float
     _latent: Optional[list] = None   # per-sequence fp32 [L_s, r], drawn lazily
     prefill_positions: Optional[np.ndarray] = None  # int64 [n_q] (prefill only)
+    scale_block: int = 0             # fp8 cache: 0 (one scale per token) or 128
 
     @property
     def n_seq(self) -> int:
@@ -181,7 +182,7 @@ def _queries(seed, cfg_id, G, n_q, H, d_I):
 
 def make_decode(name, cfg_id, seed, *, G, H, r, d_I, k, B, cache_dtype, lens,
                 plant_frac=None, n_plant=None, plant_factor, permute_blocks,
-                nope_off=None, bias=False) -> Workload:
+                nope_off=None, bias=False, scale_block=0) -> Workload:
     lens = np.asarray(lens, dtype=np.int64)
     n_seq = len(lens)
     planted = []
@@ -202,7 +203,7 @@ def make_decode(name, cfg_id, seed, *, G, H, r, d_I, k, B, cache_dtype, lens,
         cache_dtype=cache_dtype, lens=lens, block_table=bt, n_phys_blocks=nphys,
         nope_off=no, Dt=Dt, b=b, q=q, w=w,
         q_seq=np.arange(n_seq, dtype=np.int32), q_len=lens.astype(np.int32),
-        planted=planted, plant_factor=plant_factor)
+        planted=planted, plant_factor=plant_factor, scale_block=scale_block)
 
 
 def ragged_lens(seed, cfg_id, n, lo=8192, hi=131072):
@@ -265,10 +266,11 @@ def make_prefill(seed: int = 0, n_q: int = 2048, L: int = 65536, H: int = 64, r:
 
 def small_decode(seed: int, *, n_seq=2, lens=None, H=8, r=32, d_I=16, G=2, k=16, B=None,
                  cache_dtype="fp32", nope_off=None, bias=False, plant=0, factor=4.0,
-                 permute=True, cfg_id=90) -> Workload:
+                 permute=True, cfg_id=90, scale_block=0) -> Workload:
     """A tiny decode workload for fast tests (ragged lengths allowed)."""
     if lens is None:
         lens = [100 + 37 * s for s in range(n_seq)]
     return make_decode(f"small-{cfg_id}", cfg_id, seed, G=G, H=H, r=r, d_I=d_I, k=k, B=B,
                        cache_dtype=cache_dtype, lens=lens, n_plant=plant, plant_factor=factor,
-                       permute_blocks=permute, nope_off=nope_off, bias=bias)
+                       permute_blocks=permute, nope_off=nope_off, bias=bias,
+                       scale_block=scale_block)

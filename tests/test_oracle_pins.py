@@ -429,3 +429,55 @@ def test_decode_group_hs_differs_from_full_when_budget_is_small():
     samp = O.decode_group(wl, 0, rows=rows)
     for l in range(wl.G):
         assert np.array_equal(samp["u"][l], out["u"][l][rows]) and samp["sel"] == {}
+
+
+# ------------------------------------------------ per-block fp8 scales ------
+
+def test_quantize_fp8_per_block_invariants_and_reductions():
+    """Per-128-value-block scales: every block's largest element maps to the
+    top code, each block's error is within half a step of its own scale;
+    block = 0 and block >= r are the per-row quantiser."""
+    rng = np.random.default_rng(12)
+    c = (rng.standard_normal((40, 192)) * rng.uniform(0.01, 50, (40, 1))).astype(np.float32)
+    c[:, 128:] *= 20.0                     # the two blocks differ in magnitude
+    c[3, 128:] = 0.0                       # an all-zero block
+    codes, scale = O.quantize_fp8(c, 128)
+    assert scale.shape == (40, 2) and scale.dtype == np.float32
+    assert scale[3, 1] == 1.0 and np.all(codes[3, 128:] == 0)
+    deq = O.dequantize_fp8(codes, scale, 128)
+    for i in range(40):
+        for g, (a, b) in enumerate([(0, 128), (128, 192)]):
+            if i == 3 and g == 1:
+                continue
+            j = a + int(np.argmax(np.abs(c[i, a:b])))
+            assert codes[i, j] & 0x7F == 0x7E
+            mag = np.abs(O.e4m3fn_decode(codes[i, a:b] & 0x7F))
+            e = np.floor(np.log2(np.maximum(mag, 2.0 ** -6)))
+            half_step = 2.0 ** (e - 4) * scale[i, g]
+            assert np.all(np.abs(deq[i, a:b] - c[i, a:b]) <= half_step * (1 + 1e-6) + 1e-12)
+    c0, s0 = O.quantize_fp8(c)
+    c1, s1 = O.quantize_fp8(c, 256)
+    assert np.array_equal(c0, c1) and np.array_equal(s0, s1[:, 0])
+    assert np.array_equal(O.dequantize_fp8(c0, s0), O.dequantize_fp8(c1, s1, 256))
+    # per-block scales track each block: the small block loses less precision
+    err_row = np.abs(O.dequantize_fp8(c0, s0)[:, :128] - c[:, :128]).mean()
+    err_blk = np.abs(deq[:, :128] - c[:, :128]).mean()
+    assert err_blk < err_row
+
+
+def test_two_scale_record_reproduces_the_storage_accounting():
+    """A 192-value latent stored as fp8 codes with one fp32 scale per
+    128-value block is a 200-byte record; with the native layer's 132-byte
+    key it gives the pages' per-token bytes and the 61.1% reduction."""
+    g = json.load(open(os.path.join(GOLDEN, "storage_accounting.json")))
+    rng = np.random.default_rng(13)
+    codes, scale = O.quantize_fp8(rng.standard_normal((5, 192)).astype(np.float32), 128)
+    record = codes[0].nbytes + scale[0].nbytes
+    assert record == g["latent_bytes"] == 200
+    dsa, li = O.indexer_cache_bytes_per_token(g["dsa_layers"], g["dsa_bytes_per_layer_token"],
+                                              g["group"], record, g["native_layers"])
+    assert (dsa, li) == (g["expect_dsa_bytes_per_token"], g["expect_li_bytes_per_token"])
+    assert round(100 * (1 - li / dsa), 1) == g["expect_reduction_percent_1dp"]
+    # one scale per token would be 196 bytes: not the pages' figure
+    c1, s1 = O.quantize_fp8(rng.standard_normal((5, 192)).astype(np.float32))
+    assert c1[0].nbytes + s1[:1].nbytes == 196
