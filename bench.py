@@ -371,6 +371,69 @@ def copy_ceiling(torch, flush, nbytes):
             "cold_us": cold, "cold_TBps": 2 * nbytes / cold / 1e6}
 
 
+def dsa_leg(torch, flush, W, DsaGroup, batch, K=20, Kc=6):
+    """The native DSA indexer over the group's four layers at 128K: warm
+    (back-to-back steps) and cold step times, and its layer-0 key scan."""
+    from sparse_attention_indexer_latent_amd import ops
+    g = DsaGroup([W.dsa_layer(l, [131072] * batch) for l in range(4)])
+    us = loop_us(torch, g.step, K)
+    cold = [timed_pair(torch, g.step, flush, scan=True) for _ in range(Kc)]
+    d = g.layers[0]
+    scan = ops.prepared_score(d.q[0], d.w[0], None, d.q_seq, d.q_len, d.max_len, d.cache, d.scores)
+    warm_scan = scan_b2b_us(torch, scan)
+    cold_scan = float(np.median([timed_pair(torch, scan, flush)[0] for _ in range(Kc)]))
+    sbytes = batch * 131072 * (d.cache.bytes_per_token + 4)
+    out = {"workload": f"native DSA indexer, 4 layers x own fp8 key cache ({d.cache.bytes_per_token} "
+                       f"B/token: 128 values + 1 fp32 scale), H=64, batch {batch} x 131072, "
+                       f"k=2048; per layer: append the new key, li_score_topk",
+           "us_per_group_step": us,
+           "cold_us_per_group_step": float(np.median([c[0] for c in cold])),
+           "scan_bytes_per_launch": sbytes,
+           "scan_us_warm": warm_scan, "scan_frac_warm": sbytes / (warm_scan * 1e-6) / HBM_PEAK,
+           "scan_us_cold": cold_scan, "scan_frac_cold": sbytes / (cold_scan * 1e-6) / HBM_PEAK,
+           "scored_tokens_per_s": 4 * batch * 131072 / (us * 1e-6)}
+    del g
+    torch.cuda.empty_cache()
+    return out
+
+
+def budget_sweep(torch, W, DeviceWorkload, Bs, r=192, dtype="fp8", sb=128, K=20):
+    """Candidate budget B against HS step time and the followers' recall of
+    their own full-scan selections (|S_HS ∩ S_full| / k, mean over followers
+    and queries) on the synthetic 128K batch-1 workload of the pages'
+    geometry.  Synthetic decoders share a common part (D_l = (G0 + 0.3 G_l) /
+    sqrt(r)), so these recalls describe this generator, not a trained model."""
+    from sparse_attention_indexer_latent_amd import ops
+    wl = W.hs_128k(1, r=r, cache_dtype=dtype, scale_block=sb, B=max(Bs))
+    dw = DeviceWorkload(wl, hold_last=True)
+    dw.full_step()
+    torch.cuda.synchronize()
+    full = dw.sel.cpu().numpy()
+    rows = []
+    for B in Bs:
+        cand = torch.empty((wl.n_q, B), dtype=torch.int32, device="cuda")
+        hs = torch.empty((wl.G, wl.n_q, wl.k), dtype=torch.int32, device="cuda")
+        aws = ops.hs_anchor_workspace(wl.n_q, dw.max_len)
+        fws = ops.hs_workspace(wl.n_q, B, wl.k, n_f=wl.G - 1)
+
+        def step(B=B, cand=cand, hs=hs, aws=aws, fws=fws):
+            dw._pre(True)
+            ops.hs_anchor(dw.q_tilde[0], dw.w[0], dw.beta[0], dw.q_seq, dw.q_len, dw.max_len,
+                          dw.cache, B, wl.k, scores=dw.scores, cand=cand, sel=hs[0], ws=aws)
+            ops.hs_select(cand, dw.q_tilde[1:], dw.w[1:], dw.beta[1:], dw.q_seq, dw.cache, wl.k,
+                          out_idx=hs[1:], ws=fws)
+        us = loop_us(torch, step, K)
+        h = hs.cpu().numpy()
+        rec = [len(set(h[l, s].tolist()) & set(full[l, s].tolist())) / wl.k
+               for l in range(1, wl.G) for s in range(wl.n_q)]
+        rows.append({"B": B, "us_per_group_step": us, "follower_recall": float(np.mean(rec)),
+                     "scored_positions": 131072 + (wl.G - 1) * min(B, 131072)})
+    del dw
+    torch.cuda.empty_cache()
+    return {"workload": f"{wl.name} with B varied (HS step: anchor scan + nested top-B/top-k, "
+                        f"3 followers rescore B candidates)", "points": rows}
+
+
 def batch1_128k(W):
     """The 128K batch-1 group: the batch-4 workload's generator for one
     sequence."""
@@ -524,6 +587,40 @@ def main():
                     legs["hs_" + name] = lh
                 del d
                 torch.cuda.empty_cache()
+            # the pages' geometry (192-value fp8 latent, 200-byte record) and
+            # the native DSA indexer of the same group, batch 1 and 4
+            from sparse_attention_indexer_latent_amd.runtime import DsaGroup
+            for batch in (1, 4):
+                wlp = W.hs_128k(batch, r=192, cache_dtype="fp8", scale_block=128)
+                d = DeviceWorkload(wlp, hold_last=True)
+                for hs_mode in (True, False):
+                    lp = leg(torch, flush, d, hs_mode)
+                    lp["workload"] = (f"{wlp.name}: {'HS' if hs_mode else 'full-scan'} step, "
+                                      f"{d.cache.bytes_per_token} B/token (192 fp8 values + 2 "
+                                      f"fp32 block scales), B={wlp.B}, k={wlp.k}")
+                    legs[f"{'hs' if hs_mode else 'full_scan'}_128k_b{batch}_fp8r192"] = lp
+                del d
+                torch.cuda.empty_cache()
+                legs[f"dsa_128k_b{batch}"] = dsa_leg(torch, flush, W, DsaGroup, batch)
+                dsa = legs[f"dsa_128k_b{batch}"]
+                hsp = legs[f"hs_128k_b{batch}_fp8r192"]
+                out[f"hs_speedup_vs_dsa_128k_b{batch}"] = {
+                    "fp8r192_200B": dsa["us_per_group_step"] / hsp["us_per_group_step"],
+                    "fp8r192_200B_cold": dsa["cold_us_per_group_step"] / hsp["cold_us_per_group_step"],
+                    "bf16r256": dsa["us_per_group_step"] / (
+                        legs["hs_128k_b1"]["us_per_group_step"] if batch == 1 else us_step),
+                    "pages_table4_context": "2.30-2.72x (ms per decode token, all 61 indexers, "
+                                            "batch 1, eight unnamed GPUs)"}
+            out["b_sweep"] = budget_sweep(torch, W, DeviceWorkload, [2048, 4096, 8192, 16384, 32768])
+            wl8 = W.hs_128k(1, G=8, name="hs-128k-b1-bf16-r256-G8")
+            d8 = DeviceWorkload(wl8, hold_last=True)
+            for hs_mode in (True, False):
+                l8 = leg(torch, flush, d8, hs_mode)
+                l8["workload"] = (f"{wl8.name}: {'HS' if hs_mode else 'full-scan'} step of an "
+                                  f"8-layer group (7 followers), B={wl8.B}")
+                legs[f"{'hs' if hs_mode else 'full_scan'}_128k_b1_G8"] = l8
+            del d8
+            torch.cuda.empty_cache()
             out["legs"] = legs
         del flush
 

@@ -29,8 +29,8 @@
 //    bf16 q~ as is), beta as the accumulators' start value;
 //  * fp8: v_mfma_f32_16x16x128_f8f6f4 with both operands fp8: each head's q~
 //    is scaled by a power of two that brings its largest element into
-//    (224, 448] and split into three E4M3 terms (two for a bf16 q~), each the
-//    rounding of what the earlier terms left (about 2^-12 relative); the
+//    (224, 448] and split into two E4M3 terms, the second the rounding of
+//    what the first left (about 2^-8 relative, a bf16 q~'s precision); the
 //    token's scale(s) and the head's power of two multiply the fp32 dot
 //    product before beta and ReLU.
 // The epilogue (ReLU, x w, sum over 16 heads) reduces across lanes and the
@@ -178,9 +178,10 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
   using C = Cfg<EB, R, NSC>;
   constexpr bool C8 = C::C8;
   constexpr int TU = C::TU, NST = C::NST, KB = C::KB, NTILE = C::NTILE;
-  // A operand terms: bf16 hi + lo of an fp32 q~, or the bf16 q~; fp8: three
-  // terms of an fp32 q~, two of a bf16 q~
-  constexpr int NT = C8 ? (QF32 ? 3 : 2) : (QF32 ? 2 : 1);
+  // A operand terms: bf16 hi + lo of an fp32 q~, or the bf16 q~; fp8: two
+  // terms (each the E4M3 rounding of what the earlier left: about 2^-8
+  // relative, the precision of a bf16 q~, well inside the fp8 cache's own)
+  constexpr int NT = C8 ? 2 : (QF32 ? 2 : 1);
   constexpr int QROWB = QF32 ? 4 * R : 2 * R;  // bytes of one head's q~ row
   constexpr int QCH = QROWB / 16;              // 16-byte chunks of a q~ row
   // q~ rows swizzle their chunks within aligned groups of 16 (or of 8 when
@@ -487,22 +488,48 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
   // ---- compute: A operands of heads 16 hg .. +15 from the q~ copy -----------
   // bf16: lane holds k = kb*32 + (lane/16)*8 + [0, 8) of head 16 hg + lane%16;
   // fp8: k = kb*128 + (lane/16)*32 + [0, 32).  k >= R holds zero.
+  // The lane's raw q~ words leave LDS first; once every wavefront has them
+  // the q~ stages are free, and the main loop's first barrier hands them to
+  // the issuers.  (Issuing into them right here delays unit 0: those loads
+  // queue ahead of the wait for it.)
+  constexpr int RAW = C8 ? KB * (QF32 ? 8 : 4) : (QF32 ? 2 * KB : KB);  // 16-byte chunks
+  uint4 qr[RAW];
+  if (!issuer) {
+    const int h = 16 * hg + (lane & 15);
+    auto qchunk = [&](int c) INL -> uint4 {  // 16-byte chunk c of the head's row
+      return *(const uint4 *)(qst + h * QROWB + ((c ^ (h & QSWZ)) * 16));
+    };
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if constexpr (!C8) {
+        if constexpr (QF32) {  // floats kb*32 + (lane/16)*8 .. +7: chunks c0, c0 + 1
+          const int c0 = 2 * (kb * 4 + (lane >> 4));
+          qr[2 * kb] = qchunk(c0);
+          qr[2 * kb + 1] = qchunk(c0 + 1);
+        } else {
+          qr[kb] = qchunk(kb * 4 + (lane >> 4));
+        }
+      } else {
+        const int k0 = kb * 128 + (lane >> 4) * 32;
+        const bool in = k0 < R;  // R is a multiple of 64: a lane's 32 are all in or all out
+        constexpr int NCH = QF32 ? 8 : 4;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          qr[kb * NCH + c] = in ? qchunk((k0 * (QF32 ? 4 : 2)) / 16 + c) : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+  lds_barrier();  // the q~ copy is read: its stages take units from here on
+
   Frag abf[C8 ? 1 : NT][C8 ? 1 : KB];
   i32x8 a8[C8 ? NT : 1][C8 ? KB : 1];
   float hs[4];  // fp8: the power of two of heads 16 hg + 4 (lane/16) + i, as 2^-k
   if (!issuer) {
-    const int h = 16 * hg + (lane & 15);
-    // element k of head h from the staged copy (0 beyond R)
-    auto qchunk = [&](int c) INL -> uint4 {  // 16-byte chunk c of the head's row
-      return *(const uint4 *)(qst + h * QROWB + ((c ^ (h & QSWZ)) * 16));
-    };
     if constexpr (!C8) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         if constexpr (QF32) {
-          // floats kb*32 + (lane/16)*8 .. +7: chunks c0 and c0 + 1
-          const int c0 = 2 * (kb * 4 + (lane >> 4));
-          const uint4 x0 = qchunk(c0), x1 = qchunk(c0 + 1);
+          const uint4 x0 = qr[2 * kb], x1 = qr[2 * kb + 1];
           const float xs[8] = {__uint_as_float(x0.x), __uint_as_float(x0.y), __uint_as_float(x0.z),
                                __uint_as_float(x0.w), __uint_as_float(x1.x), __uint_as_float(x1.y),
                                __uint_as_float(x1.z), __uint_as_float(x1.w)};
@@ -518,7 +545,7 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
             abf[NT - 1][kb].u[e] = __builtin_bit_cast(uint32_t, lo);
           }
         } else {
-          const uint4 x = qchunk(kb * 4 + (lane >> 4));
+          const uint4 x = qr[kb];
           abf[0][kb].u[0] = x.x; abf[0][kb].u[1] = x.y; abf[0][kb].u[2] = x.z; abf[0][kb].u[3] = x.w;
         }
       }
@@ -527,11 +554,10 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
       float qv[KB][32];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int k0 = kb * 128 + (lane >> 4) * 32;
-        const bool in = k0 < R;  // R is a multiple of 64: a lane's 32 are all in or all out
+        constexpr int NCH = QF32 ? 8 : 4;
 #pragma unroll
-        for (int c = 0; c < (QF32 ? 8 : 4); ++c) {
-          const uint4 x = in ? qchunk((k0 * (QF32 ? 4 : 2)) / 16 + c) : make_uint4(0u, 0u, 0u, 0u);
+        for (int c = 0; c < NCH; ++c) {
+          const uint4 x = qr[kb * NCH + c];
           if constexpr (QF32) {
             qv[kb][4 * c + 0] = __uint_as_float(x.x); qv[kb][4 * c + 1] = __uint_as_float(x.y);
             qv[kb][4 * c + 2] = __uint_as_float(x.z); qv[kb][4 * c + 3] = __uint_as_float(x.w);
@@ -581,7 +607,6 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
       }
     }
   }
-  lds_barrier();  // the q~ copy is read: its stages take units from here on
 
   // ---- main loop: one barrier per unit ---------------------------------------
   // Compute wave (hg, th): tiles j of tokens th * TU/2 + 16 j + lane%16.
@@ -652,27 +677,34 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
       const char *sp = sh.stage[p % NST];
       f32x4 acc[NTILE][C8 ? NSC : 1];
       float sc[NTILE][NSC];
+      // tiles in pairs, their independent accumulation chains interleaved
 #pragma unroll
-      for (int j = 0; j < NTILE; ++j) {
-        const int t = th * (TU / 2) + 16 * j + (lane & 15);  // token of the unit
-        const int row = t / C::TPR, hslot = t % C::TPR;
-        const char *rp = sp + row * C::LROWB;
-        auto lds_chunk = [&](int lc) INL -> uint4 {  // logical chunk lc of the row
-          return *(const uint4 *)(rp + ((lc ^ (row & kSwz)) * 16));
+      for (int jp = 0; jp < NTILE / 2; ++jp) {
+        const int t0 = th * (TU / 2) + 32 * jp + (lane & 15), t1 = t0 + 16;  // tokens of the unit
+        const int row0 = t0 / C::TPR, row1 = t1 / C::TPR;
+        const int hs0 = t0 % C::TPR, hs1 = t1 % C::TPR;
+        const char *rp0 = sp + row0 * C::LROWB, *rp1 = sp + row1 * C::LROWB;
+        auto chunk0 = [&](int lc) INL -> uint4 {  // logical chunk lc of tile 2 jp's row
+          return *(const uint4 *)(rp0 + ((lc ^ (row0 & kSwz)) * 16));
         };
+        auto chunk1 = [&](int lc) INL -> uint4 {
+          return *(const uint4 *)(rp1 + ((lc ^ (row1 & kSwz)) * 16));
+        };
+        f32x4 &a0 = acc[2 * jp][0], &a1 = acc[2 * jp + 1][0];
         if constexpr (!C8) {
-          acc[j][0] = f32x4{bv[0], bv[1], bv[2], bv[3]};
+          a0 = f32x4{bv[0], bv[1], bv[2], bv[3]};
+          a1 = a0;
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             // half of the k-steps at a time keeps the B fragments few
             constexpr int KH = (KB + 1) / 2;
-            bf16x8 bfr[KH];
+            bf16x8 b0[KH], b1[KH];
 #pragma unroll
             for (int k = 0; k < KH; ++k) {
               const int kb = half * KH + k;
               if (kb < KB) {
-                const uint4 x = lds_chunk(hslot * C::CPS + kb * 4 + (lane >> 4));
-                bfr[k] = __builtin_bit_cast(bf16x8, x);
+                b0[k] = __builtin_bit_cast(bf16x8, chunk0(hs0 * C::CPS + kb * 4 + (lane >> 4)));
+                b1[k] = __builtin_bit_cast(bf16x8, chunk1(hs1 * C::CPS + kb * 4 + (lane >> 4)));
               }
             }
 #pragma unroll
@@ -680,31 +712,48 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
               const int kb = half * KH + k;
               if (kb < KB) {
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt)
-                  acc[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abf[tt][kb].v, bfr[k],
-                                                                      acc[j][0], 0, 0, 0);
+                for (int tt = 0; tt < NT; ++tt) {
+                  a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abf[tt][kb].v, b0[k], a0, 0, 0, 0);
+                  a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abf[tt][kb].v, b1[k], a1, 0, 0, 0);
+                }
               }
             }
           }
         } else {
 #pragma unroll
-          for (int s = 0; s < NSC; ++s) acc[j][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int s2 = 0; s2 < NSC; ++s2) {
+            acc[2 * jp][s2] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[2 * jp + 1][s2] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          i32x8 bb0[KB], bb1[KB];
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
-            const int lc0 = hslot * C::CPS + kb * 8 + 2 * (lane >> 4);
-            const uint4 x0 = lds_chunk(lc0), x1 = lds_chunk(lc0 + 1);
-            const i32x8 bb = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                              (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+            const int lc0 = hs0 * C::CPS + kb * 8 + 2 * (lane >> 4);
+            const int lc1 = hs1 * C::CPS + kb * 8 + 2 * (lane >> 4);
+            const uint4 x0 = chunk0(lc0), x1 = chunk0(lc0 + 1);
+            const uint4 y0 = chunk1(lc1), y1 = chunk1(lc1 + 1);
+            bb0[kb] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                            (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+            bb1[kb] = i32x8{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w,
+                            (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
+          }
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const int s2 = NSC == 1 ? 0 : kb;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
-              const int s = NSC == 1 ? 0 : kb;
               // operands fp8 E4M3 (format code 0) for A and B
-              acc[j][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  a8[tt][kb], bb, acc[j][s], 0, 0, 0, 0, 0, 0);
+              acc[2 * jp][s2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  a8[tt][kb], bb0[kb], acc[2 * jp][s2], 0, 0, 0, 0, 0, 0);
+              acc[2 * jp + 1][s2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  a8[tt][kb], bb1[kb], acc[2 * jp + 1][s2], 0, 0, 0, 0, 0, 0);
             }
           }
 #pragma unroll
-          for (int s = 0; s < NSC; ++s) sc[j][s] = sh.ssc[p % NST][t * NSC + s];
+          for (int s2 = 0; s2 < NSC; ++s2) {
+            sc[2 * jp][s2] = sh.ssc[p % NST][t0 * NSC + s2];
+            sc[2 * jp + 1][s2] = sh.ssc[p % NST][t1 * NSC + s2];
+          }
         }
       }
       if (p >= 1) epilogue(p - 1);

@@ -247,6 +247,28 @@ class StepGraphs:
         post.replay()
 
 
+class DsaGroup:
+    """The native DSA indexer over the same G layers, for comparison: each
+    layer appends its new token's key to its own fp8 key cache and scores
+    that cache with its own queries (no shared latent, no absorption: the
+    query itself takes the absorbed query's place), then keeps its top-k,
+    all through the same library calls (li_append_latent, li_score_topk)."""
+
+    def __init__(self, layers, device="cuda"):
+        self.layers = [DeviceWorkload(wl, device=device, hold_last=True) for wl in layers]
+
+    def step(self, events=None) -> None:
+        for i, d in enumerate(self.layers):
+            d.append()
+            raw = None if (events is None or i) else (events[0].e, events[1].e)
+            ops.score_topk(d.q[0], d.w[0], None, d.q_seq, d.q_len, d.max_len, d.cache, d.wl.k,
+                           scores=d.scores, out_idx=d.sel[0], ws=d.full_ws, scan_events=raw)
+
+    def scan0(self) -> None:
+        d = self.layers[0]
+        ops.score(d.q[0], d.w[0], None, d.q_seq, d.q_len, d.max_len, d.cache, scores=d.scores)
+
+
 def read_cache_rows(cache: ops.Cache, block_table: np.ndarray, s: int, L: int):
     """Host copy of sequence s's first L stored rows (and scales) in token order."""
     nblk = (L + BLOCK - 1) // BLOCK

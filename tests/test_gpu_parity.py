@@ -752,3 +752,31 @@ def test_graph_replays_match_eager():
         g_full.replay()
         torch.cuda.synchronize()
         assert torch.equal(dw.sel, ref_full), rep
+
+
+def test_hs_group_of_eight_layers():
+    """A group of eight layers (seven followers share the anchor's
+    candidates): every follower's candidate scores against the oracle and
+    its selection exact on them; the one-call follower step equals one call
+    per follower."""
+    say("HS with G = 8 (seven followers)")
+    wl = W.small_decode(19, n_seq=2, lens=[6000, 2500], H=64, r=256, d_I=128, G=8, k=128, B=1024,
+                        cache_dtype="bf16", plant=20, factor=3.0)
+    dw = DeviceWorkload(wl, hold_last=False)
+    dw.hs_step(append=False, keep_scores=True)
+    torch.cuda.synchronize()
+    cand = dw.cand.cpu().numpy()
+    sel = dw.hs_sel.cpu().numpy()
+    cs_all = dw.cand_scores.cpu().numpy()
+    for s in range(wl.n_q):
+        L = int(wl.q_len[s])
+        nc = min(wl.B, L)
+        C = O.sequence_latent(wl, s)
+        for l in range(1, wl.G):
+            o = O.layer_scores(C[cand[s, :nc]], wl.q[l, s], wl.Dt[l], wl.b[l], wl.nope_off, wl.w[l, s])
+            assert_scores_close(cs_all[l, s, :nc], o, RTOL_BF16, f"G=8 follower {l} query {s}")
+            ref = O.pad(O.hs_follower(cand[s, :nc], cs_all[l, s, :nc].astype(np.float64), wl.k), wl.k)
+            assert np.array_equal(sel[l, s], ref), (l, s)
+    for l in (1, 7):
+        one = ops.hs_select(dw.cand, dw.q_tilde[l], dw.w[l], dw.beta[l], dw.q_seq, dw.cache, wl.k)
+        assert torch.equal(one, dw.hs_sel[l]), l

@@ -131,3 +131,31 @@ def test_scan_shapes_hs_followers(shape):
             assert_scores_close(cs[:nc], o, RT[dt], f"HS {_id(shape)} follower {l} query {s}")
             refsel = O.pad(O.hs_follower(cand[s, :nc], cs[:nc].astype(np.float64), wl.k), wl.k)
             assert np.array_equal(sel[l, s], refsel), (l, s)
+
+
+def test_dsa_comparator_group_step():
+    """The native DSA comparator: four layers, each with its own fp8 key
+    cache (128 values + one scale, 132 B per token), append then
+    li_score_topk per layer.  Scores against the oracle (the raw query
+    against each stored key), selections exact on the dumped scores and in
+    the threshold band of the oracle's own scores."""
+    from sparse_attention_indexer_latent_amd.runtime import DsaGroup
+    from parity_util import assert_selection_band
+    lens = [9000, 4100, 300]
+    say(f"DSA comparator group step, lens {lens}")
+    layers = [W.dsa_layer(l, lens, k=512) for l in range(4)]
+    g = DsaGroup(layers)
+    g.step()
+    torch.cuda.synchronize()
+    for l, d in enumerate(g.layers):
+        wl = d.wl
+        assert d.cache.bytes_per_token == 132
+        u = d.scores.cpu().numpy()
+        sel = d.sel[0].cpu().numpy()
+        for s in range(wl.n_q):
+            L = int(wl.q_len[s])
+            K = O.sequence_latent(wl, s)[:L]
+            o = O.absorbed_scores(K, wl.q[0, s].astype(np.float64), None, wl.w[0, s])
+            assert_scores_close(u[s, :L], o, RTOL_FP8, f"DSA layer {l} query {s}")
+            assert np.array_equal(sel[s], O.pad(O.topk(u[s, :L].astype(np.float64), wl.k), wl.k))
+            assert_selection_band(sel[s], o, wl.k, RTOL_FP8, f"DSA layer {l} top-k query {s}")
