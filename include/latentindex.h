@@ -189,12 +189,13 @@ li_status li_append_absorb(const void *x, li_dtype x_dt, int32_t n_tok, const fl
  *    within 2^-16 relative of q~; a BF16 q~ is used as is.  Products are
  *    exact, sums in fp32.
  *  - FP8 cache, H = 64, r = 128, 192 or 256 (and at most 64 queries, or
- *    r = 256 with one scale per token): fp8 matrix cores.  Each head's q~ is scaled
- *    by a power of two (largest element into (224, 448]) and split into three
- *    E4M3 terms, each the rounding of what the earlier terms left (two terms
- *    for a BF16 q~), which represents q~ to about 2^-12 relative; the matrix
- *    core accumulates each 128-long group of exact fp8 products in fp32 to
- *    about 2^-11 of the group's largest product.
+ *    r = 256 with one scale per token): fp8 matrix cores.  Each head's q~ is
+ *    scaled by a power of two (largest element into (224, 448]) and split
+ *    into E4M3 terms, each the rounding of what the earlier terms left: two
+ *    terms with at most 64 queries (about 2^-8 relative, a bf16 q~'s
+ *    precision), three above that (about 2^-12; two for a BF16 q~); the
+ *    matrix core accumulates each 128-long group of exact fp8 products in
+ *    fp32 to about 2^-11 of the group's largest product.
  *  The FP8 scales (and the head's power of two) multiply the dot products
  *  of their blocks before beta and ReLU.
  */
@@ -322,6 +323,29 @@ li_status li_hs_select(const int32_t *cand, int32_t B, int32_t n_f, const void *
                        li_dtype qt_dt, const float *w, const float *beta, int32_t n_q, int32_t H,
                        const int32_t *q_seq, const li_cache *cache, int32_t k, int32_t *out_idx,
                        float *cand_scores, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * li_calib_gram -- the normal equations of the training-free calibration
+ * ("Methodology", Training-free Calibration: ridge reduced-rank regression
+ * jointly fitting the group's shared projection and every layer's decoder
+ * to the layers' indexer keys): over n calibration tokens,
+ *   G_xx = X^T X, G_xy = X^T Y, x_sum = X^T 1, y_sum = Y^T 1,
+ * written (accumulate == 0) or added to what the outputs hold (so that the
+ * tokens can come in batches).  The closed-form solves that follow work on
+ * these small matrices.
+ *   X      device [n, d] of x_dt (FP32 or BF16): the anchor hidden states.
+ *   Y      device [n, e] of y_dt (FP32 or BF16), or NULL: the layers' keys,
+ *          stacked along columns.
+ *   G_xx   device fp32 [d, d] (out); G_xy device fp32 [d, e] (out, may be
+ *          NULL); x_sum device fp32 [d], y_sum device fp32 [e] (out, each
+ *          may be NULL).
+ * Products exact in fp32 on the matrix cores, sums in fp32 in a fixed order
+ * (deterministic).  1 <= d, e <= 65536; n >= 0 (n == 0 with accumulate == 0
+ * writes zeros).
+ */
+li_status li_calib_gram(const void *X, li_dtype x_dt, int64_t n, int32_t d, const void *Y,
+                        li_dtype y_dt, int32_t e, float *G_xx, float *G_xy, float *x_sum,
+                        float *y_sum, int32_t accumulate, void *stream);
 
 /*
  * li_hs_select_noalloc -- li_hs_select for callers that cannot allocate

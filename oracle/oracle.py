@@ -44,6 +44,16 @@ Pins (tests/test_oracle_pins.py; none re-types the formula it checks):
                       HS = full for every follower; a follower with the
                       anchor's operands returns S_anchor; HS picks stay in C
   accounting          the numbers printed in [P4] and [P1] (tests/golden)
+  ridge_rrr           full rank and lam = 0 is numpy's least squares; lam > 0
+                      is least squares on the augmented system [X; sqrt(lam)
+                      I]; rank r at lam = 0 is the Eckart-Young truncation of
+                      the least-squares fit (numpy SVD of X B_ls)
+  calibrate_nope      recovers an exact shared-rank group model (projection,
+                      decoders and biases up to the latent basis) from noise-
+                      free keys
+  calibrate_rope      the fitted decoder commutes with the rotation (eq. 4)
+                      and recovers keys made by an exact complex-per-frequency
+                      model
 Parity unpinned: none of the functions above.  The planted-token structure of
 the synthetic workloads is not pinned by the pages (they print no scores).
 """
@@ -353,6 +363,79 @@ def decode_group(wl, s: int, C: Optional[np.ndarray] = None, layers=None,
             out["u_f"][l] = uf
             out["hs_sel"][l] = hs_follower(cand, uf, wl.k)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Training-free calibration ([P1] Methodology, Training-free Calibration:
+# ridge reduced-rank regression jointly fits the group's shared projection and
+# every layer's decoder from calibration hidden states and the layers' own
+# indexer keys, minimising key-reconstruction error at a given latent rank;
+# the NoPE and RoPE branches are fitted separately, each in closed form).
+# ---------------------------------------------------------------------------
+
+
+def ridge_rrr(X: np.ndarray, Y: np.ndarray, rank: int, lam: float):
+    """min_B ||Y - X B||_F^2 + lam ||B||_F^2 subject to rank(B) <= rank, the
+    reduced-rank ridge regression of Mukherjee and Zhu ("Reduced rank ridge
+    regression and its kernel extensions", 2011): B_lam = (X^T X + lam I)^-1
+    X^T Y is the ridge fit; the rank constraint keeps the top `rank` right
+    singular vectors V of the augmented fit [X B_lam; sqrt(lam) B_lam], and
+    B = B_lam V V^*.  Works for real or complex Y (X real).  Returns
+    (P = B_lam V [d, rank], D = conj(V) [e, rank]) with B = P D^T."""
+    X = np.asarray(X, dtype=F64)
+    Y = np.asarray(Y)
+    Y = Y.astype(np.complex128 if np.iscomplexobj(Y) else F64)
+    d = X.shape[1]
+    B_lam = np.linalg.solve(X.T @ X + lam * np.eye(d), X.T @ Y)
+    aug = np.concatenate([X @ B_lam, np.sqrt(lam) * B_lam], axis=0)
+    V = np.linalg.svd(aug, full_matrices=False)[2].conj().T[:, :rank]    # [e, rank]
+    return B_lam @ V, V.conj()
+
+
+def calibrate_nope(X: np.ndarray, keys: list, rank: int, lam: float):
+    """NoPE branch: one projection P_N [d_model, r_N] shared by the group and
+    each layer's decoder D^(l),N [d_N, r_N] and bias b^(l) (eq. 3) from
+    hidden states X [n, d_model] and the layers' NoPE keys keys[l] [n, d_N].
+    The bias takes the means (the fit runs on centred data).  Returns
+    (P_N, [D^(l),N], [b^(l)])."""
+    X = np.asarray(X, dtype=F64)
+    Ys = [np.asarray(k, dtype=F64) for k in keys]
+    xm = X.mean(axis=0)
+    Y = np.concatenate(Ys, axis=1)
+    ym = Y.mean(axis=0)
+    P, D = ridge_rrr(X - xm, Y - ym, rank, lam)
+    b = ym - D @ (P.T @ xm)
+    dn = Ys[0].shape[1]
+    return P, [D[l * dn:(l + 1) * dn] for l in range(len(Ys))], \
+        [b[l * dn:(l + 1) * dn] for l in range(len(Ys))]
+
+
+def calibrate_rope(X: np.ndarray, keys: list, pairs_per_freq: int, lam: float):
+    """RoPE branch (eqs. 1, 3-4): keys[l] [n, d_R] are layer l's rotary
+    key coordinates before rotation, pair (2j, 2j+1) at frequency j.  The
+    decoder may only mix pairs of one frequency, as complex scalars (then it
+    commutes with the rotation, eq. 4), so each frequency is its own complex
+    ridge reduced-rank regression of the layers' pairs [n, m] on X, at rank
+    pairs_per_freq.  Returns (P_R [d_model, r_R] with latent pair (2q, 2q+1) =
+    (Re, Im) of the q-th complex latent, q = j * pairs_per_freq + i, and
+    [D^(l),R [d_R, r_R]] in real form)."""
+    X = np.asarray(X, dtype=F64)
+    Ks = [np.asarray(k, dtype=F64) for k in keys]
+    m, n_freq = len(Ks), Ks[0].shape[1] // 2
+    a = pairs_per_freq
+    P_R = np.zeros((X.shape[1], 2 * n_freq * a))
+    D_R = [np.zeros((2 * n_freq, 2 * n_freq * a)) for _ in range(m)]
+    for j in range(n_freq):
+        Yf = np.stack([K[:, 2 * j] + 1j * K[:, 2 * j + 1] for K in Ks], axis=1)   # [n, m]
+        P, D = ridge_rrr(X, Yf, a, lam)          # zeta = X P [n, a]; pair_l = zeta D[l]^T
+        for i in range(a):
+            q = j * a + i
+            P_R[:, 2 * q], P_R[:, 2 * q + 1] = P[:, i].real, P[:, i].imag
+            for l in range(m):
+                c = D[l, i]                        # complex scalar: pair_j += c * zeta_q
+                D_R[l][2 * j, 2 * q], D_R[l][2 * j, 2 * q + 1] = c.real, -c.imag
+                D_R[l][2 * j + 1, 2 * q], D_R[l][2 * j + 1, 2 * q + 1] = c.imag, c.real
+    return P_R, D_R
 
 
 # ---------------------------------------------------------------------------

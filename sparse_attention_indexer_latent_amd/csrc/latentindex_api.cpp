@@ -370,6 +370,27 @@ li_status li_score_topk(const void *q_tilde, li_dtype qt_dt, const float *w, con
                       k, out_idx, k, nullptr, ws, ws_bytes, scan_events, stream);
 }
 
+li_status li_calib_gram(const void *X, li_dtype x_dt, int64_t n, int32_t d, const void *Y,
+                        li_dtype y_dt, int32_t e, float *G_xx, float *G_xy, float *x_sum,
+                        float *y_sum, int32_t accumulate, void *stream) {
+  if (x_dt != LI_FP32 && x_dt != LI_BF16) return fail(LI_ERR_INVALID, "X dtype must be FP32 or BF16");
+  if (n < 0) return fail(LI_ERR_INVALID, "n < 0");
+  if (d < 1 || d > 65536) return fail(LI_ERR_INVALID, "d = %d out of [1, 65536]", d);
+  if (!X && n > 0) return fail(LI_ERR_INVALID, "X is NULL");
+  if (!G_xx) return fail(LI_ERR_INVALID, "G_xx is NULL");
+  if (Y) {
+    if (y_dt != LI_FP32 && y_dt != LI_BF16) return fail(LI_ERR_INVALID, "Y dtype must be FP32 or BF16");
+    if (e < 1 || e > 65536) return fail(LI_ERR_INVALID, "e = %d out of [1, 65536]", e);
+  } else if (G_xy || y_sum) {
+    return fail(LI_ERR_INVALID, "G_xy / y_sum need Y");
+  }
+  li_status s = check_device();
+  if (s != LI_OK) return s;
+  return hip_status(li::launch_calib_gram(X, x_dt == LI_BF16, n, d, Y, y_dt == LI_BF16, e, G_xx,
+                                          G_xy, x_sum, y_sum, accumulate, (hipStream_t)stream),
+                    "li_calib_gram launch");
+}
+
 size_t li_hs_workspace_bytes(int32_t n_f, int32_t n_q, int32_t B, int32_t k) {
   if (n_f <= 0 || n_q <= 0 || B <= 0 || k <= 0) return 0;
   const int64_t rows = (int64_t)n_f * n_q;

@@ -136,6 +136,12 @@ hipError_t launch_topk2_counted(const float *scores, int64_t ld, int n_rows, con
                                 int max_len, int k_outer, int32_t *out_outer, int k_inner,
                                 int32_t *out_inner, void *ws, hipStream_t st);
 
+// calib.hip: normal equations of the calibration (G_xx = X^T X, G_xy = X^T Y,
+// column sums), written or added to.
+hipError_t launch_calib_gram(const void *X, int x_bf16, int64_t n, int d, const void *Y,
+                             int y_bf16, int e, float *G_xx, float *G_xy, float *x_sum,
+                             float *y_sum, int accumulate, hipStream_t st);
+
 // Fill n int32 values with v (device).
 hipError_t launch_fill_i32(int32_t *dst, int n, int32_t v, hipStream_t st);
 

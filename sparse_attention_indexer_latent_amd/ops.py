@@ -72,6 +72,7 @@ _SIGS = {
     "li_score_topk": (_I32, [_P, _I32, _P, _P, _I32, _I32, _P, _P, _I32,
                              ctypes.POINTER(LiCacheStruct), _P, _I64, _I32, _P, _P, _SZ, _P, _P]),
     "li_hs_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "li_calib_gram": (_I32, [_P, _I32, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _P, _I32, _P]),
     "li_hs_select": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P,
                             ctypes.POINTER(LiCacheStruct), _I32, _P, _P, _P, _SZ, _P]),
     "li_hs_select_noalloc": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P,
@@ -557,3 +558,33 @@ def hs_select(cand: torch.Tensor, q_tilde: torch.Tensor, w: torch.Tensor,
                               k, out_idx.data_ptr(), _ptr(cand_scores), ws.data_ptr(), ws.numel(),
                               _stream()))
     return (out_idx, cand_scores) if want_scores else out_idx
+
+
+def calib_gram(X: torch.Tensor, Y: Optional[torch.Tensor] = None, G_xx=None, G_xy=None,
+               x_sum=None, y_sum=None, accumulate: bool = False):
+    """Normal equations of the calibration: (X^T X, X^T Y, X^T 1, Y^T 1) over
+    the rows of X [n, d] and Y [n, e] (fp32 or bf16 device tensors), written
+    or, with accumulate, added to the given outputs."""
+    _need(X, "X", (torch.float32, torch.bfloat16))
+    n, d = X.shape
+    dev = X.device
+    if Y is not None:
+        _need(Y, "Y", (torch.float32, torch.bfloat16))
+        if Y.shape[0] != n:
+            raise ValueError("X and Y must have the same rows")
+    e = Y.shape[1] if Y is not None else 1
+    mk = lambda shape: torch.zeros(shape, dtype=torch.float32, device=dev)  # noqa: E731
+    G_xx = mk((d, d)) if G_xx is None else G_xx
+    x_sum = mk((d,)) if x_sum is None else x_sum
+    if Y is not None:
+        G_xy = mk((d, e)) if G_xy is None else G_xy
+        y_sum = mk((e,)) if y_sum is None else y_sum
+    for t, nm, cnt in ((G_xx, "G_xx", d * d), (G_xy, "G_xy", d * e), (x_sum, "x_sum", d),
+                       (y_sum, "y_sum", e)):
+        if t is not None:
+            _need(t, nm, torch.float32)
+            _numel(t, cnt, nm)
+    _check(lib().li_calib_gram(X.data_ptr(), _dtype_code(X), n, d, _ptr(Y),
+                               _dtype_code(Y) if Y is not None else LI_FP32, e, G_xx.data_ptr(),
+                               _ptr(G_xy), _ptr(x_sum), _ptr(y_sum), int(accumulate), _stream()))
+    return G_xx, G_xy, x_sum, y_sum

@@ -246,6 +246,58 @@ def config(i: int, seed: int = 0) -> Workload:
     raise ValueError(f"no configuration {i}")
 
 
+def hs_128k(batch: int, seed: int = 0, r: int = 256, cache_dtype: str = "bf16",
+            scale_block: int = 0, B: int = 8192, G: int = 4, name: str = None) -> Workload:
+    """The 128K hierarchical-selection workload (the batch-4 configuration's
+    generator) at any batch, latent width, cache type, candidate budget and
+    group size.  r = 192 with an fp8 cache and scale_block = 128 is the
+    DeepSeek-V3.2 geometry of the LatentIndex explainer's storage paragraph
+    (192 values, a 200-byte record)."""
+    name = name or f"hs-128k-b{batch}-{cache_dtype}-r{r}" + (f"-sb{scale_block}" if scale_block
+                                                               else "")
+    return make_decode(name, 3 if r == 256 else 5, seed, G=G, H=64, r=r, d_I=128, k=2048, B=B,
+                       cache_dtype=cache_dtype, lens=[131072] * batch, plant_frac=0.01,
+                       plant_factor=3.0, permute_blocks=True, scale_block=scale_block)
+
+
+def dsa_layer(layer: int, lens, seed: int = 0, H: int = 64, d_I: int = 128,
+              k: int = 2048) -> Workload:
+    """One layer of a native DSA indexer, the comparator of the pages' Table 4:
+    the layer's own key cache of d_I fp8 values and one fp32 scale per token
+    (132 bytes at d_I = 128), queries [n_q, H, d_I] and head weights, no
+    shared latent.  Its keys are seeded draws of their own (1 % of tokens
+    planted x3); the queries score them directly (the absorbed-query slot
+    holds the raw query)."""
+    return make_decode(f"dsa-key-layer{layer}", 30 + layer, seed, G=1, H=H, r=d_I, d_I=d_I, k=k,
+                       B=None, cache_dtype="fp8", lens=list(lens), plant_frac=0.01,
+                       plant_factor=3.0, permute_blocks=True)
+
+
+def calibration_set(seed: int = 0, n: int = 4096, d_model: int = 96, m: int = 4, d_R: int = 16,
+                    d_N: int = 32, noise: float = 0.1):
+    """Synthetic calibration inputs for one group: anchor hidden states X
+    [n, d_model] (per-feature scales log-uniform in [0.3, 3]), and per layer
+    the draws of a native indexer's key projections W_R[l] [d_model, d_R] and
+    W_N[l] [d_model, d_N], each a shared part plus 0.3x a layer part over
+    sqrt(d_model) (the layers' keys are then X W, which the caller forms),
+    key-noise draws E[l] [n, d_R + d_N] scaled by `noise`, NoPE key offsets
+    [m, d_N], and the keys' rotary frequencies [d_R / 2] (10000^(-2j/d_R))."""
+    rng = _rng(seed, 70, 1)
+    X = rng.standard_normal((n, d_model), dtype=np.float32)
+    X *= np.exp(rng.uniform(np.log(0.3), np.log(3.0), d_model)).astype(np.float32)
+    inv = np.float32(1.0 / math.sqrt(d_model))
+    w0R = rng.standard_normal((d_model, d_R), dtype=np.float32)
+    w0N = rng.standard_normal((d_model, d_N), dtype=np.float32)
+    WR = np.stack([(w0R + np.float32(0.3) * rng.standard_normal((d_model, d_R), dtype=np.float32)) * inv
+                   for _ in range(m)])
+    WN = np.stack([(w0N + np.float32(0.3) * rng.standard_normal((d_model, d_N), dtype=np.float32)) * inv
+                   for _ in range(m)])
+    E = rng.standard_normal((m, n, d_R + d_N), dtype=np.float32) * np.float32(noise)
+    off = rng.standard_normal((m, d_N), dtype=np.float32)
+    theta = (10000.0 ** (-np.arange(d_R // 2) * 2.0 / d_R)).astype(np.float32)
+    return X, WR, WN, E, off, theta
+
+
 def make_prefill(seed: int = 0, n_q: int = 2048, L: int = 65536, H: int = 64, r: int = 256,
                  d_I: int = 128, k: int = 2048, G: int = 4, cfg_id: int = 4) -> Workload:
     lens = np.array([L], dtype=np.int64)

@@ -481,3 +481,100 @@ def test_two_scale_record_reproduces_the_storage_accounting():
     # one scale per token would be 196 bytes: not the pages' figure
     c1, s1 = O.quantize_fp8(rng.standard_normal((5, 192)).astype(np.float32))
     assert c1[0].nbytes + s1[:1].nbytes == 196
+
+
+# ------------------------------------------------- training-free calibration --
+
+def test_ridge_rrr_reduces_to_least_squares_and_ridge():
+    """Full rank: lam = 0 is ordinary least squares (numpy.linalg.lstsq);
+    lam > 0 is the ridge fit, i.e. least squares on the augmented system
+    [X; sqrt(lam) I] B = [Y; 0]."""
+    rng = np.random.default_rng(40)
+    X = rng.standard_normal((80, 7))
+    Y = rng.standard_normal((80, 5))
+    P, D = O.ridge_rrr(X, Y, 5, 0.0)
+    assert np.allclose(P @ D.T, np.linalg.lstsq(X, Y, rcond=None)[0], atol=1e-10)
+    lam = 3.0
+    P, D = O.ridge_rrr(X, Y, 5, lam)
+    Xa = np.concatenate([X, np.sqrt(lam) * np.eye(7)])
+    Ya = np.concatenate([Y, np.zeros((7, 5))])
+    assert np.allclose(P @ D.T, np.linalg.lstsq(Xa, Ya, rcond=None)[0], atol=1e-10)
+
+
+def test_ridge_rrr_rank_constraint_is_the_truncated_svd_fit():
+    """lam = 0, rank r: the fitted values are the best rank-r approximation
+    (Eckart-Young) of the least-squares fitted values; the residual grows as
+    the rank shrinks; exactly rank-r data is fitted exactly."""
+    rng = np.random.default_rng(41)
+    X = rng.standard_normal((100, 9))
+    Y = X @ rng.standard_normal((9, 6)) + 0.5 * rng.standard_normal((100, 6))
+    B_ols = np.linalg.lstsq(X, Y, rcond=None)[0]
+    U, S, Vh = np.linalg.svd(X @ B_ols, full_matrices=False)
+    errs = []
+    for r in range(1, 7):
+        P, D = O.ridge_rrr(X, Y, r, 0.0)
+        fit = X @ P @ D.T
+        assert np.allclose(fit, (U[:, :r] * S[:r]) @ Vh[:r], atol=1e-9), r
+        errs.append(np.linalg.norm(Y - fit))
+    assert all(a >= b - 1e-12 for a, b in zip(errs, errs[1:]))
+    Y2 = X @ rng.standard_normal((9, 2)) @ rng.standard_normal((2, 6))
+    P, D = O.ridge_rrr(X, Y2, 2, 0.0)
+    assert np.allclose(X @ P @ D.T, Y2, atol=1e-9)
+
+
+def test_calibrate_nope_recovers_an_exact_group_model():
+    """Keys generated by a shared projection, per-layer decoders and biases
+    (eq. 3) are reconstructed exactly at that rank; scoring the calibrated
+    latent through absorbed queries (eqs. 6-8) equals scoring the original
+    keys."""
+    rng = np.random.default_rng(42)
+    n, d, r, dn, m, H = 400, 24, 6, 10, 4, 3
+    X = rng.standard_normal((n, d))
+    P0 = rng.standard_normal((d, r))
+    Ds = [rng.standard_normal((dn, r)) for _ in range(m)]
+    bs = [rng.standard_normal(dn) for _ in range(m)]
+    keys = [X @ P0 @ D.T + b for D, b in zip(Ds, bs)]
+    P, Dc, bc = O.calibrate_nope(X, keys, r, 0.0)
+    C = X @ P                                     # the calibrated latent
+    for l in range(m):
+        assert np.allclose(C @ Dc[l].T + bc[l], keys[l], atol=1e-8), l
+        q = rng.standard_normal((H, dn))
+        w = rng.standard_normal(H)
+        u_keys = np.maximum(keys[l] @ q.T, 0.0) @ w
+        qt, beta = O.absorb(q, Dc[l].T, bc[l], 0)
+        assert np.allclose(O.absorbed_scores(C, qt, beta, w), u_keys, atol=1e-7), l
+
+
+def test_calibrate_rope_commutes_with_rotation_and_recovers_keys():
+    """RoPE branch: the decoders are complex scalars per frequency, so they
+    commute with rotation (eq. 4: R_t D = D Q_t with the latent's pairs
+    rotating at their frequency); keys generated by such a model are
+    reconstructed exactly, and scoring the rotated latent equals scoring the
+    rotated keys."""
+    rng = np.random.default_rng(43)
+    n, d, nf, m, a = 300, 20, 4, 3, 1
+    X = rng.standard_normal((n, d))
+    theta = np.array([1.0, 0.3, 0.05, 0.007])
+    pz = rng.standard_normal((d, nf)) + 1j * rng.standard_normal((d, nf))
+    coef = rng.standard_normal((m, nf)) + 1j * rng.standard_normal((m, nf))
+    keys = []
+    for l in range(m):
+        kc = (X @ pz) * coef[l]                   # [n, nf] complex pairs before rotation
+        K = np.empty((n, 2 * nf))
+        K[:, 0::2], K[:, 1::2] = kc.real, kc.imag
+        keys.append(K)
+    P_R, D_R = O.calibrate_rope(X, keys, a, 0.0)
+    Z = X @ P_R                                   # un-rotated latent R branch
+    for l in range(m):
+        assert np.allclose(Z @ D_R[l].T, keys[l], atol=1e-8), l
+    pos = rng.integers(0, 100000, n)
+    lat_theta = np.repeat(theta, a)               # each latent pair at its key pair's frequency
+    Zrot = O.rope_rotate(Z, pos, lat_theta)
+    for l in range(m):
+        Krot = O.rope_rotate(keys[l], pos, theta)
+        assert np.allclose(Zrot @ D_R[l].T, Krot, atol=1e-7), l   # R_t D z = D Q_t z
+        # and the decoder carries no cross-frequency term
+        for j in range(nf):
+            for q in range(nf * a):
+                if q // a != j:
+                    assert np.all(D_R[l][2 * j:2 * j + 2, 2 * q:2 * q + 2] == 0)
