@@ -74,9 +74,10 @@ typedef enum li_dtype {
  *   r           latent width d_C; a multiple of 16, at most 1024.
  *   scale_block FP8: 0 (one scale per token, n_scales = 1) or 128 (one scale
  *               per 128-value block, n_scales = ceil(r / 128): with r = 192,
- *               a 200-byte token record of 192 codes and two fp32 scales, the
- *               "200-byte latent including FP8 scales" of the LatentIndex
- *               explainer's storage paragraph).  Must be 0 for other types.
+ *               a 200-byte token record of 192 codes and two fp32 scales: the
+ *               200-byte per-token latent, scales included, that the
+ *               LatentIndex explainer's storage paragraph counts).  Must be 0
+ *               for other types.
  */
 typedef struct li_cache {
   void *data;
