@@ -40,6 +40,7 @@ import numpy as np
 
 HBM_PEAK = 8.0e12  # B/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15  # flop/s, MI355X dense bf16 matrix cores
+MFMA_FP32_PEAK = 157.3e12  # flop/s, MI355X dense fp32 matrix cores
 
 
 def parse():
@@ -434,6 +435,51 @@ def budget_sweep(torch, W, DeviceWorkload, Bs, r=192, dtype="fp8", sb=128, K=20)
                         f"3 followers rescore B candidates)", "points": rows}
 
 
+def calibration_leg(torch, n=16384, d=7168, m=4, d_R=64, d_N=64, reps=3):
+    """The calibration's normal equations at DeepSeek-V3.2's hidden size: one
+    li_calib_gram over n bf16 hidden-state rows X [n, d] and the group's keys
+    Y [n, m (d_R + d_N)] (random draws: timing only), against the dense fp32
+    matrix-core peak (the kernel multiplies on v_mfma_f32_16x16x4f32).
+    Algorithmic flop: 2 n per distinct output, i.e. n d (d + 1) for the
+    symmetric X^T X plus 2 n d e for X^T Y.  Then the host's closed form
+    (float64) from those normal equations, timed apart."""
+    from sparse_attention_indexer_latent_amd import calibrate, ops
+    e = m * (d_R + d_N)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    X = torch.randn((n, d), generator=g, device="cuda").to(torch.bfloat16)
+    Y = torch.randn((n, e), generator=g, device="cuda").to(torch.bfloat16)
+    G = torch.empty((d, d), dtype=torch.float32, device="cuda")
+    H = torch.empty((d, e), dtype=torch.float32, device="cuda")
+    xs = torch.empty(d, dtype=torch.float32, device="cuda")
+    ys = torch.empty(e, dtype=torch.float32, device="cuda")
+    ops.calib_gram(X, Y, G, H, xs, ys)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        ops.calib_gram(X, Y, G, H, xs, ys)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flop = n * d * (d + 1) + 2 * n * d * e
+    ne = (G.double().cpu().numpy(), H.double().cpu().numpy(), xs.double().cpu().numpy(),
+          ys.double().cpu().numpy(), n)
+    del X, Y, G, H
+    torch.cuda.empty_cache()
+    theta = 10000.0 ** (-np.arange(d_R // 2) * 2.0 / d_R)
+    t0 = time.perf_counter()
+    cal = calibrate.fit_from_normal_equations(ne, m, d_R, theta, 128, 1, 1.0)
+    host_s = time.perf_counter() - t0
+    return {"workload": f"calibration normal equations: n={n} bf16 rows, d_model={d}, "
+                        f"{m} layers x (d_R={d_R} + d_N={d_N}) keys; closed form r = "
+                        f"{cal.P.shape[1]} (r_R={cal.r_R}, r_N=128), lam=1",
+            "gram_ms": ms, "roofline": {"bound": "mfma", "achieved": flop / (ms * 1e-3) / 1e12,
+                                        "peak": MFMA_FP32_PEAK / 1e12, "unit": "TFLOP/s",
+                                        "frac": flop / (ms * 1e-3) / MFMA_FP32_PEAK,
+                                        "flop_per_launch": flop},
+            "host_closed_form_s": host_s}
+
+
 def batch1_128k(W):
     """The 128K batch-1 group: the batch-4 workload's generator for one
     sequence."""
@@ -626,6 +672,8 @@ def main():
 
     if not args.no_prefill:
         out["prefill"] = prefill_leg(torch, ops, W, DeviceWorkload, args.prefill_iters)
+    if not args.no_legs and not args.no_extra:
+        out["calibration"] = calibration_leg(torch)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -9,7 +9,8 @@ and RoPE branches separately, each in closed form:
   * the O(n d^2) normal equations over the calibration tokens (X^T X, X^T Y,
     column sums) run on the GPU matrix cores (li_calib_gram);
   * the closed-form solves on those small matrices run in float64 on the
-    host: (G + lam I) B = H by Cholesky, then the rank constraint keeps the
+    host: (G + lam I) B = H by Cholesky (one factor per branch, shared by
+    every rotary frequency), then the rank constraint keeps the
     top eigenvectors V of B^* H (= the augmented fit's Gram [X B;
     sqrt(lam) B]^* [X B; sqrt(lam) B]), P = B V and D = conj(V) (Mukherjee
     and Zhu, "Reduced rank ridge regression", 2011).
@@ -34,6 +35,7 @@ from typing import Sequence
 
 import numpy as np
 import torch
+from scipy.linalg import cho_factor, cho_solve
 
 from . import ops
 
@@ -54,12 +56,13 @@ def _top_eigvecs(M: np.ndarray, k: int) -> np.ndarray:
     return V[:, np.argsort(w)[::-1][:k]]
 
 
-def _ridge_rank_solve(G: np.ndarray, H: np.ndarray, rank: int, lam: float):
-    """(P, D) with P D^T the rank-`rank` ridge fit from the normal equations
-    G = X^T X and H = X^T Y (Y real or complex)."""
-    L = np.linalg.cholesky(G + lam * np.eye(G.shape[0]))
-    B = np.linalg.solve(L.T, np.linalg.solve(L, H)) if not np.iscomplexobj(H) else \
-        np.linalg.solve(L.T, np.linalg.solve(L, H.real)) + 1j * np.linalg.solve(L.T, np.linalg.solve(L, H.imag))
+def _ridge_rank_solve(cf, H: np.ndarray, rank: int):
+    """(P, D) with P D^T the rank-`rank` ridge fit from the Cholesky factor
+    cf of G + lam I (G = X^T X) and H = X^T Y (Y real or complex)."""
+    if np.iscomplexobj(H):
+        B = cho_solve(cf, H.real) + 1j * cho_solve(cf, H.imag)
+    else:
+        B = cho_solve(cf, H)
     V = _top_eigvecs(B.conj().T @ H, rank)
     return B @ V, V.conj()
 
@@ -88,16 +91,24 @@ def fit_group(X: torch.Tensor, rope_keys: Sequence[torch.Tensor], nope_keys: Seq
     """X: device [n, d_model] anchor hidden states; rope_keys[l] device
     [n, d_R] (before rotation, pair (2j, 2j+1) at frequency key_theta[j]) and
     nope_keys[l] device [n, d_N] of each layer of the group."""
-    m = len(nope_keys)
     d_R = rope_keys[0].shape[1] if rope_keys else 0
-    d_N = nope_keys[0].shape[1]
-    G, H, xs, ys, n = normal_equations(X, list(rope_keys) + list(nope_keys))
+    ne = normal_equations(X, list(rope_keys) + list(nope_keys))
+    return fit_from_normal_equations(ne, len(nope_keys), d_R, key_theta, r_N, pairs_per_freq, lam)
+
+
+def fit_from_normal_equations(ne, m: int, d_R: int, key_theta: np.ndarray, r_N: int,
+                              pairs_per_freq: int, lam: float) -> GroupCalibration:
+    """The closed form from (X^T X, X^T Y, x_sum, y_sum, n) of normal_equations,
+    Y = [rope keys of layers 0..m-1 | nope keys of layers 0..m-1]."""
+    G, H, xs, ys, n = ne
     d = G.shape[0]
+    d_N = (H.shape[1] - m * d_R) // m
     xm, ym = xs / n, ys / n
     # NoPE: centred regression of every layer's NoPE keys together
     HN = H[:, m * d_R:] - n * np.outer(xm, ym[m * d_R:])
     GN = G - n * np.outer(xm, xm)
-    P_N, D_N = _ridge_rank_solve(GN, HN, r_N, lam)
+    eye = lam * np.eye(d)
+    P_N, D_N = _ridge_rank_solve(cho_factor(GN + eye), HN, r_N)
     b_all = ym[m * d_R:] - D_N @ (P_N.T @ xm)
     # RoPE: per frequency, a complex regression of the layers' pairs
     nf = d_R // 2
@@ -105,10 +116,11 @@ def fit_group(X: torch.Tensor, rope_keys: Sequence[torch.Tensor], nope_keys: Seq
     r_R = 2 * nf * a
     P_R = np.zeros((d, r_R))
     D_R = np.zeros((m, d_R, r_R))
+    cf = cho_factor(G + eye) if nf else None   # one factor serves every frequency
     for j in range(nf):
         cols_re = [l * d_R + 2 * j for l in range(m)]
         Hf = H[:, cols_re] + 1j * H[:, [c + 1 for c in cols_re]]
-        Pf, Df = _ridge_rank_solve(G, Hf, a, lam)
+        Pf, Df = _ridge_rank_solve(cf, Hf, a)
         for i in range(a):
             q = j * a + i
             P_R[:, 2 * q], P_R[:, 2 * q + 1] = Pf[:, i].real, Pf[:, i].imag

@@ -29,12 +29,16 @@ __device__ __forceinline__ float ld1(const void *p, int64_t off) {
   else return ((const float *)p)[off];
 }
 
-template <bool ABF, bool BBF>
+// SYM (A == B, C = A^T A): only blocks on or above the diagonal run; an
+// off-diagonal block also writes its transpose, so every element of C is
+// still owned by exactly one workgroup.
+template <bool ABF, bool BBF, bool SYM>
 __global__ void __launch_bounds__(256)
 gram_kernel(const void *__restrict__ A, int64_t n, int da, const void *__restrict__ B, int db,
             float *__restrict__ C, int64_t ldc, int accumulate) {
   __shared__ float As[kKS][kBT + kPadC];
   __shared__ float Bs[kKS][kBT + kPadC];
+  if (SYM && blockIdx.y > blockIdx.x) return;  // uniform
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int i0 = blockIdx.y * kBT, j0 = blockIdx.x * kBT;
   const int wi = wave >> 1, wj = wave & 1;
@@ -81,6 +85,10 @@ gram_kernel(const void *__restrict__ A, int64_t n, int da, const void *__restric
         if (i < da && j < db) {
           float *o = C + (int64_t)i * ldc + j;
           *o = (accumulate ? *o : 0.f) + acc[a][b][v];
+          if (SYM && i0 != j0) {  // the mirrored element, below the diagonal
+            float *t = C + (int64_t)j * ldc + i;
+            *t = (accumulate ? *t : 0.f) + acc[a][b][v];
+          }
         }
       }
 }
@@ -95,11 +103,11 @@ colsum_kernel(const void *__restrict__ A, int64_t n, int da, float *__restrict__
   s[j] = (accumulate ? s[j] : 0.f) + acc;
 }
 
-template <bool ABF, bool BBF>
+template <bool ABF, bool BBF, bool SYM = false>
 hipError_t gram(const void *A, int64_t n, int da, const void *B, int db, float *C, int accumulate,
                 hipStream_t st) {
   dim3 grid((db + kBT - 1) / kBT, (da + kBT - 1) / kBT);
-  gram_kernel<ABF, BBF><<<grid, 256, 0, st>>>(A, n, da, B, db, C, db, accumulate);
+  gram_kernel<ABF, BBF, SYM><<<grid, 256, 0, st>>>(A, n, da, B, db, C, db, accumulate);
   return hipGetLastError();
 }
 
@@ -108,8 +116,8 @@ hipError_t gram(const void *A, int64_t n, int da, const void *B, int db, float *
 hipError_t launch_calib_gram(const void *X, int x_bf16, int64_t n, int d, const void *Y,
                              int y_bf16, int e, float *G_xx, float *G_xy, float *x_sum,
                              float *y_sum, int accumulate, hipStream_t st) {
-  hipError_t err = x_bf16 ? gram<true, true>(X, n, d, X, d, G_xx, accumulate, st)
-                          : gram<false, false>(X, n, d, X, d, G_xx, accumulate, st);
+  hipError_t err = x_bf16 ? gram<true, true, true>(X, n, d, X, d, G_xx, accumulate, st)
+                          : gram<false, false, true>(X, n, d, X, d, G_xx, accumulate, st);
   if (err != hipSuccess) return err;
   if (Y && G_xy) {
     if (x_bf16)

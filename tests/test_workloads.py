@@ -54,3 +54,33 @@ def test_latent_stream_independent_of_other_sequences():
     wl = W.small_decode(3, n_seq=3)
     one = W.small_decode(3, n_seq=3)
     assert np.array_equal(wl.latent(2), one.latent(2))
+
+
+def test_calibration_host_solve_matches_oracle(monkeypatch):
+    """The host half of the calibration (closed form from the normal
+    equations) against the oracle's regression on the raw data, with the
+    normal equations formed in float64 on the CPU in place of the GPU Gram."""
+    import torch
+    from oracle import oracle as O
+    from sparse_attention_indexer_latent_amd import calibrate
+
+    def cpu_normal_equations(X, keys, batch=1 << 16):
+        Xn = X.double().numpy()
+        Y = np.concatenate([k.double().numpy() for k in keys], axis=1)
+        return Xn.T @ Xn, Xn.T @ Y, Xn.sum(0), Y.sum(0), Xn.shape[0]
+
+    monkeypatch.setattr(calibrate, "normal_equations", cpu_normal_equations)
+    X, WR, WN, E, off, theta = W.calibration_set(2, n=2000, d_model=40, m=3, d_R=8, d_N=12)
+    R = [X.astype(np.float64) @ WR[l] + E[l][:, :8] for l in range(3)]
+    N = [X.astype(np.float64) @ WN[l] + E[l][:, 8:] + off[l] for l in range(3)]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))  # noqa: E731
+    cal = calibrate.fit_group(t(X), [t(k) for k in R], [t(k) for k in N], theta, 6, 2, 0.3)
+    P_N, D_N, b_N = O.calibrate_nope(X, N, 6, 0.3)
+    P_R, D_R = O.calibrate_rope(X, R, 2, 0.3)
+    assert cal.r_R == 16 and cal.P.shape == (40, 22) and cal.Dt.shape == (3, 22, 20)
+    for l in range(3):
+        assert np.allclose(cal.P[:, 16:] @ cal.Dt[l, 16:, 8:], P_N @ D_N[l].T, atol=1e-9)
+        assert np.allclose(cal.P[:, :16] @ cal.Dt[l, :16, :8], P_R @ D_R[l].T, atol=1e-9)
+        assert np.allclose(cal.b[l], b_N[l], atol=1e-9)
+        assert np.all(cal.Dt[l, :16, 8:] == 0) and np.all(cal.Dt[l, 16:, :8] == 0)
+    assert np.allclose(cal.rope_theta, np.repeat(theta, 2))
