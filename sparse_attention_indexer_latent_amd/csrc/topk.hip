@@ -381,19 +381,31 @@ __device__ uint32_t nt_find(const uint32_t *hist, int nb, uint32_t nd, uint32_t 
 // the lane holding the nd-th largest key, then every lane takes one of that
 // lane's bins and a second prefix sum picks the bin.  nd must be at least 1
 // and at most the histogram total.
-__device__ uint32_t wave_find(const uint32_t *hist, int nb, uint32_t nd, uint32_t *above,
-                              uint32_t *count) {
+template <int NB>
+__device__ __forceinline__ uint32_t wave_find_nb(const uint32_t *hist, int nb_rt, uint32_t nd,
+                                                 uint32_t *above, uint32_t *count) {
+  const int nb = NB ? NB : nb_rt;
   const int lane = threadIdx.x % kWave;
   const int per = nb / kWave;
   const int top = nb - 1 - lane * per;
   uint32_t sum = 0;
   {
-    // 16 bytes at a time, chunk order rotated by lane (bank spread)
+    // 16 bytes at a time, chunk order rotated by lane (bank spread); with a
+    // compile-time size every read is issued before the first is summed
     const uint4 *h4 = (const uint4 *)(hist + top - per + 1);
     const int nc = per / 4;
-    for (int e = 0; e < nc; ++e) {
-      const uint4 v = h4[(e + lane) & (nc - 1)];
-      sum += (v.x + v.y) + (v.z + v.w);
+    if constexpr (NB != 0) {
+      constexpr int NC = NB / kWave / 4;
+      uint4 v[NC];
+#pragma unroll
+      for (int e = 0; e < NC; ++e) v[e] = h4[(e + lane) & (NC - 1)];
+#pragma unroll
+      for (int e = 0; e < NC; ++e) sum += (v[e].x + v[e].y) + (v[e].z + v[e].w);
+    } else {
+      for (int e = 0; e < nc; ++e) {
+        const uint4 v = h4[(e + lane) & (nc - 1)];
+        sum += (v.x + v.y) + (v.z + v.w);
+      }
     }
   }
   const uint32_t incl = wave_incl_scan(sum), excl = incl - sum;
@@ -408,6 +420,13 @@ __device__ uint32_t wave_find(const uint32_t *hist, int nb, uint32_t nd, uint32_
   *above = __shfl(ex2, t, kWave);
   *count = __shfl(v, t, kWave);
   return (uint32_t)(topL - t);
+}
+
+__device__ uint32_t wave_find(const uint32_t *hist, int nb, uint32_t nd, uint32_t *above,
+                              uint32_t *count) {
+  if (nb == 4096) return wave_find_nb<4096>(hist, nb, nd, above, count);
+  if (nb == 1024) return wave_find_nb<1024>(hist, nb, nd, above, count);
+  return wave_find_nb<0>(hist, nb, nd, above, count);
 }
 
 // Sum over the wavefront, in every lane (DPP scan, then lane 63's total).
@@ -766,15 +785,26 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
 #pragma unroll
   for (int e = 0; e < 2 * 1024 / kSelThreads; ++e) (&sh.h10[0][0])[e * kSelThreads + tid] = b[e];
   // offsets of the segments' lists in the row's flattened extracted keys
-  uint32_t carry = 0;
-  for (int b0 = 0; b0 < S; b0 += kSelThreads) {
-    const uint32_t c = (b0 + tid < S) ? (b0 == 0 ? c_first : cnt[b0 + tid]) : 0u;
-    uint32_t tot;
-    const uint32_t ex = nt_scan<kSelThreads>(c, sh.wt, &tot);
-    if (b0 + tid < S) sh.seg_off[b0 + tid] = carry + ex;
-    carry += tot;
+  // (rows of up to 64 segments: one wavefront's prefix sum, no barrier; the
+  // barrier below publishes it)
+  if (S <= kWave) {
+    if (wave == 0) {
+      const uint32_t c = lane < S ? c_first : 0u;
+      const uint32_t incl = wave_incl_scan(c);
+      if (lane < S) sh.seg_off[lane] = incl - c;
+      if (lane == S - 1) sh.seg_off[S] = incl;
+    }
+  } else {
+    uint32_t carry = 0;
+    for (int b0 = 0; b0 < S; b0 += kSelThreads) {
+      const uint32_t c = (b0 + tid < S) ? (b0 == 0 ? c_first : cnt[b0 + tid]) : 0u;
+      uint32_t tot;
+      const uint32_t ex = nt_scan<kSelThreads>(c, sh.wt, &tot);
+      if (b0 + tid < S) sh.seg_off[b0 + tid] = carry + ex;
+      carry += tot;
+    }
+    if (tid == 0) sh.seg_off[S] = carry;
   }
-  if (tid == 0) sh.seg_off[S] = carry;
   for (int b0 = tid; b0 < 2 * 1024; b0 += kSelThreads) {
     (&sh.hlow[0][0])[b0] = 0;
     (&sh.hbef[0][0])[b0] = 0;
@@ -873,8 +903,13 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
     uint32_t above, c;
     const uint32_t d = wave_find(sh.hlow[j], 1024, need_w, &above, &c);
     uint32_t gl = 0;  // keys of the 22-bit prefix above theta, before this segment
-    for (int b0 = lane; b0 < 1024; b0 += kWave)
-      if ((uint32_t)b0 > d) gl += sh.hbef[j][b0];
+    {
+      uint32_t hb[1024 / kWave];  // every read issued before the first is used
+#pragma unroll
+      for (int i = 0; i < 1024 / kWave; ++i) hb[i] = sh.hbef[j][lane + i * kWave];
+#pragma unroll
+      for (int i = 0; i < 1024 / kWave; ++i) gl += (uint32_t)(lane + i * kWave) > d ? hb[i] : 0u;
+    }
     gl = wave_sum_u32(gl);
     if (lane == 0) {
       const uint32_t ne = need_w - above, eb = sh.hbef[j][d];
