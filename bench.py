@@ -59,7 +59,8 @@ def parse():
                          "three times (calibrates hardware byte counters)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk leg")
     ap.add_argument("--prefill-iters", type=int, default=10)
-    ap.add_argument("--path", choices=["hs", "full", "b1", "c1", "c2", "prefill"], default="hs",
+    ap.add_argument("--path", choices=["hs", "full", "b1", "c1", "c2", "prefill", "calib"],
+                    default="hs",
                     help="with --profile-steps: which step to run (hs / full: the 4 x 128K HS or "
                          "full-scan step; b1: the 128K batch-1 full-scan step; c1: 32K batch 1; "
                          "c2: 16 ragged fp8 sequences; prefill: the prefill chunk)")
@@ -505,6 +506,9 @@ def main():
     torch.cuda.set_device(0)
     if ops.lib().li_check_device() != ops.LI_OK:
         raise SystemExit(ops.lib().li_last_error().decode())
+    if args.path == "calib":  # the calibration's normal equations alone (for profiling)
+        print(json.dumps(calibration_leg(torch)), flush=True)
+        return
     if args.profile_steps and args.path == "prefill":
         pf = prefill_setup(torch, W, DeviceWorkload)
         for _ in range(args.warmup + args.profile_steps):

@@ -18,14 +18,18 @@ from parity_util import RTOL_FP32, assert_scores_close, say
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("shape", [(1000, 533, 70, 33), (777, 300, 256, 192)],
+                         ids=["ragged", "vector-rows"])
 @pytest.mark.parametrize("bf16", [False, True])
-def test_calib_gram_against_float64(bf16):
-    """Two batches accumulated (ragged sizes, not multiples of the 64 x 64
-    blocks or the 32-row slabs) against the float64 products of the same
-    values; fp32 sums of exact products: relative error ~ n 2^-24."""
-    say(f"calib gram bf16={bf16}")
+def test_calib_gram_against_float64(bf16, shape):
+    """Two batches accumulated against the float64 products of the same
+    values: ragged sizes (not multiples of the 128 x 128 blocks, the 16-row
+    slabs or a 16-byte row), and rows that take the vector loads with partial
+    slabs and several blocks on and off the diagonal; fp32 sums of exact
+    products: relative error ~ n 2^-24."""
+    n1, n2, d, e = shape
+    say(f"calib gram bf16={bf16} n={n1}+{n2} d={d} e={e}")
     rng = np.random.default_rng(50)
-    n1, n2, d, e = 1000, 533, 70, 33
     X = rng.standard_normal((n1 + n2, d)).astype(np.float32) * 3
     Y = rng.standard_normal((n1 + n2, e)).astype(np.float32)
     dt = torch.bfloat16 if bf16 else torch.float32
@@ -108,3 +112,28 @@ def test_calibrated_group_scores_through_the_library():
                       torch.full((1,), L, dtype=torch.int32, device="cuda"), L, cache)
         o = O.layer_scores(C, q[l, 0], Dt32[l], b32[l], cal.nope_off, w[l, 0])
         assert_scores_close(u[0, :L].cpu().numpy(), o, RTOL_FP32, f"calibrated layer {l}")
+
+
+def test_calib_gram_sums_without_cross_products():
+    """Through the C ABI: y_sum requested with G_xy NULL, and n = 0 (zeros
+    written), against float64."""
+    say("calib gram: y_sum without G_xy, n = 0")
+    rng = np.random.default_rng(52)
+    X = torch.from_numpy(rng.standard_normal((300, 40)).astype(np.float32)).cuda()
+    Y = torch.from_numpy(rng.standard_normal((300, 130)).astype(np.float32)).cuda()
+    G = torch.full((40, 40), 7.0, device="cuda")
+    xs = torch.full((40,), 7.0, device="cuda")
+    ys = torch.full((130,), 7.0, device="cuda")
+    lib = ops.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    assert lib.li_calib_gram(X.data_ptr(), ops.LI_FP32, 300, 40, Y.data_ptr(), ops.LI_FP32, 130,
+                             G.data_ptr(), None, xs.data_ptr(), ys.data_ptr(), 0, st) == ops.LI_OK
+    torch.cuda.synchronize()
+    Xe, Ye = X.double().cpu().numpy(), Y.double().cpu().numpy()
+    assert np.allclose(ys.double().cpu().numpy(), Ye.sum(0), rtol=1e-5, atol=1e-4)
+    assert np.allclose(xs.double().cpu().numpy(), Xe.sum(0), rtol=1e-5, atol=1e-4)
+    assert np.allclose(G.double().cpu().numpy(), Xe.T @ Xe, rtol=1e-5, atol=1e-3)
+    assert lib.li_calib_gram(X.data_ptr(), ops.LI_FP32, 0, 40, Y.data_ptr(), ops.LI_FP32, 130,
+                             G.data_ptr(), None, xs.data_ptr(), ys.data_ptr(), 0, st) == ops.LI_OK
+    torch.cuda.synchronize()
+    assert torch.all(G == 0) and torch.all(xs == 0) and torch.all(ys == 0)
