@@ -31,9 +31,9 @@ Readings taken where the configuration text is terse:
     are multiplied by the planting factor before any quantisation.
   * Ragged lengths are round(exp(U[ln 8192, ln 131072])).
   * The prefill chunk's absorbed queries are drawn directly on the bf16 grid
-    (an N(0, d_I*(1+0.3^2)/r) draw with the low 16 bits of the fp32 pattern
-    cleared), which matches the variance of Dt_l @ q without this module
-    doing the absorption itself.
+    (an N(0, d_I*(1+0.3^2)/r) fp32 draw rounded to bf16, nearest-even), which
+    matches the variance of Dt_l @ q without this module doing the absorption
+    itself.
   * The decode step appends the last token of each sequence: the cache holds
     positions 0..L-2 before the step and 0..L-1 after it; layer queries score
     all L positions (causal set inclusive of the current token).
@@ -114,7 +114,8 @@ class Workload:
         std = math.sqrt(self.d_I * (1.0 + 0.3 ** 2) / self.r)
         qt = rng.standard_normal((self.n_q, self.H, self.r), dtype=np.float32)
         qt *= np.float32(std)
-        bits = (qt.view(np.uint32) >> 16).astype(np.uint16)
+        u = qt.view(np.uint32).astype(np.uint64)
+        bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)  # nearest, ties to even
         w = rng.standard_normal((self.n_q, self.H), dtype=np.float32)
         w *= np.float32(1.0 / math.sqrt(self.H))
         return bits, w
