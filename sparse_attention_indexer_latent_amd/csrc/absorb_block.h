@@ -63,7 +63,11 @@ __device__ __forceinline__ void absorb_block(const void *__restrict__ q, int n_q
   // out-of-range rows read a valid row and are zeroed, so loads need no branches
   const int64_t qo = qrow(a_ok ? slot : 0);
   const float *dr = D + (int64_t)(b_ok ? j : 0) * d_I;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // four independent accumulation chains (one per float4 lane), summed in a
+  // fixed order at the end, so consecutive matrix-core ops do not wait on
+  // each other
+  f32x4 acc4[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
+                   {0.f, 0.f, 0.f, 0.f}};
   for (int d0 = 0; d0 < d_I; d0 += kKC) {
     float4 av[8], bv[8];
 #pragma unroll
@@ -77,12 +81,13 @@ __device__ __forceinline__ void absorb_block(const void *__restrict__ q, int n_q
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].x, bv[c].x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].y, bv[c].y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].z, bv[c].z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].w, bv[c].w, acc, 0, 0, 0);
+      acc4[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].x, bv[c].x, acc4[0], 0, 0, 0);
+      acc4[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].y, bv[c].y, acc4[1], 0, 0, 0);
+      acc4[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].z, bv[c].z, acc4[2], 0, 0, 0);
+      acc4[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].w, bv[c].w, acc4[3], 0, 0, 0);
     }
   }
+  const f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
   // acc[v] = D[4 g + v][i] of the tile
   const int jo = bx * kT + 16 * tj + i;
   if (jo < r) {
