@@ -71,7 +71,9 @@ def normal_equations(X: torch.Tensor, keys: Sequence[torch.Tensor], batch: int =
     """Accumulate X^T X, X^T Y and the column sums on the GPU over batches of
     rows (Y = the key blocks side by side).  Returns float64 host arrays."""
     n, d = X.shape
-    Y = torch.cat([k.to(X.dtype) for k in keys], dim=1).contiguous()
+    # the keys keep their precision: bf16 only when every block is bf16
+    ydt = torch.bfloat16 if all(k.dtype == torch.bfloat16 for k in keys) else torch.float32
+    Y = torch.cat([k.to(ydt) for k in keys], dim=1).contiguous()
     e = Y.shape[1]
     dev = X.device
     G = torch.zeros((d, d), dtype=torch.float32, device=dev)
