@@ -399,14 +399,16 @@ def dsa_leg(torch, flush, W, DsaGroup, batch, K=20, Kc=6):
     return out
 
 
-def budget_sweep(torch, W, DeviceWorkload, Bs, r=192, dtype="fp8", sb=128, K=20):
+def budget_sweep(torch, W, DeviceWorkload, Bs, r=192, dtype="fp8", sb=128, K=20, layer_corr=0.0):
     """Candidate budget B against HS step time and the followers' recall of
     their own full-scan selections (|S_HS ∩ S_full| / k, mean over followers
     and queries) on the synthetic 128K batch-1 workload of the pages'
     geometry.  Synthetic decoders share a common part (D_l = (G0 + 0.3 G_l) /
-    sqrt(r)), so these recalls describe this generator, not a trained model."""
+    sqrt(r)); the layers' queries and head weights are independent, or
+    correlated at layer_corr.  These recalls describe the generator, not a
+    trained model."""
     from sparse_attention_indexer_latent_amd import ops
-    wl = W.hs_128k(1, r=r, cache_dtype=dtype, scale_block=sb, B=max(Bs))
+    wl = W.hs_128k(1, r=r, cache_dtype=dtype, scale_block=sb, B=max(Bs), layer_corr=layer_corr)
     dw = DeviceWorkload(wl, hold_last=True)
     dw.full_step()
     torch.cuda.synchronize()
@@ -662,6 +664,8 @@ def main():
                     "pages_table4_context": "2.30-2.72x (ms per decode token, all 61 indexers, "
                                             "batch 1, eight unnamed GPUs)"}
             out["b_sweep"] = budget_sweep(torch, W, DeviceWorkload, [2048, 4096, 8192, 16384, 32768])
+            out["b_sweep_correlated_layers"] = budget_sweep(
+                torch, W, DeviceWorkload, [2048, 4096, 8192, 16384, 32768], layer_corr=0.9)
             wl8 = W.hs_128k(1, G=8, name="hs-128k-b1-bf16-r256-G8")
             d8 = DeviceWorkload(wl8, hold_last=True)
             for hs_mode in (True, False):

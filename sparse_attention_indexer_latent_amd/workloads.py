@@ -30,6 +30,10 @@ Readings taken where the configuration text is terse:
   * Planted tokens are drawn uniformly without replacement; their latent rows
     are multiplied by the planting factor before any quantisation.
   * Ragged lengths are round(exp(U[ln 8192, ln 131072])).
+  * Queries q ~ N(0, 1) and head weights w ~ N(0, 1)/sqrt(H) per (layer,
+    query, head), independent across layers unless a layer correlation rho
+    is asked for: then each layer's draw is rho x a group-shared draw +
+    sqrt(1 - rho^2) x its own.
   * The prefill chunk's absorbed queries are drawn directly on the bf16 grid
     (an N(0, d_I*(1+0.3^2)/r) fp32 draw rounded to bf16, nearest-even), which
     matches the variance of Dt_l @ q without this module doing the absorption
@@ -171,19 +175,33 @@ def _decoders(seed, cfg_id, G, r, d_I):
     return Dt
 
 
-def _queries(seed, cfg_id, G, n_q, H, d_I):
+def _queries(seed, cfg_id, G, n_q, H, d_I, layer_corr=0.0):
+    """Per-layer queries and head weights; with layer_corr = rho > 0 every
+    layer's draw is rho x a draw shared by the group + sqrt(1 - rho^2) x its
+    own (same marginal distribution, correlation rho between layers)."""
     q = np.empty((G, n_q, H, d_I), dtype=np.float32)
     w = np.empty((G, n_q, H), dtype=np.float32)
+    sw = np.float32(1.0 / math.sqrt(H))
+    if layer_corr:
+        rng0 = _rng(seed, cfg_id, 3100)
+        q0 = rng0.standard_normal((n_q, H, d_I), dtype=np.float32)
+        w0 = rng0.standard_normal((n_q, H), dtype=np.float32)
+        a = np.float32(layer_corr)
+        c = np.float32(math.sqrt(1.0 - layer_corr ** 2))
     for l in range(G):
         rng = _rng(seed, cfg_id, 3000 + l)
         q[l] = rng.standard_normal((n_q, H, d_I), dtype=np.float32)
-        w[l] = rng.standard_normal((n_q, H), dtype=np.float32) * np.float32(1.0 / math.sqrt(H))
+        w[l] = rng.standard_normal((n_q, H), dtype=np.float32)
+        if layer_corr:
+            q[l] = a * q0 + c * q[l]
+            w[l] = a * w0 + c * w[l]
+        w[l] *= sw
     return q, w
 
 
 def make_decode(name, cfg_id, seed, *, G, H, r, d_I, k, B, cache_dtype, lens,
                 plant_frac=None, n_plant=None, plant_factor, permute_blocks,
-                nope_off=None, bias=False, scale_block=0) -> Workload:
+                nope_off=None, bias=False, scale_block=0, layer_corr=0.0) -> Workload:
     lens = np.asarray(lens, dtype=np.int64)
     n_seq = len(lens)
     planted = []
@@ -194,7 +212,7 @@ def make_decode(name, cfg_id, seed, *, G, H, r, d_I, k, B, cache_dtype, lens,
         planted.append(_planted_ids(seed, cfg_id, s, L, n, r))
     bt, nphys = _block_table(seed, cfg_id, lens, permute_blocks)
     Dt = _decoders(seed, cfg_id, G, r, d_I)
-    q, w = _queries(seed, cfg_id, G, n_seq, H, d_I)
+    q, w = _queries(seed, cfg_id, G, n_seq, H, d_I, layer_corr)
     no = d_I if nope_off is None else nope_off
     b = np.zeros((G, d_I - no), dtype=np.float32)
     if bias and d_I - no > 0:
@@ -248,17 +266,20 @@ def config(i: int, seed: int = 0) -> Workload:
 
 
 def hs_128k(batch: int, seed: int = 0, r: int = 256, cache_dtype: str = "bf16",
-            scale_block: int = 0, B: int = 8192, G: int = 4, name: str = None) -> Workload:
+            scale_block: int = 0, B: int = 8192, G: int = 4, name: str = None,
+            layer_corr: float = 0.0) -> Workload:
     """The 128K hierarchical-selection workload (the batch-4 configuration's
     generator) at any batch, latent width, cache type, candidate budget and
     group size.  r = 192 with an fp8 cache and scale_block = 128 is the
     DeepSeek-V3.2 geometry of the LatentIndex explainer's storage paragraph
     (192 values, a 200-byte record)."""
-    name = name or f"hs-128k-b{batch}-{cache_dtype}-r{r}" + (f"-sb{scale_block}" if scale_block
-                                                               else "")
+    name = name or (f"hs-128k-b{batch}-{cache_dtype}-r{r}" + (f"-sb{scale_block}" if scale_block
+                                                                else "")
+                    + (f"-rho{layer_corr:g}" if layer_corr else ""))
     return make_decode(name, 3 if r == 256 else 5, seed, G=G, H=64, r=r, d_I=128, k=2048, B=B,
                        cache_dtype=cache_dtype, lens=[131072] * batch, plant_frac=0.01,
-                       plant_factor=3.0, permute_blocks=True, scale_block=scale_block)
+                       plant_factor=3.0, permute_blocks=True, scale_block=scale_block,
+                       layer_corr=layer_corr)
 
 
 def dsa_layer(layer: int, lens, seed: int = 0, H: int = 64, d_I: int = 128,

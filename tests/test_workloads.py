@@ -84,3 +84,21 @@ def test_calibration_host_solve_matches_oracle(monkeypatch):
         assert np.allclose(cal.b[l], b_N[l], atol=1e-9)
         assert np.all(cal.Dt[l, :16, 8:] == 0) and np.all(cal.Dt[l, 16:, :8] == 0)
     assert np.allclose(cal.rope_theta, np.repeat(theta, 2))
+
+
+def test_layer_correlated_queries():
+    """rho = 0 leaves the independent draws unchanged; rho > 0 keeps each
+    layer's marginal variance and correlates layers at about rho."""
+    a = W.small_decode(5, n_seq=2, H=64, d_I=128, G=4)
+    b = W.make_decode("x", 90, 5, G=4, H=64, r=32, d_I=128, k=16, B=None, cache_dtype="fp32",
+                      lens=[100, 137], n_plant=0, plant_factor=4.0, permute_blocks=True)
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.w, b.w)
+    c = W.make_decode("x", 90, 5, G=4, H=64, r=32, d_I=128, k=16, B=None, cache_dtype="fp32",
+                      lens=[100, 137], n_plant=0, plant_factor=4.0, permute_blocks=True,
+                      layer_corr=0.9)
+    q = c.q.reshape(4, -1).astype(np.float64)
+    assert np.allclose(q.std(axis=1), 1.0, atol=0.02)
+    cc = np.corrcoef(q)
+    assert np.all(np.abs(cc[np.triu_indices(4, 1)] - 0.81) < 0.03)   # rho^2 between layers
+    w = c.w.reshape(4, -1).astype(np.float64)
+    assert np.allclose(w.std(axis=1), 1 / 8.0, rtol=0.3)   # 128 draws per layer
