@@ -48,7 +48,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--workload", default="hs-128k-b4",
+                    help="headline workload (a name from workloads.WORKLOADS)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-extra", action="store_true", help="skip the cold, legs and ceiling parts")
@@ -59,11 +60,12 @@ def parse():
                          "three times (calibrates hardware byte counters)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk leg")
     ap.add_argument("--prefill-iters", type=int, default=10)
-    ap.add_argument("--path", choices=["hs", "full", "b1", "c1", "c2", "prefill", "calib"],
+    ap.add_argument("--path", choices=["hs", "full", "b1", "dsv32-32k", "ragged-fp8", "prefill",
+                                       "calib"],
                     default="hs",
                     help="with --profile-steps: which step to run (hs / full: the 4 x 128K HS or "
-                         "full-scan step; b1: the 128K batch-1 full-scan step; c1: 32K batch 1; "
-                         "c2: 16 ragged fp8 sequences; prefill: the prefill chunk)")
+                         "full-scan step; b1: the 128K batch-1 full-scan step; dsv32-32k: 32K batch 1; "
+                         "ragged-fp8: 16 ragged fp8 sequences; prefill: the prefill chunk)")
     ap.add_argument("--no-legs", action="store_true", help="skip the legs beside the headline")
     ap.add_argument("--graphs", action="store_true",
                     help="replay the step as two HIP graphs around a direct scan launch instead of "
@@ -210,7 +212,7 @@ def cpu_baseline(wl, seconds: float):
 def prefill_setup(torch, W, DeviceWorkload):
     """Device operands of the prefill chunk: the 64K-token latent, every
     layer's bf16 absorbed queries and head weights, score and index buffers."""
-    wl = W.config(4)
+    wl = W.named("prefill-2048x64k")
     dw = DeviceWorkload(wl, hold_last=False)
     qts, ws = [], []
     for layer in range(wl.G):
@@ -517,14 +519,15 @@ def main():
             prefill_chunk(ops, *pf)
         torch.cuda.synchronize()
         return
-    if args.profile_steps and args.path in ("b1", "c1", "c2"):
-        wl = batch1_128k(W) if args.path == "b1" else W.config(int(args.path[1]))
+    if args.profile_steps and args.path in ("b1", "dsv32-32k", "ragged-fp8"):
+        wl = {"b1": batch1_128k(W), "dsv32-32k": W.named("dsv32-decode-32k"),
+              "ragged-fp8": W.named("ragged-16x8k-128k-fp8")}[args.path]
         dw = DeviceWorkload(wl, hold_last=True)
         for _ in range(args.warmup + args.profile_steps):
             dw.full_step()
         torch.cuda.synchronize()
         return
-    wl = W.config(args.config)
+    wl = W.named(args.workload)
     hs = wl.B is not None and args.path != "full"
     dw = DeviceWorkload(wl, hold_last=True)
     if args.graphs:
@@ -625,8 +628,8 @@ def main():
             del dw
             torch.cuda.empty_cache()
             for name, wlf, with_hs in (("128k_b1", batch1_128k(W), True),
-                                       ("cfg1_32k_b1_bf16", W.config(1), False),
-                                       ("cfg2_ragged16_fp8", W.config(2), False)):
+                                       ("32k_b1_bf16", W.named("dsv32-decode-32k"), False),
+                                       ("ragged16_fp8", W.named("ragged-16x8k-128k-fp8"), False)):
                 d = DeviceWorkload(wlf, hold_last=True)
                 lf = leg(torch, flush, d, False)
                 lf["workload"] = (f"{wlf.name}: full-scan step, {wlf.n_q} x L "

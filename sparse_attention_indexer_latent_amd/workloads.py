@@ -230,46 +230,53 @@ def ragged_lens(seed, cfg_id, n, lo=8192, hi=131072):
     return np.rint(np.exp(u)).astype(np.int64)
 
 
-def config(i: int, seed: int = 0) -> Workload:
-    """The five synthetic configurations, by index.
+WORKLOADS = ("tiny-4k", "dsv32-decode-32k", "ragged-16x8k-128k-fp8", "hs-128k-b4",
+             "prefill-2048x64k")
 
-    0  tiny: 1 sequence, L=4096, H=8, r=32, d_I=64, fp32 cache, k=256,
-       16 planted tokens x4 (CPU-seconds parity case).
-    1  DeepSeek-V3.2-shaped decode at 32K: H=64, r=256, d_I=128, bf16 cache,
-       batch 1, k=2048, 1% planted x3.
-    2  batched long decode: 16 sequences, ragged log-uniform 8K-128K,
-       fp8 e4m3 cache with per-token fp32 scale, 64-token pages behind a
-       random block table, k=2048.
-    3  HS at 128K: batch 4, L=131072 each, bf16, paged as 2, B=8192, k=2048.
-    4  prefill chunk: 2048 queries at positions 63488..65535 against a
-       65536-token bf16 latent, H=64, r=256, causal, k=2048.
+
+def named(name: str, seed: int = 0) -> Workload:
+    """The five synthetic workloads, by name.
+
+    tiny-4k                 1 sequence, L=4096, H=8, r=32, d_I=64, fp32 cache,
+                            k=256, 16 planted tokens x4 (CPU-seconds parity case).
+    dsv32-decode-32k        DeepSeek-V3.2-shaped decode at 32K: H=64, r=256,
+                            d_I=128, bf16 cache, batch 1, k=2048, 1% planted x3.
+    ragged-16x8k-128k-fp8   batched long decode: 16 sequences, ragged
+                            log-uniform 8K-128K, fp8 e4m3 cache with per-token
+                            fp32 scale, 64-token pages behind a random block
+                            table, k=2048.
+    hs-128k-b4              HS at 128K: batch 4, L=131072 each, bf16, paged as
+                            the ragged workload, B=8192, k=2048.
+    prefill-2048x64k        prefill chunk: 2048 queries at positions
+                            63488..65535 against a 65536-token bf16 latent,
+                            H=64, r=256, causal, k=2048.
     """
-    if i == 0:
+    if name == "tiny-4k":
         return make_decode("tiny-4k", 0, seed, G=4, H=8, r=32, d_I=64, k=256, B=None,
                            cache_dtype="fp32", lens=[4096], n_plant=16, plant_factor=4.0,
                            permute_blocks=False)
-    if i == 1:
+    if name == "dsv32-decode-32k":
         return make_decode("dsv32-decode-32k", 1, seed, G=4, H=64, r=256, d_I=128, k=2048,
                            B=None, cache_dtype="bf16", lens=[32768], plant_frac=0.01,
                            plant_factor=3.0, permute_blocks=False)
-    if i == 2:
+    if name == "ragged-16x8k-128k-fp8":
         return make_decode("ragged-16x8k-128k-fp8", 2, seed, G=4, H=64, r=256, d_I=128,
                            k=2048, B=None, cache_dtype="fp8", lens=ragged_lens(seed, 2, 16),
                            plant_frac=0.01, plant_factor=3.0, permute_blocks=True)
-    if i == 3:
+    if name == "hs-128k-b4":
         return make_decode("hs-128k-b4", 3, seed, G=4, H=64, r=256, d_I=128, k=2048, B=8192,
                            cache_dtype="bf16", lens=[131072] * 4, plant_frac=0.01,
                            plant_factor=3.0, permute_blocks=True)
-    if i == 4:
+    if name == "prefill-2048x64k":
         return make_prefill(seed)
-    raise ValueError(f"no configuration {i}")
+    raise ValueError(f"no workload {name!r}; known: {', '.join(WORKLOADS)}")
 
 
 def hs_128k(batch: int, seed: int = 0, r: int = 256, cache_dtype: str = "bf16",
             scale_block: int = 0, B: int = 8192, G: int = 4, name: str = None,
             layer_corr: float = 0.0) -> Workload:
-    """The 128K hierarchical-selection workload (the batch-4 configuration's
-    generator) at any batch, latent width, cache type, candidate budget and
+    """The 128K hierarchical-selection workload (hs-128k-b4's generator) at
+    any batch, latent width, cache type, candidate budget and
     group size.  r = 192 with an fp8 cache and scale_block = 128 is the
     DeepSeek-V3.2 geometry of the LatentIndex explainer's storage paragraph
     (192 values, a 200-byte record)."""

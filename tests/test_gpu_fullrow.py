@@ -45,11 +45,10 @@ def _oracle_rows(wl):
     return out
 
 
-@pytest.fixture(scope="module", params=[1, 2, 3], ids=["cfg1-32k-b1-bf16", "cfg2-ragged16-fp8",
-                                                         "cfg3-128k-b4-bf16"])
+@pytest.fixture(scope="module", params=["dsv32-decode-32k", "ragged-16x8k-128k-fp8", "hs-128k-b4"])
 def stepped(request):
     cfg = request.param
-    wl = W.config(cfg)
+    wl = W.named(cfg)
     say(f"full-row parity: {wl.name}: device step")
     dw = DeviceWorkload(wl, hold_last=True)
     dw.full_step(append=True, keep_scores=True)

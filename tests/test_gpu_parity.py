@@ -192,8 +192,8 @@ def _scores_vs_oracle(wl, dw, rtol, layers=None, sample=None):
 
 
 def test_score_valu_tiny_config_fp32():
-    say("score VALU config 0 (tiny fp32)")
-    wl = W.config(0)
+    say("score VALU, tiny workload (L 4096, H 8, r 32, fp32)")
+    wl = W.named("tiny-4k")
     dw = DeviceWorkload(wl, hold_last=False)
     _scores_vs_oracle(wl, dw, RTOL_FP32)
 
@@ -238,8 +238,8 @@ def test_score_valu_r192(dtype, H):
 
 
 def test_score_config1_32k_bf16():
-    say("score config 1 (32K, H=64, r=256, bf16): all 4 layers")
-    wl = W.config(1)
+    say("score 32K batch-1 workload (H=64, r=256, bf16): all 4 layers")
+    wl = W.named("dsv32-decode-32k")
     dw = DeviceWorkload(wl, hold_last=False)
     _scores_vs_oracle(wl, dw, RTOL_BF16)
 
@@ -275,11 +275,11 @@ def test_score_plan_guess_holds_and_falls_back():
 
 
 def test_score_config2_fp8_sampled():
-    """Config 2 at full size (16 ragged sequences, 8K-128K, fp8 cache behind a
+    """The ragged fp8 workload at full size (16 sequences, 8K-128K, fp8 cache behind a
     random block table) on the matrix-core path: sampled tokens of every
     query, first and last pages included, against the oracle."""
-    say("score config 2 (16 ragged sequences, fp8 E4M3 + per-token scale): layers 0 and 3, sampled")
-    wl = W.config(2)
+    say("score ragged workload (16 sequences, fp8 E4M3 + per-token scale): layers 0 and 3, sampled")
+    wl = W.named("ragged-16x8k-128k-fp8")
     dw = DeviceWorkload(wl, hold_last=False)
     rng = np.random.default_rng(2)
     for l in (0, 3):
@@ -498,7 +498,7 @@ def test_hs_anchor_fused_equals_two_calls(case):
         wl = W.small_decode(14, n_seq=4, lens=[3000, 70, 12000, 6500], H=64, r=256, d_I=128, G=1,
                             k=100, B=1000, cache_dtype="bf16", nope_off=64, bias=True)
     else:
-        wl = W.config(3)
+        wl = W.named("hs-128k-b4")
     dw = DeviceWorkload(wl, hold_last=False)
     dw.absorb(0)
     n_q, L = wl.n_q, dw.max_len

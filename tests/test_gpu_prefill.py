@@ -109,7 +109,7 @@ def test_prefill_config4_all_layers_scores_and_topk():
     selection over the same (GPU) scores and within the threshold band of the
     oracle's own scores; every workgroup-boundary row on sampled tokens (the
     first and last 64 positions of its prefix and 512 random ones)."""
-    wl = W.config(4)
+    wl = W.named("prefill-2048x64k")
     say(f"prefill config: {wl.name}")
     dw = DeviceWorkload(wl, hold_last=False)
     lat = O.sequence_latent(wl, 0)

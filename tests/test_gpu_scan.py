@@ -74,7 +74,7 @@ def test_scan_batch4_128k_sampled_and_deterministic():
     queries of layers 0 and 3: sampled tokens (first and last pages, planted
     tokens, 1,500 random) against the oracle, and a second launch
     bit-identical to the first."""
-    wl = W.config(3)
+    wl = W.named("hs-128k-b4")
     say(f"scan: {wl.name}")
     dw = DeviceWorkload(wl, hold_last=False)
     rng = np.random.default_rng(3)
@@ -101,7 +101,7 @@ def test_hs_step_batch4_128k_followers():
     and selection exact on its dumped scores, every follower's candidate
     scores against the oracle, and every follower's selection exact on its
     dumped candidate scores."""
-    wl = W.config(3)
+    wl = W.named("hs-128k-b4")
     say(f"HS step followers: {wl.name}")
     dw = DeviceWorkload(wl, hold_last=False)
     dw.hs_step(append=False, keep_scores=True)

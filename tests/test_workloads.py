@@ -6,7 +6,7 @@ from sparse_attention_indexer_latent_amd import workloads as W
 
 
 def test_config0_shapes_and_determinism():
-    a, b = W.config(0), W.config(0)
+    a, b = W.named("tiny-4k"), W.named("tiny-4k")
     assert a.H == 8 and a.r == 32 and a.d_I == 64 and a.k == 256 and a.G == 4
     assert a.lens.tolist() == [4096] and a.cache_dtype == "fp32"
     assert a.Dt.shape == (4, 32, 64) and a.q.shape == (4, 1, 8, 64) and a.w.shape == (4, 1, 8)
@@ -22,11 +22,11 @@ def test_config0_shapes_and_determinism():
 
 
 def test_seeds_differ():
-    assert not np.array_equal(W.config(0, seed=0).latent(0), W.config(0, seed=1).latent(0))
+    assert not np.array_equal(W.named("tiny-4k", seed=0).latent(0), W.named("tiny-4k", seed=1).latent(0))
 
 
 def test_config2_ragged_paged():
-    wl = W.config(2)
+    wl = W.named("ragged-16x8k-128k-fp8")
     assert wl.n_seq == 16 and wl.cache_dtype == "fp8"
     assert wl.lens.min() >= 8192 and wl.lens.max() <= 131072
     nblk = (wl.lens + 63) // 64
@@ -39,10 +39,10 @@ def test_config2_ragged_paged():
 
 
 def test_config3_and_prefill_shapes():
-    wl = W.config(3)
+    wl = W.named("hs-128k-b4")
     assert wl.lens.tolist() == [131072] * 4 and wl.B == 8192 and wl.k == 2048
     assert wl.block_table.shape == (4, 2048)
-    pf = W.config(4)
+    pf = W.named("prefill-2048x64k")
     assert pf.n_q == 2048 and pf.prefill_positions[0] == 63488 and pf.prefill_positions[-1] == 65535
     assert pf.q_len[0] == 63489 and pf.q_len[-1] == 65536
     bits, w = pf.prefill_queries(0)
