@@ -665,7 +665,12 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
       // all that is left in flight
       wait_vm_rt(vpu * (issued - 1 - p));
       lds_barrier();  // unit p is in for everyone; unit p-1 has been read
-      const int upto = min(nu, p + C::AHEAD + 1);  // stage of unit p + AHEAD = that of p - 1
+      // At most one unit per barrier: an issue stalls while the CU's
+      // outstanding loads are at their limit, so a second unit here would
+      // hold this wavefront (and with it the next barrier) until part of
+      // the first had landed.  After the q~ stages free up that keeps two
+      // units in flight beyond the one being computed.
+      const int upto = min(nu, min(p + C::AHEAD + 1, issued + 1));  // stage of p + AHEAD = that of p - 1
       for (int u = issued; u < upto; ++u) issue_unit(u);
       issued = max(issued, upto);
     }
