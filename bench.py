@@ -401,6 +401,33 @@ def dsa_leg(torch, flush, W, DsaGroup, batch, K=20, Kc=6):
     return out
 
 
+def context_sweep(torch, W, DeviceWorkload, DsaGroup, Ls, K=20):
+    """HS step of the pages' geometry (192-value fp8 latent, 200-byte record,
+    B = 8192) against the native DSA indexer of the same four layers (132 B
+    per token per layer), batch 1, at each context length of the pages'
+    Table 4; warm step times (back-to-back steps)."""
+    rows = []
+    for L in Ls:
+        wl = W.hs_128k(1, r=192, cache_dtype="fp8", scale_block=128, L=L)
+        d = DeviceWorkload(wl, hold_last=True)
+        hs_us = loop_us(torch, d.hs_step, K)
+        full_us = loop_us(torch, d.full_step, K)
+        del d
+        g = DsaGroup([W.dsa_layer(l, [L]) for l in range(4)])
+        dsa_us = loop_us(torch, g.step, K)
+        del g
+        torch.cuda.empty_cache()
+        rows.append({"L": L, "hs_us_per_group_step": hs_us, "full_scan_us_per_group_step": full_us,
+                     "dsa_us_per_group_step": dsa_us, "hs_speedup_vs_dsa": dsa_us / hs_us,
+                     "hs_latent_bytes": 200 * (L + 3 * min(8192, L)), "dsa_key_bytes": 4 * 132 * L})
+    return {"workload": "batch 1, H=64, k=2048; HS: 200 B/token latent (192 fp8 values + 2 fp32 "
+                        "block scales), B=8192, 3 followers; DSA: 4 layers x own fp8 key cache "
+                        "(128 values + 1 fp32 scale = 132 B/token)",
+            "pages_table4_context": "HS over DSA 2.30-2.72x at 8K-128K (ms per decode token, all "
+                                    "61 indexers, batch 1, eight unnamed GPUs)",
+            "points": rows}
+
+
 def budget_sweep(torch, W, DeviceWorkload, Bs, r=192, dtype="fp8", sb=128, K=20, layer_corr=0.0):
     """Candidate budget B against HS step time and the followers' recall of
     their own full-scan selections (|S_HS ∩ S_full| / k, mean over followers
@@ -666,6 +693,8 @@ def main():
                         legs["hs_128k_b1"]["us_per_group_step"] if batch == 1 else us_step),
                     "pages_table4_context": "2.30-2.72x (ms per decode token, all 61 indexers, "
                                             "batch 1, eight unnamed GPUs)"}
+            out["context_sweep"] = context_sweep(torch, W, DeviceWorkload, DsaGroup,
+                                                 [8192, 16384, 32768, 65536, 131072])
             out["b_sweep"] = budget_sweep(torch, W, DeviceWorkload, [2048, 4096, 8192, 16384, 32768])
             out["b_sweep_correlated_layers"] = budget_sweep(
                 torch, W, DeviceWorkload, [2048, 4096, 8192, 16384, 32768], layer_corr=0.9)

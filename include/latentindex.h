@@ -230,7 +230,8 @@ li_status li_topk(const float *scores, int64_t ld, int32_t n_rows, const int32_t
  * ("Hierarchical Selection" paragraph): from the anchor's full score rows,
  * the candidate set C = top-min(B, |V|) positions and the anchor's own
  * selection S = top-min(k, |V|) (S is inside C because B >= k), both in one
- * pass over the scores.
+ * pass over the scores (rows of at most 8192 positions: one single-workgroup
+ * selection per output instead, which is faster there).
  *   scores, ld, n_rows, valid_len, max_len: as for li_topk.
  *   max_len    at most 2,097,152 (LI_ERR_UNSUPPORTED beyond).
  *   B, cand    1 <= B <= 65536; cand device int32 [n_rows, B] (out):
@@ -255,9 +256,10 @@ li_status li_hs_anchor_select(const float *scores, int64_t ld, int32_t n_rows,
  * li_hs_anchor -- the anchor layer's whole part of hierarchical selection in
  * one call ("Hierarchical Selection" paragraph, eq. 8): its scores of every
  * position (as li_score) and, from them, C and S (as li_hs_anchor_select).
- * For a bf16 cache with H = 64, r = 256 and at most 64 queries, the scorer
- * builds the rows' key histograms as it writes the scores, so the selection
- * does not read them an extra time; otherwise it is the two calls in turn.
+ * For a bf16 cache with H = 64, r = 256, at most 64 queries and max_len
+ * above 8192, the scorer builds the rows' key histograms as it writes the
+ * scores, so the selection does not read them an extra time; otherwise it
+ * is the two calls in turn.
  *   q_tilde .. ld: as for li_score; q_len[i] is also row i's valid length;
  *               max_len at most 2,097,152 (LI_ERR_UNSUPPORTED beyond).
  *   B, cand, k, sel: as for li_hs_anchor_select.
@@ -278,9 +280,9 @@ li_status li_hs_anchor(const void *q_tilde, li_dtype qt_dt, const float *w, cons
  * li_score_topk -- one layer's full-scan selection in one call ("Methodology",
  * eq. 8 and the TopK definition after it): the scores of every position (as
  * li_score) and each query's top-min(k, q_len[i]) positions (as li_topk with
- * valid_len = q_len).  For a bf16 cache with H = 64, r = 256 and at most 64
- * queries the scorer builds the rows' key histograms as it writes the
- * scores, so the selection reads them once fewer.
+ * valid_len = q_len).  For a bf16 cache with H = 64, r = 256, at most 64
+ * queries and max_len above 8192 the scorer builds the rows' key histograms
+ * as it writes the scores, so the selection reads them once fewer.
  *   q_tilde .. ld: as for li_score; max_len at most 2,097,152.
  *   k, out_idx   1 <= k <= 65536; out_idx device int32 [n_q, k] (out):
  *                ascending token ids, -1 padded.

@@ -298,6 +298,20 @@ li_status li_hs_anchor_select(const float *scores, int64_t ld, int32_t n_rows,
   if (!ws || ws_bytes < need) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
   li_status s = check_device();
   if (s != LI_OK) return s;
+  if (max_len <= li::topk_single_max()) {
+    // short rows: one single-workgroup launch per selection; where B covers
+    // the row, C is the row's positions in order and comes with S's launch
+    if (sel && B >= max_len)
+      return hip_status(li::launch_topk_with_all(scores, ld, n_rows, valid_len, max_len, k, sel, B,
+                                                 cand, (hipStream_t)stream),
+                        "li_hs_anchor_select launch");
+    hipError_t e = li::launch_topk(scores, ld, n_rows, valid_len, nullptr, 0, 1, max_len, B, cand,
+                                   nullptr, nullptr, (hipStream_t)stream);
+    if (e == hipSuccess && sel)
+      e = li::launch_topk(scores, ld, n_rows, valid_len, nullptr, 0, 1, max_len, k, sel, nullptr,
+                          nullptr, (hipStream_t)stream);
+    return hip_status(e, "li_hs_anchor_select launch");
+  }
   hipError_t e = sel ? li::launch_topk2(scores, ld, n_rows, valid_len, max_len > 0 ? max_len : 1, B,
                                         cand, k, sel, ws, (hipStream_t)stream)
                      : li::launch_topk2(scores, ld, n_rows, valid_len, max_len > 0 ? max_len : 1, B,
@@ -328,7 +342,9 @@ li_status li_hs_anchor(const void *q_tilde, li_dtype qt_dt, const float *w, cons
   if ((s = check_device()) != LI_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   li::CacheView cv = li::view_of(*cache);
-  const bool fused = max_len > 0 && !li::score_prefill_supported(qt_dt, H, n_q, cv) &&
+  // (short rows take the single-workgroup selection, which needs no histograms)
+  const bool fused = max_len > li::topk_single_max() &&
+                     !li::score_prefill_supported(qt_dt, H, n_q, cv) &&
                      li::score_scan_supported(qt_dt, H, n_q, max_len, cv) &&
                      n_q <= li::topk2_counted_max_rows();
   auto record = [&](int i) {

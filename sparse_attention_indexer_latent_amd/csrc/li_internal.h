@@ -116,6 +116,17 @@ hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_
                        const int32_t *ids, int64_t ids_ld, int ids_rows, int max_len, int k,
                        int32_t *out_idx,
                        float *out_val, void *ws, hipStream_t st);
+// Rows of at most this many positions are selected by one workgroup per row
+// in a single launch (no workspace), which beats the two launches of the
+// nested multi-workgroup pass there.
+int topk_single_max();
+// The single-workgroup selection of rows of at most topk_single_max()
+// positions (max_len), writing besides the top-k of each row the list of all
+// its positions, -1 padded to all_k >= max_len (a selection whose size
+// covers the row).
+hipError_t launch_topk_with_all(const float *scores, int64_t ld, int n_rows,
+                                const int32_t *valid_len, int max_len, int k, int32_t *out_idx,
+                                int all_k, int32_t *all_idx, hipStream_t st);
 
 // Two nested selections (k_outer >= k_inner) in one pass; ws of
 // topk2_ws_bytes(n_rows, max_len) bytes; rows of at most topk2_max_len()

@@ -68,8 +68,14 @@ union Frag {
   uint32_t u[4];
 };
 
+// query i's length, clamped into [0, max_len]
+__device__ __forceinline__ int qlen_at(const int32_t *q_len, int i, int max_len) {
+  return min(max(q_len[i], 0), max_len);
+}
 template <int TOK>
-__device__ __forceinline__ int qpages(const int32_t *q_len, int i) { return (q_len[i] + TOK - 1) / TOK; }
+__device__ __forceinline__ int qpages(const int32_t *q_len, int i, int max_len) {
+  return (qlen_at(q_len, i, max_len) + TOK - 1) / TOK;
+}
 
 // Wave 0 works out this workgroup's contiguous range of the flattened
 // (query, page) list and writes (query, page, sequence) per local page into
@@ -79,14 +85,14 @@ __device__ __forceinline__ int qpages(const int32_t *q_len, int i) { return (q_l
 // guarantees the range fits whenever every q_len honours its bound).
 template <int TOK, typename SH>
 __device__ void plan_range(SH &sh, int n_q, const int32_t *q_len, const int32_t *q_seq, int cap,
-                           int len0, int seq0) {
+                           int len0, int seq0, int max_len) {
   const int lane = threadIdx.x % kWave;
   const int np0 = (len0 + TOK - 1) / TOK;
-  auto pages_of = [&](int q) { return q < kWave ? __shfl(np0, q, kWave) : qpages<TOK>(q_len, q); };
+  auto pages_of = [&](int q) { return q < kWave ? __shfl(np0, q, kWave) : qpages<TOK>(q_len, q, max_len); };
   auto seq_of = [&](int q) { return q < kWave ? __shfl(seq0, q, kWave) : q_seq[q]; };
   int64_t T = 0;
   for (int c = 0; c < n_q; c += kWave) {
-    int np = c == 0 ? np0 : (c + lane < n_q ? qpages<TOK>(q_len, c + lane) : 0);
+    int np = c == 0 ? np0 : (c + lane < n_q ? qpages<TOK>(q_len, c + lane, max_len) : 0);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) np += __shfl_xor(np, o, kWave);
     T += np;
@@ -98,7 +104,7 @@ __device__ void plan_range(SH &sh, int n_q, const int32_t *q_len, const int32_t 
   int64_t cum = 0;
   if (cnt > 0) {
     for (int c = 0; c < n_q; c += kWave) {
-      const int np = c == 0 ? np0 : (c + lane < n_q ? qpages<TOK>(q_len, c + lane) : 0);
+      const int np = c == 0 ? np0 : (c + lane < n_q ? qpages<TOK>(q_len, c + lane, max_len) : 0);
       int incl = np;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -433,9 +439,9 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
     const int sq = (int)((f0s + ti) / PPQ), spg = (int)((f0s + ti) % PPQ);
     const int sblk = cv.block_table[(int64_t)sq * cv.max_blocks + ((spg * TOK) >> 6)];
     const int li = min(lane, n_q - 1);
-    int len0 = q_len[li], seq0 = q_seq[li];  // real lengths and sequences of the first 64 queries
+    int len0 = qlen_at(q_len, li, max_len), seq0 = q_seq[li];  // the first 64 queries' lengths and sequences
     if (lane >= n_q) len0 = seq0 = 0;
-    const int slen = q_len[sq];
+    const int slen = qlen_at(q_len, sq, max_len);
     const int q0 = cnt_s > 0 ? (int)(f0s / PPQ) : 0;
     if (tid < cnt_s) {
       sh.prow[tid] = ((sblk >= 0 && sblk < cv.n_blocks) ? sblk : 0) * kPage + ((spg * TOK) & 63);
@@ -470,7 +476,7 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
             sh.f0 = f0;
           }
         } else {
-          plan_range<TOK>(sh, n_q, q_len, q_seq, kMaxPagesPerWG, len0, seq0);
+          plan_range<TOK>(sh, n_q, q_len, q_seq, kMaxPagesPerWG, len0, seq0, max_len);
         }
       }
     }
@@ -512,7 +518,7 @@ score_mfma_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
       // valid tokens per unit (read by the stores, after the loop's barriers)
       for (int p = tid; p < npl; p += kThreads) {
         const int q = sh.pq[p];
-        const int len = n_q <= kWave ? sh.qlen[q] : q_len[q];
+        const int len = n_q <= kWave ? sh.qlen[q] : qlen_at(q_len, q, max_len);
         sh.pvalid[p] = min(TOK, len - sh.ppg[p] * TOK);
       }
     }

@@ -110,7 +110,7 @@ score_prefill_kernel(const uint16_t *__restrict__ q_tilde, const float *__restri
     const int sq = qi < n_q ? q_seq[qi] : -1;
     const bool ok = sq >= 0 && sq < cv.n_seq;  // others are skipped
     sh.qseq[tid] = ok ? sq : -1;
-    sh.qlen[tid] = ok ? min(q_len[qi], max_len) : 0;
+    sh.qlen[tid] = ok ? min(max(q_len[qi], 0), max_len) : 0;
   }
   bar();
   const int myseq = sh.qseq[wave];

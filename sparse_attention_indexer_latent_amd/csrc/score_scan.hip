@@ -374,7 +374,7 @@ score_scan_kernel(const void *__restrict__ q_tilde, const float *__restrict__ w,
     constexpr int kCT = kCW * kWave;  // compute threads
     static_assert(2 * kCT >= kMaxPages, "two page-table entries per compute thread");
     const int li = min(lane, n_q - 1);
-    int len0 = q_len[li], seq0 = q_seq[li];
+    int len0 = min(max(q_len[li], 0), max_len), seq0 = q_seq[li];
     if (lane >= n_q) len0 = seq0 = 0;
     const int npg = gnu * C::PPU;  // pages of the guessed range
     int pg[2];

@@ -21,12 +21,12 @@ __global__ void __launch_bounds__(256)
 score_valu_kernel(const void *__restrict__ q_tilde, int qt_dt, const float *__restrict__ w,
                   const float *__restrict__ beta, int H, const int32_t *__restrict__ q_seq,
                   const int32_t *__restrict__ q_len, CacheView cv, const int32_t *__restrict__ cand,
-                  int B, int cand_rows, float *__restrict__ out, int64_t ld, int TT) {
+                  int B, int cand_rows, float *__restrict__ out, int64_t ld, int TT, int max_len) {
   extern __shared__ float lds[];
   const int r = cv.r;
   const int i = blockIdx.y;
   const int t0 = blockIdx.x * TT;
-  const int n = cand ? B : q_len[i];
+  const int n = cand ? B : min(max(q_len[i], 0), max_len);
   if (t0 >= n) return;  // uniform across the workgroup, before any barrier
   const int nt = min(TT, n - t0);
   float *qs = lds;                      // [H][r]
@@ -120,7 +120,7 @@ hipError_t launch_score_valu(const void *q_tilde, int qt_dt, const float *w, con
   if (e != hipSuccess) return e;
   dim3 grid((max_len + TT - 1) / TT, n_q);
   score_valu_kernel<<<grid, 256, lds, st>>>(q_tilde, qt_dt, w, beta, H, q_seq, q_len, cv, cand, B,
-                                            max(cand_rows, 1), out, ld, TT);
+                                            max(cand_rows, 1), out, ld, TT, max_len);
   return hipGetLastError();
 }
 

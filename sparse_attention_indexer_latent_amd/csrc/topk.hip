@@ -87,7 +87,7 @@ topk_row_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
   TopkShared &sh = *reinterpret_cast<TopkShared *>(smem);
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
-  const int n = valid_len[row];
+  const int n = max(valid_len[row], 0);
   const float *u = scores + (int64_t)row * ld;
   const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
   int32_t *oi = out_idx + (int64_t)row * k;
@@ -309,7 +309,7 @@ topk_hist_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__
 #pragma unroll
   for (int j = 0; j < kSegPer; ++j)
     v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (p0 + tid + j * kSegThreads) * 4, 0, 0));
-  const int n = valid_len[row];
+  const int n = min(max(valid_len[row], 0), m.max_len);
   zero_share<kSegThreads>(m.h10 + (int64_t)row * 2 * 1024, 2 * 1024, seg, gridDim.x);
   if (p0 >= n) return;
   const int p1 = min(n, p0 + kSeg);
@@ -470,7 +470,7 @@ topk_extract_kernel(const float *__restrict__ scores, int64_t ld, const int32_t 
 #pragma unroll
     for (int e = 0; e < kBins / kSegThreads; ++e) a[e] = g[e * kSegThreads + tid];
   }
-  const int n = valid_len[row];
+  const int n = min(max(valid_len[row], 0), m.max_len);
   if (p0 >= n) {
     if (tid == 0) m.seg_cnt[(int64_t)row * m.S + seg] = 0;
     return;
@@ -739,7 +739,7 @@ topk_select_kernel(const float *__restrict__ scores, int64_t ld,
   // histograms, the segments' key counts, this segment's extracted keys and positions, and the first
   // 256 extracted keys of the 8 segments this wavefront scans first.  Each
   // segment owns kSeg slots, so these are in bounds whatever the counts.
-  const int n = valid_len[row];
+  const int n = min(max(valid_len[row], 0), m.max_len);
   uint32_t b[2 * 1024 / kSelThreads];
   {
     const uint32_t *g10 = m.h10 + (int64_t)row * 2 * 1024;
@@ -1007,7 +1007,7 @@ topk_lds_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
   extern __shared__ __align__(16) unsigned char smem[];
   LdsRowShared &sh = *reinterpret_cast<LdsRowShared *>(smem);
   const int row = blockIdx.x, tid = threadIdx.x;
-  const int n = min(valid_len ? valid_len[row] : const_len, kLdsRow);
+  const int n = max(min(valid_len ? valid_len[row] : const_len, min(const_len, kLdsRow)), 0);
   const float *u = scores + (int64_t)row * ld;
   const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
   int32_t *oi = out_idx + (int64_t)row * k;
@@ -1109,7 +1109,8 @@ __device__ __forceinline__ void r8_find(const uint32_t (&c)[PER], int nb, uint32
 __global__ void __launch_bounds__(kThreads)
 topk_r8_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ valid_len,
                int const_len, const int32_t *__restrict__ ids, int64_t ids_ld, int ids_rows, int k,
-               int32_t *__restrict__ out_idx, float *__restrict__ out_val) {
+               int32_t *__restrict__ out_idx, float *__restrict__ out_val,
+               int32_t *__restrict__ all_idx, int all_k) {
   __shared__ R8Shared sh;
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const float *u = scores + (int64_t)row * ld;
@@ -1155,13 +1156,17 @@ topk_r8_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__re
       for (int j = 0; j < kR8Per; ++j) id[j] = p0 + j;
     }
   }
-  const int n = valid_len ? min(valid_len[row], cap) : cap;
+  const int n = max(valid_len ? min(valid_len[row], cap) : cap, 0);
   int32_t *oi = out_idx + (int64_t)row * k;
   float *ov = out_val ? out_val + (int64_t)row * k : nullptr;
   const int m = min(k, n);
   for (int j = m + tid; j < k; j += kThreads) {
     oi[j] = -1;
     if (ov) ov[j] = -INFINITY;
+  }
+  if (all_idx) {  // a second output that takes every position (all_k >= n)
+    int32_t *oa = all_idx + (int64_t)row * all_k;
+    for (int j = tid; j < all_k; j += kThreads) oa[j] = j < n ? (idm ? idm[j] : j) : -1;
   }
   if (n <= k) {
     for (int p = tid; p < n; p += kThreads) {
@@ -1321,7 +1326,7 @@ topk_reg_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
                 int32_t *__restrict__ out_idx, float *__restrict__ out_val) {
   __shared__ RegShared sh;
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid % kWave;
-  const int n = min(valid_len[row], NIT * 4 * kThreads);
+  const int n = max(min(valid_len[row], NIT * 4 * kThreads), 0);
   const float *u = scores + (int64_t)row * ld;
   const int32_t *idm = ids ? ids + (int64_t)(row % ids_rows) * ids_ld : nullptr;
   int32_t *oi = out_idx + (int64_t)row * k;
@@ -1519,12 +1524,21 @@ size_t topk_ws_bytes(int n_rows, int max_len, int) {
   return (max_len > kLdsRow && use_multi(n_rows, max_len)) ? multi_ws_bytes(n_rows, max_len) : 0;
 }
 
+hipError_t launch_topk_with_all(const float *scores, int64_t ld, int n_rows,
+                                const int32_t *valid_len, int max_len, int k, int32_t *out_idx,
+                                int all_k, int32_t *all_idx, hipStream_t st) {
+  if (max_len > kR8Max || all_k < max_len) return hipErrorInvalidValue;
+  topk_r8_kernel<<<n_rows, kThreads, 0, st>>>(scores, ld, valid_len, max_len, nullptr, 0, 1, k, out_idx,
+                                              nullptr, all_idx, all_k);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_t *valid_len,
                        const int32_t *ids, int64_t ids_ld, int ids_rows, int max_len, int k, int32_t *out_idx,
                        float *out_val, void *ws, hipStream_t st) {
   if (max_len <= kR8Max) {
     topk_r8_kernel<<<n_rows, kThreads, 0, st>>>(scores, ld, valid_len, max_len, ids, ids_ld, ids_rows, k,
-                                                out_idx, out_val);
+                                                out_idx, out_val, nullptr, 0);
     return hipGetLastError();
   }
   if (max_len <= kLdsRow) {
@@ -1558,6 +1572,8 @@ hipError_t launch_topk(const float *scores, int64_t ld, int n_rows, const int32_
 }
 
 size_t topk2_ws_bytes(int n_rows, int max_len) { return multi_ws_bytes(n_rows, max_len); }
+
+int topk_single_max() { return kR8Max; }
 
 int64_t topk2_max_len() { return (int64_t)kMaxSegs * kSeg; }
 

@@ -274,17 +274,18 @@ def named(name: str, seed: int = 0) -> Workload:
 
 def hs_128k(batch: int, seed: int = 0, r: int = 256, cache_dtype: str = "bf16",
             scale_block: int = 0, B: int = 8192, G: int = 4, name: str = None,
-            layer_corr: float = 0.0) -> Workload:
+            layer_corr: float = 0.0, L: int = 131072) -> Workload:
     """The 128K hierarchical-selection workload (hs-128k-b4's generator) at
     any batch, latent width, cache type, candidate budget and
-    group size.  r = 192 with an fp8 cache and scale_block = 128 is the
+    group size (and, for a sweep over context lengths, any length L).
+    r = 192 with an fp8 cache and scale_block = 128 is the
     DeepSeek-V3.2 geometry of the LatentIndex explainer's storage paragraph
     (192 values, a 200-byte record)."""
-    name = name or (f"hs-128k-b{batch}-{cache_dtype}-r{r}" + (f"-sb{scale_block}" if scale_block
-                                                                else "")
+    name = name or (f"hs-{L // 1024}k-b{batch}-{cache_dtype}-r{r}"
+                    + (f"-sb{scale_block}" if scale_block else "")
                     + (f"-rho{layer_corr:g}" if layer_corr else ""))
     return make_decode(name, 3 if r == 256 else 5, seed, G=G, H=64, r=r, d_I=128, k=2048, B=B,
-                       cache_dtype=cache_dtype, lens=[131072] * batch, plant_frac=0.01,
+                       cache_dtype=cache_dtype, lens=[L] * batch, plant_frac=0.01,
                        plant_factor=3.0, permute_blocks=True, scale_block=scale_block,
                        layer_corr=layer_corr)
 

@@ -460,6 +460,37 @@ def test_hs_anchor_select_nested_exact(B, k):
         assert np.array_equal(sel[i], O.pad(O.topk(row, k), k)), i
 
 
+@pytest.mark.parametrize("B,k", [(8192, 2048), (3000, 2048), (5000, 1)])
+def test_hs_anchor_select_short_rows_exact(B, k):
+    """Rows of at most 8192 positions take one single-workgroup launch per
+    selection; both outputs exact against the oracle (ties included), and a
+    long-row call on the same workspace afterwards is still exact."""
+    say(f"hs_anchor_select short rows B={B} k={k}")
+    rng = np.random.default_rng(3 * B + k)
+    lens = [0, 1, 17, 2048, 5000, 8191, 8192]
+    u = np.round(rng.standard_normal((len(lens), 8192)), 2).astype(np.float32)
+    ws = ops.hs_anchor_workspace(len(lens), 131072)
+    cand, sel = ops.hs_anchor_select(torch.from_numpy(u).cuda(),
+                                     torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda(),
+                                     8192, B, k, ws=ws)
+    torch.cuda.synchronize()
+    cand, sel = cand.cpu().numpy(), sel.cpu().numpy()
+    for i, n in enumerate(lens):
+        row = u[i, :n].astype(np.float64)
+        assert np.array_equal(cand[i], O.pad(O.hs_candidates(row, B), B)), i
+        assert np.array_equal(sel[i], O.pad(O.topk(row, k), k)), i
+    ul = np.round(rng.standard_normal((2, 40000)), 2).astype(np.float32)
+    ll = np.asarray([40000, 31000], dtype=np.int32)
+    cand, sel = ops.hs_anchor_select(torch.from_numpy(ul).cuda(), torch.from_numpy(ll).cuda(),
+                                     40000, B, k, ws=ws)
+    torch.cuda.synchronize()
+    cand, sel = cand.cpu().numpy(), sel.cpu().numpy()
+    for i, n in enumerate(ll):
+        row = ul[i, :n].astype(np.float64)
+        assert np.array_equal(cand[i], O.pad(O.hs_candidates(row, B), B)), ("long", i)
+        assert np.array_equal(sel[i], O.pad(O.topk(row, k), k)), ("long", i)
+
+
 def test_hs_anchor_select_reuses_one_workspace():
     """One workspace across calls of different row counts and lengths (each
     call leaves its counting arrays zeroed for the next), every result exact."""
