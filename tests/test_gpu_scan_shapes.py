@@ -159,3 +159,39 @@ def test_dsa_comparator_group_step():
             assert_scores_close(u[s, :L], o, RTOL_FP8, f"DSA layer {l} query {s}")
             assert np.array_equal(sel[s], O.pad(O.topk(u[s, :L].astype(np.float64), wl.k), wl.k))
             assert_selection_band(sel[s], o, wl.k, RTOL_FP8, f"DSA layer {l} top-k query {s}")
+
+
+@pytest.mark.parametrize("L", [8192, 16384])
+def test_pages_geometry_hs_and_full_step(L):
+    """The context sweep's batch-1 workload of the pages' geometry (192 fp8
+    values + two block scales, B = 8192, k = 2048) at 8K (B covers the row:
+    the candidate set is every position and the selections must equal the
+    full-scan step's) and at 16K: every anchor and follower score against the
+    oracle, every selection exact on the dumped scores."""
+    say(f"pages' geometry HS and full step, L={L}")
+    wl = W.hs_128k(1, r=192, cache_dtype="fp8", scale_block=128, L=L)
+    dw = DeviceWorkload(wl, hold_last=False)
+    dw.hs_step(append=False, keep_scores=True)
+    torch.cuda.synchronize()
+    u = dw.scores.cpu().numpy()[0, :L]
+    cand = dw.cand.cpu().numpy()[0]
+    hs_sel = dw.hs_sel.cpu().numpy()[:, 0]
+    cs_all = dw.cand_scores.cpu().numpy()[:, 0]
+    C = O.sequence_latent(wl, 0)[:L]
+    o0 = O.layer_scores(C, wl.q[0, 0], wl.Dt[0], wl.b[0], wl.nope_off, wl.w[0, 0])
+    assert_scores_close(u, o0, RTOL_FP8, f"pages' geometry L={L} anchor")
+    assert np.array_equal(cand, O.pad(O.hs_candidates(u.astype(np.float64), wl.B), wl.B))
+    assert np.array_equal(hs_sel[0], O.pad(O.topk(u.astype(np.float64), wl.k), wl.k))
+    nc = min(wl.B, L)
+    if L <= wl.B:
+        assert np.array_equal(cand[:L], np.arange(L)) and np.all(cand[L:] == -1)
+    for l in range(1, wl.G):
+        cs = cs_all[l]
+        o = O.layer_scores(C[cand[:nc]], wl.q[l, 0], wl.Dt[l], wl.b[l], wl.nope_off, wl.w[l, 0])
+        assert_scores_close(cs[:nc], o, RTOL_FP8, f"pages' geometry L={L} follower {l}")
+        assert np.array_equal(hs_sel[l], O.pad(O.hs_follower(cand[:nc], cs[:nc].astype(np.float64),
+                                                             wl.k), wl.k)), l
+    if L <= wl.B:  # HS scores every position of every layer: it is the full scan
+        dw.full_step(append=False)
+        torch.cuda.synchronize()
+        assert np.array_equal(dw.sel.cpu().numpy()[:, 0], hs_sel)
