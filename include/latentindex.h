@@ -239,7 +239,8 @@ li_status li_topk(const float *scores, int64_t ld, int32_t n_rows, const int32_t
  *   k, sel     1 <= k <= B; sel device int32 [n_rows, k] (out), ascending,
  *              -1 padded.  sel may be NULL when only C is wanted.
  *   ws         device workspace of li_hs_anchor_workspace_bytes() bytes,
- *              zeroed once before its first use (e.g. one hipMemsetAsync).
+ *              zeroed once before its first use (e.g. one hipMemsetAsync);
+ *              none (0 bytes, ws may be NULL) for max_len <= 8192.
  *              Each call leaves the counters it relies on zeroed again, so
  *              the workspace serves later calls of any n_rows <= 64 and
  *              max_len it is large enough for without another clear (with

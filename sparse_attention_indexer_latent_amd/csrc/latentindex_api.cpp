@@ -277,7 +277,8 @@ li_status li_topk(const float *scores, int64_t ld, int32_t n_rows, const int32_t
 }
 
 size_t li_hs_anchor_workspace_bytes(int32_t n_rows, int32_t max_len) {
-  if (n_rows <= 0 || max_len <= 0) return 0;
+  // rows of at most topk_single_max() positions select without a workspace
+  if (n_rows <= 0 || max_len <= li::topk_single_max()) return 0;
   return li::topk2_ws_bytes(n_rows, max_len);
 }
 
@@ -294,8 +295,8 @@ li_status li_hs_anchor_select(const float *scores, int64_t ld, int32_t n_rows,
                 (long long)li::topk2_max_len());
   if (n_rows == 0) return LI_OK;
   if (!scores || !valid_len || !cand) return fail(LI_ERR_INVALID, "scores/valid_len/cand is NULL");
-  size_t need = li_hs_anchor_workspace_bytes(n_rows, max_len > 0 ? max_len : 1);
-  if (!ws || ws_bytes < need) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
+  size_t need = li_hs_anchor_workspace_bytes(n_rows, max_len);
+  if (need && (!ws || ws_bytes < need)) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
   li_status s = check_device();
   if (s != LI_OK) return s;
   if (max_len <= li::topk_single_max()) {
@@ -337,8 +338,8 @@ li_status li_hs_anchor(const void *q_tilde, li_dtype qt_dt, const float *w, cons
                 (long long)li::topk2_max_len());
   if (n_q == 0) return LI_OK;
   if (!q_len || !scores || !cand) return fail(LI_ERR_INVALID, "q_len/scores/cand is NULL");
-  size_t need = li_hs_anchor_workspace_bytes(n_q, max_len > 0 ? max_len : 1);
-  if (!ws || ws_bytes < need) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
+  size_t need = li_hs_anchor_workspace_bytes(n_q, max_len);
+  if (need && (!ws || ws_bytes < need)) return fail(LI_ERR_INVALID, "workspace needs %zu bytes", need);
   if ((s = check_device()) != LI_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   li::CacheView cv = li::view_of(*cache);

@@ -81,24 +81,27 @@ def test_validation_errors_are_host_side(L):
                               ops.LI_FP32, 1, 0, 64, 128, FAKE, 0, None, 64, FAKE, None,
                               None) == ops.LI_OK  # nothing to do: no launch
     # the fused anchor call: B < k, max_len > ld, NULL outputs, too small a workspace
-    big = L.li_hs_anchor_workspace_bytes(4, 256)
-    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
-                          FAKE, 256, 100, FAKE, 200, FAKE, FAKE, big, None,
+    # (rows of 20000 positions: a length that needs the workspace)
+    c = _cache(max_blocks=400)
+    big = L.li_hs_anchor_workspace_bytes(4, 20000)
+    assert big > 0
+    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 20000, ctypes.byref(c),
+                          FAKE, 20000, 100, FAKE, 200, FAKE, FAKE, big, None,
                           None) == ops.LI_ERR_INVALID
     assert b"B (100) < k (200)" in L.li_last_error()
-    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
+    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 20000, ctypes.byref(c),
                           FAKE, 128, 100, FAKE, 10, FAKE, FAKE, big, None,
                           None) == ops.LI_ERR_INVALID  # max_len > ld
-    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
-                          None, 256, 100, FAKE, 10, FAKE, FAKE, big, None,
+    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 20000, ctypes.byref(c),
+                          None, 20000, 100, FAKE, 10, FAKE, FAKE, big, None,
                           None) == ops.LI_ERR_INVALID  # scores NULL
-    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
-                          FAKE, 256, 100, FAKE, 10, FAKE, FAKE, big - 1, None,
+    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 20000, ctypes.byref(c),
+                          FAKE, 20000, 100, FAKE, 10, FAKE, FAKE, big - 1, None,
                           None) == ops.LI_ERR_INVALID  # workspace too small
     assert b"workspace needs" in L.li_last_error()
     # no queries: a no-op that succeeds without a device
-    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 0, 64, FAKE, FAKE, 256, ctypes.byref(c),
-                          FAKE, 256, 100, FAKE, 10, FAKE, FAKE, big, None, None) == ops.LI_OK
+    assert L.li_hs_anchor(FAKE, ops.LI_FP32, FAKE, None, 0, 64, FAKE, FAKE, 20000, ctypes.byref(c),
+                          FAKE, 20000, 100, FAKE, 10, FAKE, FAKE, big, None, None) == ops.LI_OK
 
 
 def test_workspace_sizes(L):
@@ -106,9 +109,12 @@ def test_workspace_sizes(L):
     assert L.li_append_workspace_bytes(4, 7168, 256, 1) > 0
     assert L.li_hs_workspace_bytes(1, 4, 8192, 2048) >= 4 * 8192 * 4
     assert L.li_hs_workspace_bytes(3, 4, 8192, 2048) >= 3 * 4 * 8192 * 4
-    # the anchor workspace: the same size whatever the call shape up to 64 rows at the front
-    assert L.li_hs_anchor_workspace_bytes(4, 131072) > L.li_hs_anchor_workspace_bytes(4, 4096)
-    assert L.li_hs_anchor_workspace_bytes(64, 4096) >= 64 * 4096 * 4
+    # the anchor workspace: none for rows of at most 8192 positions (one single-workgroup
+    # selection per output), else sized by rows and length
+    assert L.li_hs_anchor_workspace_bytes(4, 4096) == 0
+    assert L.li_hs_anchor_workspace_bytes(4, 8192) == 0
+    assert L.li_hs_anchor_workspace_bytes(4, 131072) > L.li_hs_anchor_workspace_bytes(4, 8193) > 0
+    assert L.li_hs_anchor_workspace_bytes(64, 16384) >= 64 * 16384 * 4
 
 
 def test_anchor_selection_rejects_rows_beyond_its_segment_table(L):
@@ -160,15 +166,15 @@ def test_header_constant_matches_binding():
 
 def test_score_topk_checks_on_the_host(L):
     FAKE = 0x1000
-    c = _cache()
-    big = L.li_hs_anchor_workspace_bytes(4, 256)
-    assert L.li_score_topk(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
-                           FAKE, 256, 0, FAKE, FAKE, big, None, None) == ops.LI_ERR_INVALID
+    c = _cache(max_blocks=400)
+    big = L.li_hs_anchor_workspace_bytes(4, 20000)
+    assert L.li_score_topk(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 20000, ctypes.byref(c),
+                           FAKE, 20000, 0, FAKE, FAKE, big, None, None) == ops.LI_ERR_INVALID
     assert b"k = 0" in L.li_last_error()
-    assert L.li_score_topk(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
-                           FAKE, 256, 70000, FAKE, FAKE, big, None, None) == ops.LI_ERR_INVALID
-    assert L.li_score_topk(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 256, ctypes.byref(c),
-                           FAKE, 256, 16, FAKE, FAKE, big - 1, None, None) == ops.LI_ERR_INVALID
+    assert L.li_score_topk(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 20000, ctypes.byref(c),
+                           FAKE, 20000, 70000, FAKE, FAKE, big, None, None) == ops.LI_ERR_INVALID
+    assert L.li_score_topk(FAKE, ops.LI_FP32, FAKE, None, 4, 64, FAKE, FAKE, 20000, ctypes.byref(c),
+                           FAKE, 20000, 16, FAKE, FAKE, big - 1, None, None) == ops.LI_ERR_INVALID
     assert b"workspace needs" in L.li_last_error()
-    assert L.li_score_topk(FAKE, ops.LI_FP32, FAKE, None, 0, 64, FAKE, FAKE, 256, ctypes.byref(c),
-                           FAKE, 256, 16, FAKE, FAKE, big, None, None) == ops.LI_OK
+    assert L.li_score_topk(FAKE, ops.LI_FP32, FAKE, None, 0, 64, FAKE, FAKE, 20000, ctypes.byref(c),
+                           FAKE, 20000, 16, FAKE, FAKE, big, None, None) == ops.LI_OK

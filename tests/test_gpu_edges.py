@@ -97,3 +97,45 @@ def test_empty_batches_are_no_ops():
                                    None, ws.data_ptr(), ws.numel(), st) == ops.LI_OK
     torch.cuda.synchronize()
     assert torch.all(out == 7)
+
+
+@pytest.mark.parametrize("L", [8192, 40000])
+def test_selection_lengths_out_of_range_are_clamped(L):
+    """Device-side valid lengths outside [0, max_len] (a caller error the host
+    cannot see) are clamped by every selection kernel: a negative length
+    selects nothing, one above max_len selects as max_len; both the
+    single-workgroup path (rows <= 8192) and the multi-workgroup path."""
+    say(f"out-of-range valid lengths, L={L}")
+    rng = np.random.default_rng(L)
+    u = np.round(rng.standard_normal((3, L)), 2).astype(np.float32)
+    valid = np.array([-5, L + 1000, L // 2], dtype=np.int32)
+    ud = torch.from_numpy(u).cuda()
+    vd = torch.from_numpy(valid).cuda()
+    idx = ops.topk(ud, vd, L, 2048).cpu().numpy()
+    cand, sel = ops.hs_anchor_select(ud, vd, L, 4096, 2048)
+    cand, sel = cand.cpu().numpy(), sel.cpu().numpy()
+    for i, n in enumerate([0, L, L // 2]):
+        row = u[i, :n].astype(np.float64)
+        assert np.array_equal(idx[i], O.pad(O.topk(row, 2048), 2048)), i
+        assert np.array_equal(cand[i], O.pad(O.hs_candidates(row, 4096), 4096)), i
+        assert np.array_equal(sel[i], O.pad(O.topk(row, 2048), 2048)), i
+
+
+def test_short_rows_candidates_only_and_zero_length():
+    """The single-workgroup anchor selection when only C is asked for (B
+    covering the row: C is every position), and max_len = 0 (every output
+    padding)."""
+    say("short rows: C only, and max_len = 0")
+    u = np.round(np.random.default_rng(5).standard_normal((2, 3000)), 1).astype(np.float32)
+    vd = torch.tensor([3000, 1234], dtype=torch.int32, device="cuda")
+    ud = torch.from_numpy(u).cuda()
+    cand, sel = ops.hs_anchor_select(ud, vd, 3000, 4096, 100, want_sel=False)
+    assert sel is None
+    c = cand.cpu().numpy()
+    for i, n in enumerate([3000, 1234]):
+        assert np.array_equal(c[i], O.pad(np.arange(n), 4096)), i
+    z = torch.zeros((2, 16), device="cuda")
+    vz = torch.zeros(2, dtype=torch.int32, device="cuda")
+    cand, sel = ops.hs_anchor_select(z, vz, 0, 64, 8)
+    idx = ops.topk(z, vz, 0, 8)
+    assert torch.all(cand == -1) and torch.all(sel == -1) and torch.all(idx == -1)
