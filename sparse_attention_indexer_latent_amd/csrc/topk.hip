@@ -1394,8 +1394,8 @@ topk_reg_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
   uint32_t need = (uint32_t)k - sh.sel_above;
   // Gather every key at or above bin b1 (the selection plus bin b1's rest)
   // with its position into an LDS list: per-thread counts, one block scan
-  // for the offsets, then branch-free writes (lanes with nothing to write
-  // hit a slot of their own past the list).
+  // for the offsets, then writes of the listed keys only (a few percent of
+  // the row), so the LDS sees only their traffic.
   uint32_t *ckey = sh.hA + kRegBins + 1024, *cpos = ckey + kRegCand + kWave;
   const uint32_t lo = b1 << 21;
   uint32_t cnt = 0;
@@ -1407,11 +1407,11 @@ topk_reg_kernel(const float *__restrict__ scores, int64_t ld, const int32_t *__r
   if (listed) {
 #pragma unroll
     for (int e = 0; e < NIT * 4; ++e) {
-      const bool pr = key[e] >= lo;
-      const uint32_t at = pr ? slot : (uint32_t)(kRegCand + lane);
-      ckey[at] = key[e];
-      cpos[at] = (e >> 2) * 4096 + 4 * tid + (e & 3);
-      slot += pr ? 1u : 0u;
+      if (key[e] >= lo) {
+        ckey[slot] = key[e];
+        cpos[slot] = (e >> 2) * 4096 + 4 * tid + (e & 3);
+        ++slot;
+      }
     }
   }
   lds_sync();
