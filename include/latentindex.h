@@ -257,10 +257,11 @@ li_status li_hs_anchor_select(const float *scores, int64_t ld, int32_t n_rows,
  * li_hs_anchor -- the anchor layer's whole part of hierarchical selection in
  * one call ("Hierarchical Selection" paragraph, eq. 8): its scores of every
  * position (as li_score) and, from them, C and S (as li_hs_anchor_select).
- * For a bf16 cache with H = 64, r = 256, at most 64 queries and max_len
- * above 8192, the scorer builds the rows' key histograms as it writes the
- * scores, so the selection does not read them an extra time; otherwise it
- * is the two calls in turn.
+ * For the caches the issuer/compute scorer serves (bf16 with r = 192 or
+ * 256, fp8 with r = 128, 192 or 256), H = 64, at most 64 queries (on
+ * distinct sequences) and max_len above 8192, the scorer builds the rows'
+ * key histograms as it writes the scores, so the selection does not read
+ * them an extra time; otherwise it is the two calls in turn.
  *   q_tilde .. ld: as for li_score; q_len[i] is also row i's valid length;
  *               max_len at most 2,097,152 (LI_ERR_UNSUPPORTED beyond).
  *   B, cand, k, sel: as for li_hs_anchor_select.
@@ -281,9 +282,9 @@ li_status li_hs_anchor(const void *q_tilde, li_dtype qt_dt, const float *w, cons
  * li_score_topk -- one layer's full-scan selection in one call ("Methodology",
  * eq. 8 and the TopK definition after it): the scores of every position (as
  * li_score) and each query's top-min(k, q_len[i]) positions (as li_topk with
- * valid_len = q_len).  For a bf16 cache with H = 64, r = 256, at most 64
- * queries and max_len above 8192 the scorer builds the rows' key histograms
- * as it writes the scores, so the selection reads them once fewer.
+ * valid_len = q_len).  On the caches and shapes li_hs_anchor names, the
+ * scorer builds the rows' key histograms as it writes the scores, so the
+ * selection reads them once fewer.
  *   q_tilde .. ld: as for li_score; max_len at most 2,097,152.
  *   k, out_idx   1 <= k <= 65536; out_idx device int32 [n_q, k] (out):
  *                ascending token ids, -1 padded.
