@@ -260,9 +260,8 @@ li_status li_hs_anchor_select(const float *scores, int64_t ld, int32_t n_rows,
  * For the caches the issuer/compute scorer serves (bf16 with r = 192 or
  * 256, fp8 with r = 128, 192 or 256), H = 64, at most 64 queries (and no
  * more than the cache has sequences) and max_len above 8192, the scorer
- * builds the rows'
- * key histograms as it writes the scores, so the selection does not read
- * them an extra time; otherwise it is the two calls in turn.
+ * builds the rows' key histograms as it writes the scores, so the selection
+ * does not read them an extra time; otherwise it is the two calls in turn.
  *   q_tilde .. ld: as for li_score; q_len[i] is also row i's valid length;
  *               max_len at most 2,097,152 (LI_ERR_UNSUPPORTED beyond).
  *   B, cand, k, sel: as for li_hs_anchor_select.
