@@ -10,6 +10,7 @@ namespace {
 
 constexpr int kT = 32;    // output block rows and columns per workgroup
 constexpr int kKC = 128;  // d per slice: 32 per k slot
+static_assert(kT * kKC % (4 * 256) == 0, "a chunk's tiles stage in whole float4s per thread");
 
 // Rows of the output are "row slots": with a shared decoder, slot = s*H + h
 // (all rows); with per-head decoders, bz selects the head and
@@ -58,26 +59,42 @@ __device__ __forceinline__ void absorb_block(const void *__restrict__ q, int n_q
   // this wavefront's 16 x 16 tile; lane supplies row i of A and of B, slot g
   const int ti = wave >> 1, tj = wave & 1;
   const int i = lane % 16, g = lane / 16;
-  const int slot = by * kT + 16 * ti + i, j = bx * kT + 16 * tj + i;
-  const bool a_ok = slot < n_rows, b_ok = j < r;
-  // out-of-range rows read a valid row and are zeroed, so loads need no branches
-  const int64_t qo = qrow(a_ok ? slot : 0);
-  const float *dr = D + (int64_t)(b_ok ? j : 0) * d_I;
+  // The workgroup's 32 query rows and 32 decoder rows of each d-chunk are
+  // staged in LDS once (each row serves two wavefronts); rows and dims out of
+  // range are staged as zeros.
+  __shared__ __align__(16) float qs[kT][kKC + 4];
+  __shared__ __align__(16) float ds[kT][kKC + 4];
   // four independent accumulation chains (one per float4 lane), summed in a
   // fixed order at the end, so consecutive matrix-core ops do not wait on
   // each other
   f32x4 acc4[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
                    {0.f, 0.f, 0.f, 0.f}};
+  // beta for this block's rows, computed once (by the column-0 blocks): eight
+  // threads per row, each a chain over its dims in ascending order (from the
+  // staged rows), then a fixed-order combination of the eight partial sums.
+  const bool want_beta = beta && bx == 0;  // uniform
+  const int rr = tid / 8, part = tid % 8;
+  const int sl = by * kT + rr;
+  float bs = 0.f;
   for (int d0 = 0; d0 < d_I; d0 += kKC) {
+#pragma unroll
+    for (int k4 = 0; k4 < kT * kKC / 4 / 256; ++k4) {
+      const int e = (int)threadIdx.x + 256 * k4;
+      const int row = e / (kKC / 4), c4 = e % (kKC / 4);
+      const int d = d0 + 4 * c4;
+      const int qslot = by * kT + row, jrow = bx * kT + row;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
+      if (qslot < n_rows && d < d_I) x = ldq4<BF16Q>(q, qrow(qslot) + d);
+      if (jrow < r && d < d_I) y = *(const float4 *)(D + (int64_t)jrow * d_I + d);
+      *reinterpret_cast<float4 *>(&qs[row][4 * c4]) = x;
+      *reinterpret_cast<float4 *>(&ds[row][4 * c4]) = y;
+    }
+    __syncthreads();
     float4 av[8], bv[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int d = d0 + 32 * g + 4 * c;
-      const int dc = d < d_I ? d : 0;
-      av[c] = ldq4<BF16Q>(q, qo + dc);
-      bv[c] = *(const float4 *)(dr + dc);
-      if (!(a_ok && d < d_I)) av[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (!(b_ok && d < d_I)) bv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      av[c] = *reinterpret_cast<const float4 *>(&qs[16 * ti + i][32 * g + 4 * c]);
+      bv[c] = *reinterpret_cast<const float4 *>(&ds[16 * tj + i][32 * g + 4 * c]);
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -86,6 +103,13 @@ __device__ __forceinline__ void absorb_block(const void *__restrict__ q, int n_q
       acc4[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].z, bv[c].z, acc4[2], 0, 0, 0);
       acc4[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c].w, bv[c].w, acc4[3], 0, 0, 0);
     }
+    if (want_beta && b && sl < n_rows) {
+      // this thread's dims d = nope_off + part (mod 8), d >= nope_off, in the chunk
+      int d = nope_off + part;
+      if (d < d0) d += ((d0 - d + 7) / 8) * 8;
+      for (; d < min(d_I, d0 + kKC); d += 8) bs = fmaf(qs[rr][d - d0], b[d - nope_off], bs);
+    }
+    __syncthreads();  // the next chunk reuses the tiles
   }
   const f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
   // acc[v] = D[4 g + v][i] of the tile
@@ -99,16 +123,8 @@ __device__ __forceinline__ void absorb_block(const void *__restrict__ q, int n_q
       q_tilde[orow * r + jo] = acc[v];
     }
   }
-  // beta for this block's rows, computed once (by the column-0 blocks): eight
-  // threads per row, a fixed-order combination of their partial sums.
-  if (beta && bx == 0) {
-    const int rr = tid / 8, part = tid % 8;
-    const int sl = by * kT + rr;
-    float s = 0.f;
-    if (b && sl < n_rows) {
-      const int64_t off = qrow(sl);
-      for (int d = nope_off + part; d < d_I; d += 8) s = fmaf(ldq<BF16Q>(q, off + d), b[d - nope_off], s);
-    }
+  if (want_beta) {
+    float s = bs;
     s += __shfl_xor(s, 1, kWave);
     s += __shfl_xor(s, 2, kWave);
     s += __shfl_xor(s, 4, kWave);
