@@ -7,12 +7,13 @@
 // over that head's queries.  Several layers (each with its own decoder) go
 // in one launch: blockIdx.z enumerates (layer, head).  Both operands are
 // contiguous along d, and the GEMM runs on the fp32 matrix cores
-// (v_mfma_f32_16x16x4f32) with no LDS: a workgroup computes a 32 x 32
-// output block, one wavefront per 16 x 16 tile.  The instruction takes, for
-// each of its 4 k slots g, A[i][g] from lane i + 16 g and B[g][j] from lane
-// j + 16 g; slot g is given the contiguous quarter d in [32 g, 32 g + 32) of
-// each 128-wide slice of d, so every lane streams its own row of q and of Dt
-// with 16-byte loads straight into registers, and step t of the chain pairs
+// (v_mfma_f32_16x16x4f32): a workgroup computes a 32 x 32 output block, one
+// wavefront per 16 x 16 tile, from its 32 query rows and 32 decoder rows of
+// each 128-wide slice of d, staged in LDS once (each row feeds two
+// wavefronts).  The instruction takes, for each of its 4 k slots g, A[i][g]
+// from lane i + 16 g and B[g][j] from lane j + 16 g; slot g is given the
+// contiguous quarter d in [32 g, 32 g + 32) of the slice, so every lane reads
+// its own row of q and of Dt in 16-byte pieces, and step t of the chain pairs
 // d = 32 g + t across the slots.  The work is applied once per new query
 // instead of once per cached token.
 #include "absorb_block.h"
